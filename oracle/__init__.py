@@ -1,0 +1,352 @@
+"""CPU oracle for the MLA latent-KV insert / epilogue / gather / pack path.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The product library
+(``fp8_paged_insert_amd``) never imports it, and this package never imports the
+product library: the two share nothing but the seeded input generators.
+
+The arithmetic lives in ``mla_oracle.c`` (plain serial C, built with gcc
+``-O2 -fno-fast-math -ffp-contract=off``); this module only marshals numpy
+arrays into it.  bf16 arrays are ``numpy.uint16`` bit patterns, fp8 arrays are
+``numpy.uint8`` codes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mla_oracle.c")
+_LIB = os.path.join(_HERE, "libmla_oracle.so")
+
+CACHE_BF16 = 0
+CACHE_FP8_E4M3 = 1
+PACK_KEY_BF16 = 0
+PACK_KEY_V_FP8 = 1
+
+OK = 0
+EINVAL = -1
+EDUPSLOT = -2
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle shared library with gcc; returns its path."""
+    if not force and os.path.exists(_LIB):
+        return _LIB
+    tmp = _LIB + ".tmp"
+    cmd = [
+        "gcc", "-std=c11", "-O2", "-fno-fast-math", "-ffp-contract=off",
+        "-Wall", "-Wextra", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm",
+    ]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+_f32 = ctypes.c_float
+_f64 = ctypes.c_double
+_int = ctypes.c_int
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB)
+    sig = {
+        "orc_bf16_to_f32": (ctypes.c_float, [ctypes.c_uint16]),
+        "orc_f64_to_bf16": (ctypes.c_uint16, [_f64]),
+        "orc_e4m3_decode": (_f64, [ctypes.c_uint8]),
+        "orc_e4m3_encode": (ctypes.c_uint8, [_f64]),
+        "orc_quantize": (ctypes.c_uint8, [ctypes.c_uint16, _f32]),
+        "orc_dequantize": (ctypes.c_uint16, [ctypes.c_uint8, _f32]),
+        "orc_f64_to_bf16_n": (None, [_vp, _i64, _vp]),
+        "orc_e4m3_encode_f32_n": (None, [_vp, _i64, _vp]),
+        "orc_e4m3_decode_n": (None, [_vp, _i64, _vp]),
+        "orc_quantize_n": (None, [_vp, _i64, _f32, _vp]),
+        "orc_dequantize_n": (None, [_vp, _i64, _f32, _vp]),
+        "orc_insert_single": (_int, [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64,
+                                     _vp, _i64, _i64, _i64, _int, _f32]),
+        "orc_insert_grouped": (_int, [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp,
+                                      _vp, _i64, _i64, _i64, _i64, _i64, _i64,
+                                      _i64, _i64, _int]),
+        "orc_gemm_rows": (_int, [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp,
+                                 _i64, _vp]),
+        "orc_rmsnorm_row": (_int, [_vp, _i64, _vp, _f32, _vp]),
+        "orc_rope_row": (_int, [_vp, _i64, _i64, _f64, _vp]),
+        "orc_ctx_kv_epilogue": (_int, [_vp, _i64, _i64, _vp, _f32, _vp, _f64,
+                                       _i64, _i64, _i64, _i64, _vp, _vp, _vp,
+                                       _i64, _i64, _i64, _i64, _int, _vp]),
+        "orc_gather": (_int, [_vp, _int, _f32, _i64, _i64, _i64, _vp, _i64, _i64,
+                              _vp]),
+        "orc_pack": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _i64,
+                            _i64, _i64, _i64, _i64, _int, _f32, _f32, _vp, _vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _check(rc: int, what: str):
+    if rc != OK:
+        raise OracleError(f"{what}: oracle rejected the input (code {rc})")
+
+
+def _need(a, dtype, name):
+    if not isinstance(a, np.ndarray) or a.dtype != dtype:
+        raise TypeError(f"{name} must be a numpy {np.dtype(dtype).name} array")
+
+
+# ---------------------------------------------------------------- formats --
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float32 values (exact)."""
+    _need(bits, np.uint16, "bits")
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def f64_to_bf16(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, np.uint16)
+    _load().orc_f64_to_bf16_n(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Saturating round-to-nearest-even float32 -> e4m3fn codes."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, np.uint8)
+    _load().orc_e4m3_encode_f32_n(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def e4m3_encode_scalar(x: float) -> int:
+    return int(_load().orc_e4m3_encode(float(x)))
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, np.float64)
+    _load().orc_e4m3_decode_n(_ptr(c), c.size, _ptr(out))
+    return out
+
+
+def quantize(x_bf16: np.ndarray, scale: float) -> np.ndarray:
+    x = np.ascontiguousarray(x_bf16)
+    _need(x, np.uint16, "x_bf16")
+    out = np.empty(x.shape, np.uint8)
+    _load().orc_quantize_n(_ptr(x), x.size, float(scale), _ptr(out))
+    return out
+
+
+def dequantize(codes: np.ndarray, scale: float) -> np.ndarray:
+    c = np.ascontiguousarray(codes)
+    _need(c, np.uint8, "codes")
+    out = np.empty(c.shape, np.uint16)
+    _load().orc_dequantize_n(_ptr(c), c.size, float(scale), _ptr(out))
+    return out
+
+
+# ----------------------------------------------------------------- insert --
+def _cache_dtype_code(cache: np.ndarray) -> int:
+    if cache.dtype == np.uint16:
+        return CACHE_BF16
+    if cache.dtype == np.uint8:
+        return CACHE_FP8_E4M3
+    raise TypeError("cache must be uint16 (bf16) or uint8 (fp8 e4m3fn)")
+
+
+def insert_single(kv_c, k_pe, slots, cache, scale=1.0):
+    """In-place single-layer concat-and-cache.
+
+    kv_c [T, R] uint16, k_pe [T, P] uint16 (row strides taken from the arrays),
+    slots [T] int64, cache [num_blocks, block_size, E] (uint16 or uint8,
+    strides taken from the array).
+    """
+    _need(kv_c, np.uint16, "kv_c")
+    _need(k_pe, np.uint16, "k_pe")
+    slots = np.ascontiguousarray(slots, dtype=np.int64)
+    it_c = kv_c.itemsize
+    it = cache.itemsize
+    rc = _load().orc_insert_single(
+        _ptr(kv_c), kv_c.strides[0] // it_c, _ptr(k_pe), k_pe.strides[0] // it_c,
+        _ptr(slots), slots.shape[0], kv_c.shape[1], k_pe.shape[1],
+        _ptr(cache), cache.shape[1], cache.strides[0] // it, cache.strides[1] // it,
+        _cache_dtype_code(cache), float(scale))
+    _check(rc, "insert_single")
+
+
+def insert_grouped(kv_c, k_pe, slot_mapping, caches, scales=None):
+    """In-place grouped insert.
+
+    kv_c [L, T, R] and k_pe [L, T, P] uint16 views with any strides;
+    slot_mapping [L, T] int64 (layer stride 0 = shared mapping);
+    caches: list of L arrays [num_blocks, block_size, E] with one layout;
+    scales: float32 [L] for fp8 caches, None for bf16.
+    """
+    _need(kv_c, np.uint16, "kv_c")
+    _need(k_pe, np.uint16, "k_pe")
+    _need(slot_mapping, np.int64, "slot_mapping")
+    L, T, R = kv_c.shape
+    P = k_pe.shape[2]
+    c0 = caches[0]
+    it = c0.itemsize
+    for c in caches:
+        if c.dtype != c0.dtype or c.strides != c0.strides or c.shape[1] != c0.shape[1]:
+            raise ValueError("caches must share dtype and layout")
+    dt = _cache_dtype_code(c0)
+    ptr_arr = (ctypes.c_void_p * max(L, 1))(*[c.ctypes.data for c in caches])
+    sc = None
+    if dt == CACHE_FP8_E4M3:
+        sc = np.ascontiguousarray(scales, dtype=np.float32)
+    rc = _load().orc_insert_grouped(
+        _ptr(kv_c), kv_c.strides[0] // 2, kv_c.strides[1] // 2,
+        _ptr(k_pe), k_pe.strides[0] // 2, k_pe.strides[1] // 2,
+        ctypes.cast(ptr_arr, ctypes.c_void_p), _ptr(sc),
+        _ptr(slot_mapping), slot_mapping.strides[0] // 8,
+        L, T, R, P, c0.shape[1], c0.strides[0] // it, c0.strides[1] // it, dt)
+    _check(rc, "insert_grouped")
+
+
+# ------------------------------------------- projection / norm / rope / epi --
+def gemm_rows(x, w_kn, rows=None) -> np.ndarray:
+    """Y[rows] = X[rows] . W with W addressed as the [K, N] matrix (any strides)."""
+    _need(x, np.uint16, "x")
+    _need(w_kn, np.uint16, "w_kn")
+    T, K = x.shape
+    K2, N = w_kn.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    if x.strides[1] != 2:
+        raise ValueError("x rows must be contiguous")
+    rows = np.arange(T, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, np.int64)
+    out = np.empty((rows.shape[0], N), np.uint16)
+    rc = _load().orc_gemm_rows(_ptr(x), x.strides[0] // 2, _ptr(w_kn),
+                               w_kn.strides[0] // 2, w_kn.strides[1] // 2, K, N,
+                               _ptr(rows), rows.shape[0], _ptr(out))
+    _check(rc, "gemm_rows")
+    return out
+
+
+def rmsnorm_row(x, gamma, eps) -> np.ndarray:
+    x = np.ascontiguousarray(x, np.uint16)
+    gamma = np.ascontiguousarray(gamma, np.uint16)
+    out = np.empty_like(x)
+    _check(_load().orc_rmsnorm_row(_ptr(x), x.size, _ptr(gamma), float(eps), _ptr(out)),
+           "rmsnorm_row")
+    return out
+
+
+def rope_row(x, pos, base=10000.0) -> np.ndarray:
+    x = np.ascontiguousarray(x, np.uint16)
+    out = np.empty_like(x)
+    _check(_load().orc_rope_row(_ptr(x), x.size, int(pos), float(base), _ptr(out)),
+           "rope_row")
+    return out
+
+
+def ctx_kv_epilogue(all_kv, gamma, eps, positions, slot_mapping, caches,
+                    scales=None, rope_base=10000.0, kv_lora_rank=512):
+    """Norm + RoPE of every (layer, token) row, then the grouped insert.
+
+    all_kv: [T, L, R+P] uint16 view (any strides); gamma [L, R] uint16;
+    positions [T] int64; slot_mapping [L, T] int64 (layer stride 0 allowed);
+    caches: list of L cache arrays, or None to compute the rows only.
+    Returns the bf16 rows [L, T, R+P] that were inserted.
+    """
+    _need(all_kv, np.uint16, "all_kv")
+    T, L, W = all_kv.shape
+    R = kv_lora_rank
+    P = W - R
+    gamma = np.ascontiguousarray(gamma, np.uint16)
+    positions = np.ascontiguousarray(positions, np.int64)
+    rows = np.empty((L, T, W), np.uint16)
+    ptrs = None
+    dt = CACHE_BF16
+    sc = None
+    bs = bstride = estride = 1
+    sls = 0
+    if caches is not None:
+        c0 = caches[0]
+        it = c0.itemsize
+        dt = _cache_dtype_code(c0)
+        ptr_arr = (ctypes.c_void_p * max(L, 1))(*[c.ctypes.data for c in caches])
+        ptrs = ctypes.cast(ptr_arr, ctypes.c_void_p)
+        bs, bstride, estride = c0.shape[1], c0.strides[0] // it, c0.strides[1] // it
+        _need(slot_mapping, np.int64, "slot_mapping")
+        sls = slot_mapping.strides[0] // 8
+        if dt == CACHE_FP8_E4M3:
+            sc = np.ascontiguousarray(scales, dtype=np.float32)
+    rc = _load().orc_ctx_kv_epilogue(
+        _ptr(all_kv), all_kv.strides[1] // 2, all_kv.strides[0] // 2, _ptr(gamma),
+        float(eps), _ptr(positions), float(rope_base), L, T, R, P, ptrs, _ptr(sc),
+        None if caches is None else _ptr(slot_mapping), sls, bs, bstride, estride,
+        dt, _ptr(rows))
+    _check(rc, "ctx_kv_epilogue")
+    return rows
+
+
+# --------------------------------------------------------- gather / pack --
+def gather(cache, src_slots, scale=1.0, width=None) -> np.ndarray:
+    """Contiguous bf16 [T, width] rows read through src_slots (dequantised for fp8)."""
+    dt = _cache_dtype_code(cache)
+    it = cache.itemsize
+    src_slots = np.ascontiguousarray(src_slots, np.int64)
+    width = cache.shape[2] if width is None else width
+    out = np.empty((src_slots.shape[0], width), np.uint16)
+    rc = _load().orc_gather(_ptr(cache), dt, float(scale), cache.shape[1],
+                            cache.strides[0] // it, cache.strides[1] // it,
+                            _ptr(src_slots), src_slots.shape[0], width, _ptr(out))
+    _check(rc, "gather")
+    return out
+
+
+def pack(k_nope, k_pe, v=None, mode=PACK_KEY_BF16, k_scale=1.0, v_scale=1.0):
+    """Full key [T, H, nope+rope] (+ fp8 V [T, H, vdim]) from strided inputs.
+
+    k_nope [T, H, nope] uint16 view (last dim contiguous), k_pe [T, rope]
+    uint16 view (last dim contiguous), v [T, H, vdim] uint16 view or None.
+    """
+    _need(k_nope, np.uint16, "k_nope")
+    _need(k_pe, np.uint16, "k_pe")
+    T, H, nope = k_nope.shape
+    rope = k_pe.shape[-1]
+    if (k_nope.size and k_nope.strides[2] != 2) or (k_pe.size and k_pe.strides[-1] != 2):
+        raise ValueError("innermost dimensions must be contiguous")
+    kpe_ts = k_pe.strides[0] // 2
+    if mode == PACK_KEY_BF16:
+        key = np.empty((T, H, nope + rope), np.uint16)
+        vout = None
+        vd, vts, vhs = 0, 0, 0
+    else:
+        _need(v, np.uint16, "v")
+        if v.size and v.strides[2] != 2:
+            raise ValueError("v innermost dimension must be contiguous")
+        vd = v.shape[2]
+        vts, vhs = v.strides[0] // 2, v.strides[1] // 2
+        key = np.empty((T, H, nope + rope), np.uint8)
+        vout = np.empty((T, H, vd), np.uint8)
+    rc = _load().orc_pack(_ptr(k_nope), k_nope.strides[0] // 2, k_nope.strides[1] // 2,
+                          _ptr(k_pe), kpe_ts, _ptr(v), vts, vhs, T, H, nope, rope, vd,
+                          mode, float(k_scale), float(v_scale), _ptr(key), _ptr(vout))
+    _check(rc, "pack")
+    return key, vout

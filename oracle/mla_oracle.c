@@ -1,0 +1,484 @@
+/*
+ * mla_oracle.c -- plain, slow, serial CPU oracle for the MLA latent-KV
+ * insert / epilogue / gather / pack path.
+ *
+ * TEST INFRASTRUCTURE ONLY: only the test-suite, the smoke check and the
+ * benchmark's CPU-baseline leg load this.  It shares no code, header, table
+ * or helper with the HIP library, and it never calls into it.
+ *
+ * Built with gcc -O2 -fno-fast-math -ffp-contract=off, so every float
+ * operation below is one IEEE-754 operation in the precision written.
+ *
+ * Pages (cited by title and section heading):
+ *   [P1] "PR #51772 完整报告" ([Attention][MLA] Fuse Kimi-K3 chunked-context
+ *        K/V packing)
+ *   [P2] "PR #50585 完整报告" ([K3 Perf] Optimize k3 dspark fused kv)
+ *   [P3] "PR #55356 完整报告" ([Kimi Perf] Group fp8 mla cache insertion)
+ *
+ * Where the pages leave a step open, the reading taken is stated at the
+ * function.  Pins: every function here is checked by the CPU tests against
+ * closed forms, library routines (torch CPU fp8/bf16 casts, float64 matmul),
+ * brute force on tiny inputs, or invariants; none is "parity unpinned".
+ */
+#include "mla_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ======================================================================== */
+/* Number formats                                                            */
+/* ======================================================================== */
+
+/* bf16 -> f32: a bf16 value is the top half of an IEEE binary32 pattern. */
+float orc_bf16_to_f32(uint16_t b) {
+  uint32_t u = ((uint32_t)b) << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+/*
+ * Round a double to the nearest bfloat16 (8 significant bits, exponent range
+ * of binary32, IEEE subnormals), ties to even.  NaN becomes the quiet NaN
+ * 0x7FC0 with the sign kept; overflow becomes +-Inf, as round-to-nearest
+ * requires.
+ *
+ * Method: write |x| = r * 2^q where 2^q is the bf16 spacing in the binade of
+ * |x| (or the subnormal spacing 2^-133 below the normal range) and round the
+ * real r to an integer with nearbyint() in the default ties-to-even mode.
+ */
+uint16_t orc_f64_to_bf16(double x) {
+  const uint16_t sign = signbit(x) ? 0x8000u : 0u;
+  if (isnan(x)) return (uint16_t)(sign | 0x7FC0u);
+  double a = fabs(x);
+  if (isinf(a)) return (uint16_t)(sign | 0x7F80u);
+  if (a == 0.0) return sign;
+  int e;
+  (void)frexp(a, &e);            /* a = m * 2^e, 0.5 <= m < 1 */
+  int q = e - 8;                 /* 8 significant bits in this binade */
+  if (q < -133) q = -133;        /* subnormal spacing of bf16 */
+  double r = nearbyint(ldexp(a, -q));
+  double v = ldexp(r, q);
+  if (v >= 0x1p128) return (uint16_t)(sign | 0x7F80u);
+  float f = (float)v;            /* exact: v has <= 8 significant bits */
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return (uint16_t)(sign | (uint16_t)(u >> 16));
+}
+
+/*
+ * OCP FP8 e4m3fn decode: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa
+ * bits; exponent field 0 is subnormal (m * 2^-9); S.1111.111 is NaN; there is
+ * no infinity, so the largest finite magnitude is code 0x7E = 448.  This is
+ * the format behind torch.float8_e4m3fn, which [P1] 实现拆解 item 1 and the
+ * 关键源码片段 docstring of fused_mla_kv_concat_quant_fp8 name as the cast the
+ * fp8 path must match bit for bit.
+ */
+double orc_e4m3_decode(uint8_t code) {
+  const int s = code >> 7;
+  const int e = (code >> 3) & 0xF;
+  const int m = code & 0x7;
+  double v;
+  if (e == 0xF && m == 0x7) return s ? -NAN : NAN;
+  if (e == 0)
+    v = ldexp((double)m, -9);
+  else
+    v = ldexp((double)(8 + m), e - 10);
+  return s ? -v : v;
+}
+
+/*
+ * e4m3fn encode, round to nearest with ties to even, saturating:
+ *   NaN -> 0x7F | sign;  |x| >= 448 (Inf included) -> 0x7E | sign;
+ *   otherwise the finite code whose value is nearest |x|; on a tie between two
+ *   neighbouring codes the one with an even code (mantissa LSB 0) wins; the
+ *   sign bit is then attached, so -0 and tiny negatives give 0x80.
+ * Reading: the pages fix bit-identity with torch's e4m3fn cast ([P1] 风险与影响
+ * item 3) but not the overflow rule; the saturating rule is taken (it agrees
+ * with torch for every |x| <= 464, which covers all workloads here).
+ * Implementation: a plain nearest-value search over the 127 finite codes.
+ */
+static double g_e4m3_values[0x7F];
+static int g_e4m3_values_ready = 0;
+
+/* The 127 finite non-negative code values, decoded once (codes 0x00..0x7E). */
+static const double* e4m3_values(void) {
+  if (!g_e4m3_values_ready) {
+    for (int c = 0; c <= 0x7E; ++c) g_e4m3_values[c] = orc_e4m3_decode((uint8_t)c);
+    g_e4m3_values_ready = 1;
+  }
+  return g_e4m3_values;
+}
+
+uint8_t orc_e4m3_encode(double x) {
+  const uint8_t sign = signbit(x) ? 0x80u : 0u;
+  if (isnan(x)) return (uint8_t)(sign | 0x7Fu);
+  const double a = fabs(x);
+  if (a >= 448.0) return (uint8_t)(sign | 0x7Eu);
+  const double* val = e4m3_values();
+  int best = 0;
+  double best_d = fabs(a - val[0]);
+  for (int c = 1; c <= 0x7E; ++c) {
+    const double d = fabs(a - val[c]);
+    if (d < best_d || (d == best_d && (c & 1) == 0)) {
+      best = c;
+      best_d = d;
+    }
+  }
+  return (uint8_t)(sign | (uint8_t)best);
+}
+
+/*
+ * Quantise one bf16 value into the fp8 cache with a per-layer scale.
+ * [P3] 实现拆解 item 2 and 关键源码片段 (cache_kernels.cu): the fp8 branch
+ * converts each bf16 element with the layer's kv_scales entry.  Reading: the
+ * scale is a dequantisation scale, so the stored code is
+ * encode(fl32(x) / scale) with one IEEE fp32 division (never a reciprocal
+ * multiply).
+ */
+uint8_t orc_quantize(uint16_t x_bf16, float scale) {
+  const float x = orc_bf16_to_f32(x_bf16);
+  const float q = x / scale;
+  return orc_e4m3_encode((double)q);
+}
+
+/* Dequantise: bf16(fl32(decode(code) * scale)), one fp32 multiply, then one
+ * rounding to bf16.  Reading of the gather's "dequant" step ([P1] 实现拆解
+ * item 2: the plain-fp8 gather path feeding kv_b_proj in bf16). */
+uint16_t orc_dequantize(uint8_t code, float scale) {
+  const float d = (float)orc_e4m3_decode(code); /* exact */
+  const float p = d * scale;
+  return orc_f64_to_bf16((double)p);
+}
+
+void orc_f64_to_bf16_n(const double* x, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_f64_to_bf16(x[i]);
+}
+void orc_e4m3_encode_f32_n(const float* x, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_encode((double)x[i]);
+}
+void orc_e4m3_decode_n(const uint8_t* c, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_decode(c[i]);
+}
+void orc_quantize_n(const uint16_t* x, int64_t n, float scale, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_quantize(x[i], scale);
+}
+void orc_dequantize_n(const uint8_t* c, int64_t n, float scale, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_dequantize(c[i], scale);
+}
+
+/* ======================================================================== */
+/* Insert                                                                    */
+/* ======================================================================== */
+
+static int cmp_i64(const void* a, const void* b) {
+  const int64_t x = *(const int64_t*)a, y = *(const int64_t*)b;
+  return (x > y) - (x < y);
+}
+
+/* Two valid tokens of one layer must not name the same slot: the pages give
+ * no order between such writes, so the oracle refuses that input. */
+static int has_duplicate_slots(const int64_t* slots, int64_t n) {
+  int64_t* tmp = (int64_t*)malloc((size_t)(n > 0 ? n : 1) * sizeof(int64_t));
+  int64_t m = 0;
+  int dup = 0;
+  if (!tmp) return 1;
+  for (int64_t i = 0; i < n; ++i)
+    if (slots[i] >= 0) tmp[m++] = slots[i];
+  qsort(tmp, (size_t)m, sizeof(int64_t), cmp_i64);
+  for (int64_t i = 1; i < m; ++i)
+    if (tmp[i] == tmp[i - 1]) dup = 1;
+  free(tmp);
+  return dup;
+}
+
+/*
+ * Single-layer concat-and-cache, the per-layer operation that the grouped
+ * insert must reproduce exactly ([P3] 关键源码片段, test_cache.py: the
+ * reference is built from one concat_and_cache_mla call per layer).
+ * Per token t ([P3] 关键源码片段, cache_kernels.cu):
+ *   s = slots[t]; a negative slot means the token is skipped;
+ *   block = s / block_size, offset = s % block_size;
+ *   entry = block * block_stride + offset * entry_stride;
+ *   cache[entry + i]                = conv(kv_c[t, i])  for i < kv_lora_rank
+ *   cache[entry + kv_lora_rank + j] = conv(k_pe[t, j])  for j < pe_dim
+ * conv is a raw 16-bit copy for the bf16/auto cache and orc_quantize for fp8.
+ * No other cache element is touched.
+ */
+int orc_insert_single(const uint16_t* kv_c, int64_t kv_c_tok_stride,
+                      const uint16_t* k_pe, int64_t k_pe_tok_stride,
+                      const int64_t* slots, int64_t num_tokens,
+                      int64_t kv_lora_rank, int64_t pe_dim,
+                      void* cache, int64_t block_size, int64_t block_stride,
+                      int64_t entry_stride, int cache_dtype, float scale) {
+  if (num_tokens < 0 || kv_lora_rank < 0 || pe_dim < 0 || block_size <= 0)
+    return ORC_EINVAL;
+  if (cache_dtype != ORC_CACHE_BF16 && cache_dtype != ORC_CACHE_FP8_E4M3)
+    return ORC_EINVAL;
+  if (has_duplicate_slots(slots, num_tokens)) return ORC_EDUPSLOT;
+  for (int64_t t = 0; t < num_tokens; ++t) {
+    const int64_t s = slots[t];
+    if (s < 0) continue;
+    const int64_t block = s / block_size;
+    const int64_t offset = s % block_size;
+    const int64_t entry = block * block_stride + offset * entry_stride;
+    const uint16_t* src_c = kv_c + t * kv_c_tok_stride;
+    const uint16_t* src_p = k_pe + t * k_pe_tok_stride;
+    if (cache_dtype == ORC_CACHE_BF16) {
+      uint16_t* dst = (uint16_t*)cache + entry;
+      for (int64_t i = 0; i < kv_lora_rank; ++i) dst[i] = src_c[i];
+      for (int64_t j = 0; j < pe_dim; ++j) dst[kv_lora_rank + j] = src_p[j];
+    } else {
+      uint8_t* dst = (uint8_t*)cache + entry;
+      for (int64_t i = 0; i < kv_lora_rank; ++i)
+        dst[i] = orc_quantize(src_c[i], scale);
+      for (int64_t j = 0; j < pe_dim; ++j)
+        dst[kv_lora_rank + j] = orc_quantize(src_p[j], scale);
+    }
+  }
+  return ORC_OK;
+}
+
+/*
+ * Grouped insert over num_layers layers in one call ([P3] 功能与动机 and
+ * 实现拆解 items 2-3): layer l uses its own cache base caches[l], its own
+ * scale scales[l] (fp8 only) and the slot row slot_mapping + l *
+ * slot_layer_stride (stride 0 = one mapping shared by all layers, as the
+ * shared_slot_mapping case of [P3] 关键源码片段 test_cache.py does with
+ * expand).  By definition this is num_layers independent single-layer
+ * inserts, which is exactly the equality [P3]'s test asserts.
+ */
+int orc_insert_grouped(const uint16_t* kv_c, int64_t kv_c_layer_stride,
+                       int64_t kv_c_tok_stride,
+                       const uint16_t* k_pe, int64_t k_pe_layer_stride,
+                       int64_t k_pe_tok_stride,
+                       void* const* caches, const float* scales,
+                       const int64_t* slot_mapping, int64_t slot_layer_stride,
+                       int64_t num_layers, int64_t num_tokens,
+                       int64_t kv_lora_rank, int64_t pe_dim,
+                       int64_t block_size, int64_t block_stride,
+                       int64_t entry_stride, int cache_dtype) {
+  if (num_layers < 0) return ORC_EINVAL;
+  if (cache_dtype == ORC_CACHE_FP8_E4M3 && num_layers > 0 && !scales)
+    return ORC_EINVAL;
+  for (int64_t l = 0; l < num_layers; ++l) {
+    const float sc = cache_dtype == ORC_CACHE_FP8_E4M3 ? scales[l] : 1.0f;
+    const int rc = orc_insert_single(
+        kv_c + l * kv_c_layer_stride, kv_c_tok_stride,
+        k_pe + l * k_pe_layer_stride, k_pe_tok_stride,
+        slot_mapping + l * slot_layer_stride, num_tokens, kv_lora_rank, pe_dim,
+        caches[l], block_size, block_stride, entry_stride, cache_dtype, sc);
+    if (rc != ORC_OK) return rc;
+  }
+  return ORC_OK;
+}
+
+/* ======================================================================== */
+/* Projection, RMSNorm, RoPE, epilogue                                       */
+/* ======================================================================== */
+
+/*
+ * KV-only context projection Y = X . W for selected rows ([P2] 功能与动机 and
+ * 实现拆解 item 2: one projection hidden -> L * 576 replaces L full Q+KV
+ * projections).  Reading: bf16 operands, exact products accumulated in
+ * float64 in k order, one rounding to bf16.  W is addressed as the
+ * mathematical [K, N] matrix through (w_k_stride, w_n_stride).
+ * out is [num_rows, N].
+ */
+int orc_gemm_rows(const uint16_t* x, int64_t x_row_stride,
+                  const uint16_t* w, int64_t w_k_stride, int64_t w_n_stride,
+                  int64_t K, int64_t N, const int64_t* rows, int64_t num_rows,
+                  uint16_t* out) {
+  if (K < 0 || N < 0 || num_rows < 0) return ORC_EINVAL;
+  double* acc = (double*)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+  if (!acc) return ORC_EINVAL;
+  for (int64_t r = 0; r < num_rows; ++r) {
+    const uint16_t* xr = x + rows[r] * x_row_stride;
+    for (int64_t n = 0; n < N; ++n) acc[n] = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+      const double xv = (double)orc_bf16_to_f32(xr[k]);
+      const uint16_t* wk = w + k * w_k_stride;
+      for (int64_t n = 0; n < N; ++n)
+        acc[n] += xv * (double)orc_bf16_to_f32(wk[n * w_n_stride]);
+    }
+    for (int64_t n = 0; n < N; ++n) out[r * N + n] = orc_f64_to_bf16(acc[n]);
+  }
+  free(acc);
+  return ORC_OK;
+}
+
+/*
+ * RMSNorm of one kv_c row with the row of the 2-D weight that belongs to its
+ * layer ([P2] 关键源码片段, _precompute_fused_context_kv: ops.rms_norm with a
+ * [L, kv_lora_rank] weight, one row per draft layer).
+ * Reading (the kernel is not printed): y_i = x_i * (mean(x^2) + eps)^(-1/2) *
+ * gamma_i, evaluated in float64 and rounded once to bf16; eps is the binary32
+ * value the caller passes.
+ */
+int orc_rmsnorm_row(const uint16_t* x, int64_t n, const uint16_t* gamma,
+                    float eps, uint16_t* out) {
+  if (n <= 0) return ORC_EINVAL;
+  double ss = 0.0;
+  for (int64_t i = 0; i < n; ++i) {
+    const double v = (double)orc_bf16_to_f32(x[i]);
+    ss += v * v;
+  }
+  const double r = 1.0 / sqrt(ss / (double)n + (double)eps);
+  for (int64_t i = 0; i < n; ++i) {
+    const double v = (double)orc_bf16_to_f32(x[i]);
+    const double g = (double)orc_bf16_to_f32(gamma[i]);
+    out[i] = orc_f64_to_bf16(v * r * g);
+  }
+  return ORC_OK;
+}
+
+/*
+ * Rotary embedding of one k_pe row ([P2] 关键源码片段: RoPE is applied to k_pe
+ * with the context position of each token, the same positions for every
+ * layer).  Reading (the formula is elided on the page): the non-interleaved
+ * ("half split") form with base `base`: for i < d/2,
+ *   theta_i = pos * base^(-2i/d),
+ *   y_i       = x_i * cos(theta_i) - x_{i+d/2} * sin(theta_i)
+ *   y_{i+d/2} = x_{i+d/2} * cos(theta_i) + x_i * sin(theta_i),
+ * in float64, each output rounded once to bf16.
+ */
+int orc_rope_row(const uint16_t* x, int64_t rope_dim, int64_t pos, double base,
+                 uint16_t* out) {
+  if (rope_dim <= 0 || (rope_dim & 1)) return ORC_EINVAL;
+  const int64_t half = rope_dim / 2;
+  for (int64_t i = 0; i < half; ++i) {
+    const double theta =
+        (double)pos * pow(base, -2.0 * (double)i / (double)rope_dim);
+    const double c = cos(theta), s = sin(theta);
+    const double x1 = (double)orc_bf16_to_f32(x[i]);
+    const double x2 = (double)orc_bf16_to_f32(x[i + half]);
+    out[i] = orc_f64_to_bf16(x1 * c - x2 * s);
+    out[i + half] = orc_f64_to_bf16(x2 * c + x1 * s);
+  }
+  return ORC_OK;
+}
+
+/*
+ * The context-KV epilogue ([P2] 关键源码片段 _precompute_fused_context_kv, then
+ * [P3] 关键源码片段 dspark_mla.py): the projection output all_kv is viewed as
+ * [T, L, kv_lora_rank + pe_dim]; each (layer, token) row is split into kv_c
+ * and k_pe; kv_c goes through the layer's RMSNorm, k_pe through RoPE at the
+ * token's position; both are materialised as bf16 (the pages hold bf16
+ * all_kv_c_normed and rotated k_pe before the insert) into
+ * rows_out[L, T, kv_lora_rank + pe_dim]; then the grouped insert writes them.
+ */
+int orc_ctx_kv_epilogue(const uint16_t* all_kv, int64_t kv_layer_stride,
+                        int64_t kv_token_stride, const uint16_t* gamma,
+                        float eps, const int64_t* positions, double rope_base,
+                        int64_t num_layers, int64_t num_tokens,
+                        int64_t kv_lora_rank, int64_t pe_dim,
+                        void* const* caches, const float* scales,
+                        const int64_t* slot_mapping, int64_t slot_layer_stride,
+                        int64_t block_size, int64_t block_stride,
+                        int64_t entry_stride, int cache_dtype,
+                        uint16_t* rows_out) {
+  if (num_layers < 0 || num_tokens < 0) return ORC_EINVAL;
+  const int64_t width = kv_lora_rank + pe_dim;
+  for (int64_t l = 0; l < num_layers; ++l) {
+    for (int64_t t = 0; t < num_tokens; ++t) {
+      const uint16_t* src = all_kv + t * kv_token_stride + l * kv_layer_stride;
+      uint16_t* dst = rows_out + (l * num_tokens + t) * width;
+      int rc = orc_rmsnorm_row(src, kv_lora_rank, gamma + l * kv_lora_rank,
+                               eps, dst);
+      if (rc != ORC_OK) return rc;
+      rc = orc_rope_row(src + kv_lora_rank, pe_dim, positions[t], rope_base,
+                        dst + kv_lora_rank);
+      if (rc != ORC_OK) return rc;
+    }
+  }
+  if (!caches) return ORC_OK; /* rows only */
+  return orc_insert_grouped(rows_out, num_tokens * width, width,
+                            rows_out + kv_lora_rank, num_tokens * width, width,
+                            caches, scales, slot_mapping, slot_layer_stride,
+                            num_layers, num_tokens, kv_lora_rank, pe_dim,
+                            block_size, block_stride, entry_stride,
+                            cache_dtype);
+}
+
+/* ======================================================================== */
+/* Chunked-context gather and pack                                           */
+/* ======================================================================== */
+
+/*
+ * Gather latent rows of one sequence's context from a paged cache into a
+ * contiguous [T, width] bf16 workspace ([P1] 实现拆解 item 2:
+ * _gather_context_latent reads the context from the cache before kv_b_proj;
+ * the plain-fp8 case feeds a bf16 kv_b_proj, see the second commit's fix).
+ * Readings: the token -> slot map is a flat int64 array src_slots[T] (every
+ * entry >= 0); fp8 codes are dequantised with the cache's scale
+ * (orc_dequantize); bf16 caches are copied bit for bit.
+ */
+int orc_gather(const void* cache, int cache_dtype, float cache_scale,
+               int64_t block_size, int64_t block_stride, int64_t entry_stride,
+               const int64_t* src_slots, int64_t num_tokens, int64_t width,
+               uint16_t* out) {
+  if (num_tokens < 0 || width < 0 || block_size <= 0) return ORC_EINVAL;
+  for (int64_t j = 0; j < num_tokens; ++j) {
+    const int64_t s = src_slots[j];
+    if (s < 0) return ORC_EINVAL;
+    const int64_t entry = (s / block_size) * block_stride + (s % block_size) * entry_stride;
+    for (int64_t i = 0; i < width; ++i) {
+      if (cache_dtype == ORC_CACHE_FP8_E4M3)
+        out[j * width + i] =
+            orc_dequantize(((const uint8_t*)cache)[entry + i], cache_scale);
+      else if (cache_dtype == ORC_CACHE_BF16)
+        out[j * width + i] = ((const uint16_t*)cache)[entry + i];
+      else
+        return ORC_EINVAL;
+    }
+  }
+  return ORC_OK;
+}
+
+/*
+ * Full-key (and fp8 V) pack ([P1] 关键源码片段,
+ * fused_mla_key_concat_kv_cache.py: fused_mla_kv_concat and
+ * fused_mla_kv_concat_quant_fp8):
+ *   key[t, h, 0:nope]            = k_nope[t, h, :]
+ *   key[t, h, nope:nope+rope]    = k_pe[t, :]      (same for every head h)
+ *   v_out[t, h, :]               = v[t, h, :]      (fp8 mode only)
+ * Outputs are contiguous [T, H, nope+rope] and [T, H, v_dim].
+ * mode KEY_BF16: key is a bit copy in bf16, v is not used.
+ * mode KEY_V_FP8: every element x of key and of v becomes
+ *   encode(fl32(x) / scale) with k_scale for the key and v_scale for V.
+ * Reading: the page's op takes no scale (a plain cast, bit-identical to
+ * torch's e4m3fn cast), which is scale = 1.0.
+ */
+int orc_pack(const uint16_t* k_nope, int64_t kn_tok_stride, int64_t kn_head_stride,
+             const uint16_t* k_pe, int64_t kpe_tok_stride,
+             const uint16_t* v, int64_t v_tok_stride, int64_t v_head_stride,
+             int64_t num_tokens, int64_t num_heads, int64_t nope_dim,
+             int64_t rope_dim, int64_t v_dim, int mode, float k_scale,
+             float v_scale, void* key_out, uint8_t* v_out) {
+  if (num_tokens < 0 || num_heads < 0 || nope_dim < 0 || rope_dim < 0 || v_dim < 0)
+    return ORC_EINVAL;
+  if (mode != ORC_PACK_KEY_BF16 && mode != ORC_PACK_KEY_V_FP8) return ORC_EINVAL;
+  const int64_t kw = nope_dim + rope_dim;
+  for (int64_t t = 0; t < num_tokens; ++t) {
+    for (int64_t h = 0; h < num_heads; ++h) {
+      const int64_t ko = (t * num_heads + h) * kw;
+      const uint16_t* kn = k_nope + t * kn_tok_stride + h * kn_head_stride;
+      const uint16_t* kp = k_pe + t * kpe_tok_stride;
+      if (mode == ORC_PACK_KEY_BF16) {
+        uint16_t* key = (uint16_t*)key_out + ko;
+        for (int64_t i = 0; i < nope_dim; ++i) key[i] = kn[i];
+        for (int64_t j = 0; j < rope_dim; ++j) key[nope_dim + j] = kp[j];
+      } else {
+        uint8_t* key = (uint8_t*)key_out + ko;
+        for (int64_t i = 0; i < nope_dim; ++i) key[i] = orc_quantize(kn[i], k_scale);
+        for (int64_t j = 0; j < rope_dim; ++j)
+          key[nope_dim + j] = orc_quantize(kp[j], k_scale);
+        const uint16_t* vs = v + t * v_tok_stride + h * v_head_stride;
+        uint8_t* vo = v_out + (t * num_heads + h) * v_dim;
+        for (int64_t i = 0; i < v_dim; ++i) vo[i] = orc_quantize(vs[i], v_scale);
+      }
+    }
+  }
+  return ORC_OK;
+}
