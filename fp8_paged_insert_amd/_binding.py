@@ -1,0 +1,384 @@
+"""ctypes binding of libmla_kv.so: argument marshalling only.
+
+Every function here has the name and meaning of the C entry point declared in
+``include/mla_kv.h``; it checks what raw pointers cannot express (tensor
+dtype, device, contiguity, element counts), turns tensors into pointers,
+strides and sizes, and calls the library on the current HIP stream of the
+tensors' device.  No step of the computation runs here.  If the library is
+not built, every call raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmla_kv.so")
+
+MLA_OK = 0
+MLA_ERR_INVALID_ARGUMENT = 1
+MLA_ERR_UNSUPPORTED = 2
+MLA_ERR_MISALIGNED = 3
+MLA_ERR_DEVICE = 4
+
+MLA_KV_AUTO = 0
+MLA_KV_BF16 = 1
+MLA_KV_FP8_E4M3 = 2
+MLA_KV_FP8_E5M2 = 3
+
+MLA_PACK_KEY_BF16 = 0
+MLA_PACK_KEY_V_FP8 = 1
+
+# Every symbol include/mla_kv.h declares.
+EXPORTS = (
+    "mla_last_error", "mla_version", "mla_parse_kv_cache_dtype",
+    "mla_kv_insert_grouped", "mla_rope_cos_sin_cache", "mla_ctx_kv_epilogue",
+    "mla_ctx_kv_proj", "mla_ctx_latent_gather", "mla_ctx_kv_pack",
+)
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+_i64, _i32, _vp, _f32, _f64 = (ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                               ctypes.c_float, ctypes.c_double)
+
+_SIGS = {
+    "mla_last_error": (ctypes.c_char_p, []),
+    "mla_version": (ctypes.c_char_p, []),
+    "mla_parse_kv_cache_dtype": (_i32, [ctypes.c_char_p, ctypes.POINTER(_i32)]),
+    "mla_kv_insert_grouped": (_i32, [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _i64,
+                                     _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i32, _vp]),
+    "mla_rope_cos_sin_cache": (_i32, [_vp, _i64, _i64, _f64, _vp]),
+    "mla_ctx_kv_epilogue": (_i32, [_vp, _i64, _i64, _vp, _f32, _vp, _vp, _i64, _vp, _vp, _vp,
+                                   _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i32, _vp,
+                                   _vp]),
+    "mla_ctx_kv_proj": (_i32, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp]),
+    "mla_ctx_latent_gather": (_i32, [_vp, _i32, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp,
+                                     _i64, _vp]),
+    "mla_ctx_kv_pack": (_i32, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _i64,
+                               _i64, _i64, _i32, _vp, _vp, _vp, _vp, _i64, _vp]),
+}
+
+_lib = None
+
+
+def lib():
+    """Load libmla_kv.so (torch is imported first so both share one HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run `python -m fp8_paged_insert_amd.build` "
+            "(or __graft_entry__.build()) first -- there is no fallback path")
+    h = ctypes.CDLL(LIB_PATH, mode=ctypes.RTLD_GLOBAL)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(h, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = h
+    return h
+
+
+def last_error() -> str:
+    return lib().mla_last_error().decode()
+
+
+def version() -> str:
+    return lib().mla_version().decode()
+
+
+def _check(status: int, fn: str):
+    if status != MLA_OK:
+        raise MlaError(status, f"{fn} failed (status {status}): {last_error()}")
+
+
+def parse_kv_cache_dtype(s: str) -> int:
+    out = _i32(-1)
+    _check(lib().mla_parse_kv_cache_dtype(s.encode(), ctypes.byref(out)),
+           "mla_parse_kv_cache_dtype")
+    return out.value
+
+
+def _stream(t: torch.Tensor):
+    if t.device.type != "cuda":
+        raise RuntimeError(f"tensor on {t.device}, expected a GPU tensor")
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, dtypes, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise RuntimeError(f"{name} must have dtype {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+
+
+def _same_device(t, ref, name, ref_name):
+    if t.device != ref.device:
+        raise RuntimeError(f"{name} is not on the same CUDA device as {ref_name} "
+                           f"({t.device} vs {ref.device})")
+
+
+def _check_scales(scales, n, ref, name="kv_scales"):
+    _need(scales, (torch.float32,), name)
+    if scales.numel() != n:
+        raise RuntimeError(f"{name} must hold one scale per layer: expected {n}, got {scales.numel()}")
+    _same_device(scales, ref, name, "kv_c")
+    if not scales.is_contiguous():
+        raise RuntimeError(f"{name} must be contiguous")
+
+
+def _cache_dtype_code(kv_cache_dtype) -> int:
+    if isinstance(kv_cache_dtype, str):
+        return parse_kv_cache_dtype(kv_cache_dtype)
+    return int(kv_cache_dtype)
+
+
+def cache_ptr_table(caches, device=None) -> torch.Tensor:
+    """int64 device tensor of per-layer cache base addresses."""
+    device = device or caches[0].device
+    return torch.tensor([c.data_ptr() for c in caches], dtype=torch.int64).to(device)
+
+
+_FP8_CACHE_DTYPES = (torch.uint8, torch.float8_e4m3fn)
+
+
+def _resolve_caches(kv_caches, L, dt, width, block_size, block_stride, entry_stride, ref):
+    """Accept either an int64 device table of base addresses (the raw C form;
+    layout and dtype are then the caller's promise) or the list of per-layer
+    cache tensors, whose dtype and layout are checked against the arguments
+    before their table is built."""
+    if isinstance(kv_caches, torch.Tensor):
+        _need(kv_caches, (torch.int64,), "kv_cache_ptrs")
+        if kv_caches.numel() != L:
+            raise RuntimeError(f"kv_cache_ptrs must hold {L} addresses")
+        _same_device(kv_caches, ref, "kv_cache_ptrs", "kv_c")
+        return kv_caches
+    caches = list(kv_caches)
+    if len(caches) != L:
+        raise RuntimeError(f"expected {L} caches, got {len(caches)}")
+    want = _FP8_CACHE_DTYPES if dt == MLA_KV_FP8_E4M3 else (torch.bfloat16,)
+    c0 = caches[0]
+    for i, c in enumerate(caches):
+        _need(c, want, f"cache {i} (for kv_cache_dtype code {dt})")
+        _same_device(c, ref, f"cache {i}", "kv_c")
+        if c.dim() != 3 or c.stride() != c0.stride() or c.shape != c0.shape:
+            raise RuntimeError("all caches must be [num_blocks, block_size, entry] with one layout")
+    if c0.shape[1] != block_size or c0.stride(0) != block_stride or c0.stride(1) != entry_stride:
+        raise RuntimeError(
+            f"block_size / block_stride / entry_stride ({block_size}, {block_stride}, "
+            f"{entry_stride}) disagree with the cache layout "
+            f"({c0.shape[1]}, {c0.stride(0)}, {c0.stride(1)})")
+    if c0.stride(2) != 1 or c0.shape[2] < width:
+        raise RuntimeError(f"cache entries must hold {width} contiguous elements")
+    return cache_ptr_table(caches, ref.device)
+
+
+def _slots_2d(slot_mapping, L, T):
+    """[T] (shared) or [L, T] int64 -> (tensor, layer stride)."""
+    _need(slot_mapping, (torch.int64,), "slot_mapping")
+    if slot_mapping.dim() == 1:
+        if slot_mapping.shape[0] != T:
+            raise RuntimeError(f"slot_mapping has {slot_mapping.shape[0]} entries, expected {T}")
+        if slot_mapping.stride(0) != 1:
+            raise RuntimeError("slot_mapping must be contiguous along tokens")
+        return slot_mapping, 0
+    if tuple(slot_mapping.shape) != (L, T):
+        raise RuntimeError(f"slot_mapping shape {tuple(slot_mapping.shape)}, expected ({L}, {T})")
+    if T > 1 and slot_mapping.stride(1) != 1:
+        raise RuntimeError("slot_mapping must be contiguous along tokens")
+    return slot_mapping, slot_mapping.stride(0) if L > 1 else 0
+
+
+# ---------------------------------------------------------------------------
+def mla_kv_insert_grouped(kv_c, k_pe, kv_cache_ptrs, slot_mapping, block_size,
+                          block_stride, entry_stride, kv_scales=None,
+                          kv_cache_dtype="auto"):
+    """Grouped insert of [kv_c | k_pe] rows of every layer into its paged cache.
+
+    kv_c [L, T, R] / k_pe [L, T, P] bf16 views (innermost dim contiguous);
+    kv_cache_ptrs int64 [L] device table; slot_mapping int64 [L, T] (layer
+    stride 0 allowed) or [T] shared; block/entry strides in cache elements;
+    kv_scales fp32 [L] for fp8 caches, None otherwise.
+    """
+    _need(kv_c, (torch.bfloat16,), "kv_c")
+    _need(k_pe, (torch.bfloat16,), "k_pe")
+    if kv_c.dim() != 3 or k_pe.dim() != 3:
+        raise RuntimeError("kv_c and k_pe must be [num_layers, num_tokens, dim] views")
+    L, T, R = kv_c.shape
+    P = k_pe.shape[2]
+    if tuple(k_pe.shape[:2]) != (L, T):
+        raise RuntimeError("kv_c and k_pe disagree on layers/tokens")
+    if (R > 1 and kv_c.stride(2) != 1) or (P > 1 and k_pe.stride(2) != 1):
+        raise RuntimeError("kv_c / k_pe innermost dimension must be contiguous")
+    _same_device(k_pe, kv_c, "k_pe", "kv_c")
+    sm, sls = _slots_2d(slot_mapping, L, T)
+    _same_device(sm, kv_c, "slot_mapping", "kv_c")
+    dt = _cache_dtype_code(kv_cache_dtype)
+    kv_cache_ptrs = _resolve_caches(kv_cache_ptrs, L, dt, R + P, block_size, block_stride,
+                                    entry_stride, kv_c)
+    if dt == MLA_KV_FP8_E4M3:
+        if kv_scales is None:
+            raise RuntimeError("an fp8 cache needs kv_scales (one fp32 scale per layer)")
+        _check_scales(kv_scales, L, kv_c)
+    elif kv_scales is not None:
+        raise RuntimeError("a bf16 cache takes no kv_scales")
+    st = lib().mla_kv_insert_grouped(
+        _ptr(kv_c), kv_c.stride(0), kv_c.stride(1), _ptr(k_pe), k_pe.stride(0), k_pe.stride(1),
+        _ptr(kv_cache_ptrs), _ptr(kv_scales), _ptr(sm), sls, L, T, R, P,
+        int(block_size), int(block_stride), int(entry_stride), dt, _stream(kv_c))
+    _check(st, "mla_kv_insert_grouped")
+
+
+def mla_rope_cos_sin_cache(out, max_pos, rope_dim, base=10000.0):
+    """Fill fp32 [max_pos, rope_dim] = cos | sin table on the device."""
+    _need(out, (torch.float32,), "out")
+    if not out.is_contiguous() or out.numel() != max_pos * rope_dim:
+        raise RuntimeError("out must be a contiguous fp32 [max_pos, rope_dim] tensor")
+    _check(lib().mla_rope_cos_sin_cache(_ptr(out), int(max_pos), int(rope_dim), float(base),
+                                        _stream(out)), "mla_rope_cos_sin_cache")
+
+
+def mla_ctx_kv_epilogue(all_kv, gamma, eps, positions, cos_sin, kv_cache_ptrs, slot_mapping,
+                        block_size, block_stride, entry_stride, kv_scales=None,
+                        kv_cache_dtype="auto", kv_lora_rank=512, dbg_rows=None):
+    """RMSNorm + RoPE + quantise + grouped insert for all_kv [T, L, R+P] (bf16 view)."""
+    _need(all_kv, (torch.bfloat16,), "all_kv")
+    _need(gamma, (torch.bfloat16,), "gamma")
+    _need(positions, (torch.int64,), "positions")
+    _need(cos_sin, (torch.float32,), "cos_sin")
+    if all_kv.dim() != 3 or all_kv.stride(2) != 1:
+        raise RuntimeError("all_kv must be a [T, L, width] view with contiguous rows")
+    T, L, W = all_kv.shape
+    R = int(kv_lora_rank)
+    P = W - R
+    if tuple(gamma.shape) != (L, R) or not gamma.is_contiguous():
+        raise RuntimeError(f"gamma must be contiguous [{L}, {R}]")
+    if positions.numel() != T or not positions.is_contiguous():
+        raise RuntimeError(f"positions must be contiguous [{T}]")
+    if cos_sin.dim() != 2 or cos_sin.shape[1] != P or not cos_sin.is_contiguous():
+        raise RuntimeError(f"cos_sin must be contiguous [max_pos, {P}]")
+    for t, n in ((gamma, "gamma"), (positions, "positions"), (cos_sin, "cos_sin")):
+        _same_device(t, all_kv, n, "all_kv")
+    sm, sls = _slots_2d(slot_mapping, L, T)
+    _same_device(sm, all_kv, "slot_mapping", "all_kv")
+    dt = _cache_dtype_code(kv_cache_dtype)
+    kv_cache_ptrs = _resolve_caches(kv_cache_ptrs, L, dt, W, block_size, block_stride,
+                                    entry_stride, all_kv)
+    if dt == MLA_KV_FP8_E4M3:
+        if kv_scales is None:
+            raise RuntimeError("an fp8 cache needs kv_scales (one fp32 scale per layer)")
+        _check_scales(kv_scales, L, all_kv)
+    elif kv_scales is not None:
+        raise RuntimeError("a bf16 cache takes no kv_scales")
+    if dbg_rows is not None:
+        _need(dbg_rows, (torch.bfloat16,), "dbg_rows")
+        if tuple(dbg_rows.shape) != (L, T, W) or not dbg_rows.is_contiguous():
+            raise RuntimeError(f"dbg_rows must be contiguous [{L}, {T}, {W}]")
+    st = lib().mla_ctx_kv_epilogue(
+        _ptr(all_kv), all_kv.stride(1), all_kv.stride(0), _ptr(gamma), float(eps),
+        _ptr(positions), _ptr(cos_sin), cos_sin.shape[0], _ptr(kv_cache_ptrs), _ptr(kv_scales),
+        _ptr(sm), sls, L, T, R, P, int(block_size), int(block_stride), int(entry_stride), dt,
+        _ptr(dbg_rows), _stream(all_kv))
+    _check(st, "mla_ctx_kv_epilogue")
+
+
+def mla_ctx_kv_proj(x, w_nk, y):
+    """y[T, N] = x[T, K] . w_nk[N, K]^T (bf16 in/out, fp32 accumulation)."""
+    for t, n in ((x, "x"), (w_nk, "w_nk"), (y, "y")):
+        _need(t, (torch.bfloat16,), n)
+        if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+            raise RuntimeError(f"{n} must be a 2-D row-major matrix")
+    T, K = x.shape
+    N = w_nk.shape[0]
+    if w_nk.shape[1] != K or tuple(y.shape) != (T, N):
+        raise RuntimeError("shape mismatch: x [T, K], w_nk [N, K], y [T, N]")
+    _same_device(w_nk, x, "w_nk", "x")
+    _same_device(y, x, "y", "x")
+    _check(lib().mla_ctx_kv_proj(_ptr(x), x.stride(0), T, K, _ptr(w_nk), N, _ptr(y),
+                                 y.stride(0), _stream(x)), "mla_ctx_kv_proj")
+
+
+def mla_ctx_latent_gather(cache, src_slots, out, cache_scale=None, kv_cache_dtype="fp8",
+                          max_blocks=0):
+    """out[j, :] = dequant(cache row of src_slots[j]); cache [num_blocks, block_size, E]."""
+    _need(src_slots, (torch.int64,), "src_slots")
+    _need(out, (torch.bfloat16,), "out")
+    dt = _cache_dtype_code(kv_cache_dtype)
+    if dt == MLA_KV_FP8_E4M3:
+        _need(cache, (torch.uint8, torch.float8_e4m3fn), "cache")
+        if cache_scale is None:
+            raise RuntimeError("an fp8 cache needs cache_scale")
+        _check_scales(cache_scale, 1, cache, "cache_scale")
+    else:
+        _need(cache, (torch.bfloat16,), "cache")
+        if cache_scale is not None:
+            raise RuntimeError("a bf16 cache takes no cache_scale")
+    if cache.dim() != 3 or cache.stride(2) != 1:
+        raise RuntimeError("cache must be a [num_blocks, block_size, entry] view")
+    T = src_slots.numel()
+    if out.dim() != 2 or out.shape[0] != T or not out.is_contiguous():
+        raise RuntimeError(f"out must be contiguous [{T}, width]")
+    if not src_slots.is_contiguous():
+        raise RuntimeError("src_slots must be contiguous")
+    _same_device(src_slots, cache, "src_slots", "cache")
+    _same_device(out, cache, "out", "cache")
+    st = lib().mla_ctx_latent_gather(
+        _ptr(cache), dt, _ptr(cache_scale), cache.shape[1], cache.stride(0), cache.stride(1),
+        _ptr(src_slots), T, out.shape[1], _ptr(out), int(max_blocks), _stream(cache))
+    _check(st, "mla_ctx_latent_gather")
+
+
+def mla_ctx_kv_pack(k_nope, k_pe, key_out, v=None, v_out=None, mode=MLA_PACK_KEY_BF16,
+                    k_scale=None, v_scale=None, max_blocks=0):
+    """Contiguous full key [T, H, nope+rope] (+ fp8 V) from strided k_nope / k_pe / v."""
+    _need(k_nope, (torch.bfloat16,), "k_nope")
+    _need(k_pe, (torch.bfloat16,), "k_pe")
+    if k_pe.dim() == 3:  # [T, 1, rope]
+        k_pe = k_pe.reshape(k_pe.shape[0], k_pe.shape[-1])
+    T, H, nope = k_nope.shape
+    rope = k_pe.shape[1]
+    if (nope > 1 and k_nope.stride(2) != 1) or (rope > 1 and k_pe.stride(1) != 1):
+        raise RuntimeError("k_nope / k_pe innermost dimension must be contiguous")
+    if k_pe.shape[0] != T:
+        raise RuntimeError("k_pe must have one row per token")
+    _same_device(k_pe, k_nope, "k_pe", "k_nope")
+    _same_device(key_out, k_nope, "key_out", "k_nope")
+    if not key_out.is_contiguous() or tuple(key_out.shape) != (T, H, nope + rope):
+        raise RuntimeError(f"key_out must be contiguous [{T}, {H}, {nope + rope}]")
+    vd = vts = vhs = 0
+    if mode == MLA_PACK_KEY_BF16:
+        _need(key_out, (torch.bfloat16,), "key_out")
+        if v is not None or v_out is not None or k_scale is not None or v_scale is not None:
+            raise RuntimeError("bf16 key mode takes no v, v_out or scales")
+    elif mode == MLA_PACK_KEY_V_FP8:
+        _need(key_out, (torch.uint8, torch.float8_e4m3fn), "key_out")
+        _need(v, (torch.bfloat16,), "v")
+        _need(v_out, (torch.uint8, torch.float8_e4m3fn), "v_out")
+        if tuple(v.shape[:2]) != (T, H) or (v.shape[2] > 1 and v.stride(2) != 1):
+            raise RuntimeError("v must be a [T, H, vdim] view with contiguous rows")
+        vd, vts, vhs = v.shape[2], v.stride(0), v.stride(1)
+        if not v_out.is_contiguous() or tuple(v_out.shape) != (T, H, vd):
+            raise RuntimeError(f"v_out must be contiguous [{T}, {H}, {vd}]")
+        _same_device(v, k_nope, "v", "k_nope")
+        _same_device(v_out, k_nope, "v_out", "k_nope")
+        for sc, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+            if sc is not None:
+                _check_scales(sc, 1, k_nope, n)
+    else:
+        raise RuntimeError(f"unknown pack mode {mode}")
+    st = lib().mla_ctx_kv_pack(
+        _ptr(k_nope), k_nope.stride(0), k_nope.stride(1), _ptr(k_pe), k_pe.stride(0), _ptr(v),
+        vts, vhs, T, H, nope, rope, vd, int(mode), _ptr(k_scale), _ptr(v_scale), _ptr(key_out),
+        _ptr(v_out), int(max_blocks), _stream(k_nope))
+    _check(st, "mla_ctx_kv_pack")

@@ -1,0 +1,306 @@
+// gather_pack.hip -- chunked-context gather from the paged latent cache and
+// the full-key / fp8-V pack.
+//
+// Page: "PR #51772 完整报告" ([Attention][MLA] Fuse Kimi-K3 chunked-context
+// K/V packing).  实现拆解 item 1: one kernel per chunk reads the strided
+// kv_b_proj halves (k_nope, v) and the gathered k_pe directly, writes a
+// contiguous key [k_nope | k_pe] (and, for fp8, a contiguous fp8 V), with a
+// capped grid and a grid-stride loop for long contexts.  实现拆解 item 2: the
+// context latent is gathered from the cache before kv_b_proj; item 5: with a
+// plain fp8 cache the gathered latent must reach a bf16 kv_b_proj as bf16.
+// 关键源码片段 (fused_mla_key_concat_kv_cache.py): output shapes and the
+// bit-identity of the fp8 cast with torch's float8_e4m3fn cast.
+//
+// gfx950 design: both kernels walk a flat list of 16-byte output chunks, so
+// every store is a full 16-byte vector and consecutive lanes write
+// consecutive addresses of the contiguous outputs; loads are 16/32-byte
+// vectors along the contiguous rows of the strided inputs.  The k_pe row of
+// a token is read once per head from L2 (it is 128 bytes shared by H heads).
+#include "mla_common.hpp"
+
+namespace mla {
+namespace {
+
+// ----------------------------------------------------------------- gather --
+struct GatherArgs {
+  const uint8_t* cache;  // bytes
+  const float* scale;
+  const int64_t* slots;
+  uint16_t* out;
+  int64_t block_size, block_stride, entry_stride;  // cache elements
+  int64_t width;                                    // output row length
+  FastDiv per_row, bsize;
+  uint32_t total;
+};
+
+template <bool kFp8>
+__global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
+  constexpr int E = kFp8 ? 16 : 8;  // elements per chunk
+  const uint32_t stride = gridDim.x * blockDim.x;
+  float sc = 1.0f;
+  if constexpr (kFp8) sc = a.scale[0];
+  for (uint32_t item = blockIdx.x * blockDim.x + threadIdx.x; item < a.total; item += stride) {
+    const uint32_t j = fdiv(item, a.per_row);
+    const uint32_t c = item - j * a.per_row.d;
+    const int64_t s = a.slots[j];
+    int64_t blk, off;
+    if (s < 0x80000000LL) {
+      const uint32_t b32 = fdiv(static_cast<uint32_t>(s), a.bsize);
+      blk = b32;
+      off = static_cast<uint32_t>(s) - b32 * a.bsize.d;
+    } else {
+      blk = s / a.block_size;
+      off = s - blk * a.block_size;
+    }
+    const int64_t src_el = blk * a.block_stride + off * a.entry_stride + int64_t(c) * E;
+    uint16_t* dst = a.out + int64_t(j) * a.width + int64_t(c) * E;
+    if constexpr (kFp8) {
+      const uint4 q = ld16(a.cache + src_el);
+      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+      uint32_t o[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float f[4];
+        dec4_e4m3(w[i], f);
+        uint32_t b[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          // The converter's NaN does not keep the code's sign: rebuild it.
+          const uint32_t code = (w[i] >> (8 * k)) & 0xFFu;
+          b[k] = (code & 0x7Fu) == 0x7Fu ? (0x7FC0u | ((code & 0x80u) << 8))
+                                         : f32_to_bf16_bits(f[k] * sc);
+        }
+        o[2 * i] = b[0] | (b[1] << 16);
+        o[2 * i + 1] = b[2] | (b[3] << 16);
+      }
+      st16(dst, make_uint4(o[0], o[1], o[2], o[3]));
+      st16(dst + 8, make_uint4(o[4], o[5], o[6], o[7]));
+    } else {
+      st16(dst, ld16(reinterpret_cast<const uint16_t*>(a.cache) + src_el));
+    }
+  }
+}
+
+// ------------------------------------------------------------------- pack --
+struct PackArgs {
+  const uint16_t* k_nope;
+  int64_t kn_ts, kn_hs;
+  const uint16_t* k_pe;
+  int64_t pe_ts;
+  const uint16_t* v;
+  int64_t v_ts, v_hs;
+  const float* k_scale;
+  const float* v_scale;
+  void* key_out;
+  uint8_t* v_out;
+  FastDiv key_per_row;  // output chunks per (t, h) key row
+  FastDiv v_per_row;    // output chunks per (t, h) V row
+  FastDiv heads;
+  uint32_t nope_chunks;  // key chunks taken from k_nope
+  uint32_t key_total;    // T * H * key_per_row
+  uint32_t total;        // key_total (+ T * H * v_per_row in fp8 mode)
+};
+
+__global__ __launch_bounds__(256) void pack_bf16_kernel(const PackArgs a) {
+  constexpr int E = 8;
+  const uint32_t stride = gridDim.x * blockDim.x;
+  uint16_t* key = static_cast<uint16_t*>(a.key_out);
+  for (uint32_t item = blockIdx.x * blockDim.x + threadIdx.x; item < a.total; item += stride) {
+    const uint32_t row = fdiv(item, a.key_per_row);
+    const uint32_t c = item - row * a.key_per_row.d;
+    const uint32_t t = fdiv(row, a.heads);
+    const uint32_t h = row - t * a.heads.d;
+    const uint16_t* src = c < a.nope_chunks
+                              ? a.k_nope + int64_t(t) * a.kn_ts + int64_t(h) * a.kn_hs + c * E
+                              : a.k_pe + int64_t(t) * a.pe_ts + (c - a.nope_chunks) * E;
+    st16(key + int64_t(item) * E, ld16(src));
+  }
+}
+
+template <bool kScaled>
+__global__ __launch_bounds__(256) void pack_fp8_kernel(const PackArgs a) {
+  constexpr int E = 16;
+  const uint32_t stride = gridDim.x * blockDim.x;
+  float ks = 1.0f, vs = 1.0f;
+  if constexpr (kScaled) {
+    if (a.k_scale) ks = a.k_scale[0];
+    if (a.v_scale) vs = a.v_scale[0];
+  }
+  const float kr = 1.0f / ks, vr = 1.0f / vs;
+  uint8_t* key = static_cast<uint8_t*>(a.key_out);
+  for (uint32_t item = blockIdx.x * blockDim.x + threadIdx.x; item < a.total; item += stride) {
+    const uint16_t* src;
+    uint8_t* dst;
+    float s, r;
+    if (item < a.key_total) {
+      const uint32_t row = fdiv(item, a.key_per_row);
+      const uint32_t c = item - row * a.key_per_row.d;
+      const uint32_t t = fdiv(row, a.heads);
+      const uint32_t h = row - t * a.heads.d;
+      src = c < a.nope_chunks
+                ? a.k_nope + int64_t(t) * a.kn_ts + int64_t(h) * a.kn_hs + c * E
+                : a.k_pe + int64_t(t) * a.pe_ts + (c - a.nope_chunks) * E;
+      dst = key + int64_t(item) * E;
+      s = ks;
+      r = kr;
+    } else {
+      const uint32_t vi = item - a.key_total;
+      const uint32_t row = fdiv(vi, a.v_per_row);
+      const uint32_t c = vi - row * a.v_per_row.d;
+      const uint32_t t = fdiv(row, a.heads);
+      const uint32_t h = row - t * a.heads.d;
+      src = a.v + int64_t(t) * a.v_ts + int64_t(h) * a.v_hs + c * E;
+      dst = a.v_out + int64_t(vi) * E;
+      s = vs;
+      r = vr;
+    }
+    const uint4 x0 = ld16(src);
+    const uint4 x1 = ld16(src + 8);
+    st16(dst, quant16<kScaled>(x0, x1, s, r));
+  }
+}
+
+int64_t grid_for(int64_t total, int64_t max_blocks) {
+  const int64_t cap = max_blocks > 0 ? max_blocks : default_grid_cap();
+  return std::max<int64_t>(1, std::min<int64_t>(ceil_div(total, 256), cap));
+}
+
+}  // namespace
+}  // namespace mla
+
+using namespace mla;
+
+extern "C" int32_t mla_ctx_latent_gather(const void* cache, int32_t cache_dtype,
+                                         const float* cache_scale, int64_t block_size,
+                                         int64_t block_stride, int64_t entry_stride,
+                                         const int64_t* src_slots, int64_t num_tokens,
+                                         int64_t width, void* out, int64_t max_blocks,
+                                         mla_stream_t stream) {
+  static const char* fn = "mla_ctx_latent_gather";
+  clear_error();
+  int32_t st;
+  switch (cache_dtype) {
+    case MLA_KV_AUTO:
+    case MLA_KV_BF16:
+      if (cache_scale)
+        return fail(MLA_ERR_INVALID_ARGUMENT, "%s: a bf16 cache takes no cache_scale", fn);
+      break;
+    case MLA_KV_FP8_E4M3:
+      if (!cache_scale)
+        return fail(MLA_ERR_INVALID_ARGUMENT, "%s: an fp8 cache needs cache_scale", fn);
+      break;
+    default:
+      st = check_cache_dtype(fn, cache_dtype, cache_scale);
+      return st != MLA_OK ? st : fail(MLA_ERR_INVALID_ARGUMENT, "%s: bad cache dtype", fn);
+  }
+  if (num_tokens < 0 || width < 0 || max_blocks < 0)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: negative size", fn);
+  if (block_size <= 0 || block_stride <= 0 || entry_stride <= 0)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: block_size and strides must be positive", fn);
+  if (width > entry_stride)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: width %lld exceeds entry_stride %lld", fn,
+                (long long)width, (long long)entry_stride);
+  if (num_tokens == 0 || width == 0) return MLA_OK;
+  if (!cache || !src_slots || !out)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: NULL cache, src_slots or out", fn);
+  if (width % 16 != 0)
+    return fail(MLA_ERR_UNSUPPORTED, "%s: width must be a multiple of 16", fn);
+  const bool fp8 = is_fp8(cache_dtype);
+  const int64_t eb = fp8 ? 1 : 2;
+  if (!aligned16(cache) || !aligned16(out) || !bytes16(block_stride, eb) ||
+      !bytes16(entry_stride, eb))
+    return fail(MLA_ERR_MISALIGNED, "%s: cache/out addresses and cache strides must be "
+                "multiples of 16 bytes", fn);
+  const int64_t E = fp8 ? 16 : 8;
+  const int64_t per_row = width / E;
+  const int64_t total = num_tokens * per_row;
+  if (total >= (int64_t(1) << 31) || block_size > 0x7FFFFFFF)
+    return fail(MLA_ERR_UNSUPPORTED, "%s: too many tokens for one launch", fn);
+  GatherArgs a;
+  a.cache = static_cast<const uint8_t*>(cache);
+  a.scale = cache_scale;
+  a.slots = src_slots;
+  a.out = static_cast<uint16_t*>(out);
+  a.block_size = block_size;
+  a.block_stride = block_stride;
+  a.entry_stride = entry_stride;
+  a.width = width;
+  a.per_row = make_fastdiv(static_cast<uint32_t>(per_row));
+  a.bsize = make_fastdiv(static_cast<uint32_t>(block_size));
+  a.total = static_cast<uint32_t>(total);
+  auto s = static_cast<hipStream_t>(stream);
+  const int64_t blocks = grid_for(total, max_blocks);
+  if (fp8)
+    hipLaunchKernelGGL(gather_kernel<true>, dim3(blocks), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(gather_kernel<false>, dim3(blocks), dim3(256), 0, s, a);
+  return launch_status(fn);
+}
+
+extern "C" int32_t mla_ctx_kv_pack(const void* k_nope, int64_t kn_tok_stride,
+                                   int64_t kn_head_stride, const void* k_pe,
+                                   int64_t kpe_tok_stride, const void* v,
+                                   int64_t v_tok_stride, int64_t v_head_stride,
+                                   int64_t num_tokens, int64_t num_heads, int64_t nope,
+                                   int64_t rope, int64_t vdim, int32_t mode,
+                                   const float* k_scale, const float* v_scale,
+                                   void* key_out, void* v_out, int64_t max_blocks,
+                                   mla_stream_t stream) {
+  static const char* fn = "mla_ctx_kv_pack";
+  clear_error();
+  if (mode != MLA_PACK_KEY_BF16 && mode != MLA_PACK_KEY_V_FP8)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: unknown mode %d", fn, mode);
+  const bool fp8 = mode == MLA_PACK_KEY_V_FP8;
+  if (num_tokens < 0 || num_heads < 0 || nope < 0 || rope < 0 || vdim < 0 || max_blocks < 0)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: negative size", fn);
+  if (!fp8 && (v || v_out || k_scale || v_scale))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: bf16 key mode takes no v, v_out or scales", fn);
+  if (num_tokens == 0 || num_heads == 0) return MLA_OK;
+  if (nope + rope == 0)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: empty key rows", fn);
+  if (!k_nope || (rope > 0 && !k_pe) || !key_out || (fp8 && vdim > 0 && (!v || !v_out)))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: NULL input or output", fn);
+  if (nope % 16 || rope % 16 || vdim % 16)
+    return fail(MLA_ERR_UNSUPPORTED, "%s: nope, rope and vdim must be multiples of 16", fn);
+  if (!aligned16(k_nope) || !aligned16(k_pe) || !aligned16(key_out) || !aligned16(v) ||
+      !aligned16(v_out) || !bytes16(kn_tok_stride, 2) || !bytes16(kn_head_stride, 2) ||
+      !bytes16(kpe_tok_stride, 2) || !bytes16(v_tok_stride, 2) || !bytes16(v_head_stride, 2))
+    return fail(MLA_ERR_MISALIGNED, "%s: addresses and strides must be multiples of 16 bytes",
+                fn);
+  const int64_t E = fp8 ? 16 : 8;
+  const int64_t key_per_row = (nope + rope) / E;
+  const int64_t v_per_row = fp8 ? vdim / E : 0;
+  const int64_t rows = num_tokens * num_heads;
+  const int64_t key_total = rows * key_per_row;
+  const int64_t total = key_total + rows * v_per_row;
+  if (total >= (int64_t(1) << 31) || num_heads > 0x7FFFFFFF)
+    return fail(MLA_ERR_UNSUPPORTED, "%s: too many rows for one launch; split the chunk", fn);
+  PackArgs a;
+  a.k_nope = static_cast<const uint16_t*>(k_nope);
+  a.kn_ts = kn_tok_stride;
+  a.kn_hs = kn_head_stride;
+  a.k_pe = static_cast<const uint16_t*>(k_pe);
+  a.pe_ts = kpe_tok_stride;
+  a.v = static_cast<const uint16_t*>(v);
+  a.v_ts = v_tok_stride;
+  a.v_hs = v_head_stride;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.key_out = key_out;
+  a.v_out = static_cast<uint8_t*>(v_out);
+  a.key_per_row = make_fastdiv(static_cast<uint32_t>(key_per_row));
+  a.v_per_row = make_fastdiv(static_cast<uint32_t>(v_per_row > 0 ? v_per_row : 1));
+  a.heads = make_fastdiv(static_cast<uint32_t>(num_heads));
+  a.nope_chunks = static_cast<uint32_t>(nope / E);
+  a.key_total = static_cast<uint32_t>(key_total);
+  a.total = static_cast<uint32_t>(total);
+  auto s = static_cast<hipStream_t>(stream);
+  const int64_t blocks = grid_for(total, max_blocks);
+  if (!fp8)
+    hipLaunchKernelGGL(pack_bf16_kernel, dim3(blocks), dim3(256), 0, s, a);
+  else if (k_scale || v_scale)
+    hipLaunchKernelGGL(pack_fp8_kernel<true>, dim3(blocks), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(pack_fp8_kernel<false>, dim3(blocks), dim3(256), 0, s, a);
+  return launch_status(fn);
+}

@@ -136,7 +136,7 @@ def grouped_test_shape(device="cpu", seed=42, shared=False, fp8=True):
 
 
 def context_epilogue(device="cpu", seed=3, num_tokens=4096, hidden=7168,
-                     num_blocks=512, with_gemm=True):
+                     num_blocks=512, with_gemm=True, fp8=True):
     g = gen(seed, device)
     L, T = NUM_LAYERS, num_tokens
     N = L * KV_WIDTH
@@ -147,7 +147,8 @@ def context_epilogue(device="cpu", seed=3, num_tokens=4096, hidden=7168,
     d["gamma"] = bf16_uniform((L, KV_LORA_RANK), 0.8, 1.2, g, device)
     d["positions"] = torch.arange(T, dtype=torch.int64, device=device)
     d["scales"] = f32_uniform((L,), 0.5, 2.0, g, device)
-    d["caches"] = [random_bytes((num_blocks, 64, KV_WIDTH), g, device) for _ in range(L)]
+    fill = random_bytes if fp8 else random_bf16_bits
+    d["caches"] = [fill((num_blocks, 64, KV_WIDTH), g, device) for _ in range(L)]
     d["slot_mapping"] = torch.stack(
         [randperm(num_blocks * 64, g, device)[:T] for _ in range(L)])
     # Stand-in for the projection output when the epilogue is checked on its

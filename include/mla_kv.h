@@ -1,0 +1,249 @@
+/*
+ * mla_kv.h -- C ABI of the MI355X (gfx950) MLA latent-KV library.
+ *
+ * The library computes the data-parallel path around the MLA latent KV cache
+ * of a multi-layer draft model:
+ *   projection  mla_ctx_kv_proj        Y = X . W  (one KV-only GEMM for all layers)
+ *   epilogue    mla_ctx_kv_epilogue    RMSNorm(kv_c) | RoPE(k_pe) -> fp8/bf16 -> paged caches
+ *   insert      mla_kv_insert_grouped  [kv_c | k_pe] -> fp8/bf16 -> paged caches, all layers
+ *   gather      mla_ctx_latent_gather  paged cache rows -> contiguous bf16 workspace
+ *   pack        mla_ctx_kv_pack        [k_nope | k_pe] full key (+ fp8 V), contiguous
+ *
+ * Pages cited (title and section heading):
+ *   [P1] "PR #51772 完整报告" -- [Attention][MLA] Fuse Kimi-K3 chunked-context K/V packing
+ *   [P2] "PR #50585 完整报告" -- [K3 Perf] Optimize k3 dspark fused kv
+ *   [P3] "PR #55356 完整报告" -- [Kimi Perf] Group fp8 mla cache insertion
+ *
+ * Conventions for every entry point
+ *   - Pointers marked "device" are HIP device pointers the caller owns; the
+ *     library never allocates, frees or retains them.  Host pointers are
+ *     marked "host".  Buffers must stay alive until the stream work is done.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream) and is asynchronous; nothing synchronises inside the library.
+ *   - Strides are in ELEMENTS of the array they describe.
+ *   - bf16 arrays hold IEEE bfloat16; fp8 arrays hold OCP e4m3fn codes
+ *     (bias 7, no infinity, NaN = 0x7F/0xFF, max 448) -- the
+ *     torch.float8_e4m3fn format.
+ *   - Arguments are validated on the host before anything is enqueued; on
+ *     any error nothing is launched, the status is returned and
+ *     mla_last_error() describes it.  Values that live in device memory
+ *     (slot numbers, cache base pointers, positions) cannot be checked from
+ *     the host: they are preconditions, stated per entry point.
+ *   - A call with zero tokens (or zero layers) succeeds without launching.
+ */
+#ifndef MLA_KV_H
+#define MLA_KV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* mla_stream_t; /* hipStream_t */
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARGUMENT = 1, /* bad size, null pointer, wrong dtype/scale combination */
+  MLA_ERR_UNSUPPORTED = 2,      /* a valid request this build does not implement */
+  MLA_ERR_MISALIGNED = 3,       /* a pointer or stride breaks 16-byte row alignment */
+  MLA_ERR_DEVICE = 4            /* the HIP runtime reported an error at launch */
+} mla_status_t;
+
+/* KV cache element type.  [P3] 实现拆解 item 3 and 关键源码片段
+ * (cache_kernels.cu host checks): "auto" and "bfloat16" store raw bf16,
+ * "fp8" and "fp8_e4m3" store e4m3fn scaled per layer; "fp8_e5m2" is rejected
+ * on ROCm by the page's host code, and is UNSUPPORTED here as well. */
+typedef enum {
+  MLA_KV_AUTO = 0,
+  MLA_KV_BF16 = 1,
+  MLA_KV_FP8_E4M3 = 2,
+  MLA_KV_FP8_E5M2 = 3
+} mla_kv_dtype_t;
+
+/* Output layout of the chunked-context pack ([P1] 关键源码片段,
+ * fused_mla_kv_concat and fused_mla_kv_concat_quant_fp8). */
+typedef enum {
+  MLA_PACK_KEY_BF16 = 0,  /* bf16 full key only */
+  MLA_PACK_KEY_V_FP8 = 1  /* fp8 full key and fp8 V */
+} mla_pack_mode_t;
+
+/* Description of the last error on the calling thread ("" if none). */
+const char* mla_last_error(void);
+
+/* Library version string, e.g. "mla_kv 0.1.0 gfx950". */
+const char* mla_version(void);
+
+/* Parse a KV-cache dtype string into *out.  Accepts "auto", "bfloat16",
+ * "fp8", "fp8_e4m3" (MLA_OK); "fp8_e5m2" gives MLA_ERR_UNSUPPORTED; anything
+ * else MLA_ERR_INVALID_ARGUMENT.  Same whitelist as [P3] 关键源码片段
+ * (_GROUPED_KV_CACHE_DTYPES and the host checks of cache_kernels.cu). */
+int32_t mla_parse_kv_cache_dtype(const char* s, int32_t* out);
+
+/* ------------------------------------------------------------------------
+ * mla_kv_insert_grouped -- grouped concat-and-cache over all layers in one
+ * launch ([P3] 功能与动机, 实现拆解 items 2-3, 关键源码片段 cache_kernels.cu).
+ *
+ * For every layer l < num_layers and token t < num_tokens:
+ *   s = slot_mapping[l * slot_layer_stride + t]      (device int64)
+ *   if s < 0 the token is skipped for that layer;
+ *   else block = s / block_size, offset = s % block_size and the entry at
+ *     kv_cache_ptrs[l] + block * block_stride + offset * entry_stride
+ *   receives conv(kv_c[l, t, 0:kv_lora_rank]) at element 0 and
+ *   conv(k_pe[l, t, 0:pe_dim]) at element kv_lora_rank.
+ * conv is a raw 16-bit copy for AUTO/BF16 and, for FP8_E4M3,
+ *   e4m3fn(fl32(x) / kv_scales[l]) rounded to nearest-even, saturating at
+ *   +-448 (the quotient is the IEEE fp32 quotient).
+ * Result: bit-identical to num_layers independent single-layer inserts
+ * ([P3] 关键源码片段 test_cache.py).
+ *
+ * kv_c   device bf16; element [l, t, i] at l*kv_c_layer_stride + t*kv_c_token_stride + i
+ * k_pe   device bf16; element [l, t, j] at l*k_pe_layer_stride + t*k_pe_token_stride + j
+ *        (token-major [T, L, D] and layer-major [L, T, D] storage are both
+ *        expressed through the two strides)
+ * kv_cache_ptrs  device int64 [num_layers]: base address of each layer's cache
+ *        (bf16 elements for AUTO/BF16, bytes for FP8); all layers share
+ *        block_size / block_stride / entry_stride, in cache elements.
+ * kv_scales      device fp32 [num_layers] for FP8 (read when the kernel runs,
+ *        never cached by the library); must be NULL for AUTO/BF16.
+ * slot_mapping   device int64; slot_layer_stride 0 = one mapping for all layers.
+ * kv_cache_dtype an mla_kv_dtype_t.
+ *
+ * Alignment (MLA_ERR_MISALIGNED otherwise): kv_c and k_pe base addresses and
+ * their strides (in bytes) multiples of 16; block_stride and entry_stride in
+ * bytes multiples of 16.  kv_lora_rank and pe_dim must be multiples of 16
+ * (MLA_ERR_UNSUPPORTED otherwise); entry_stride >= kv_lora_rank + pe_dim.
+ * Preconditions (not checked): each cache base is 16-byte aligned and holds
+ * every slot used; the valid slots of one layer are distinct; layers' caches
+ * do not overlap each other or the inputs.
+ * ------------------------------------------------------------------------ */
+int32_t mla_kv_insert_grouped(
+    const void* kv_c, int64_t kv_c_layer_stride, int64_t kv_c_token_stride,
+    const void* k_pe, int64_t k_pe_layer_stride, int64_t k_pe_token_stride,
+    const int64_t* kv_cache_ptrs, const float* kv_scales,
+    const int64_t* slot_mapping, int64_t slot_layer_stride,
+    int64_t num_layers, int64_t num_tokens, int64_t kv_lora_rank, int64_t pe_dim,
+    int64_t block_size, int64_t block_stride, int64_t entry_stride,
+    int32_t kv_cache_dtype, mla_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * mla_rope_cos_sin_cache -- fill the rotary table used by the epilogue.
+ * out (device fp32 [max_pos, rope_dim]) row p = cos(theta_0..theta_{d/2-1})
+ * followed by sin(theta_0..theta_{d/2-1}), theta_i = p * base^(-2i/d),
+ * evaluated in float64 on the device and rounded to fp32.
+ * ([P2] 关键源码片段: RoPE of k_pe at each context position, the positions
+ * being the same for every layer; the formula itself is not printed, the
+ * non-interleaved form with the given base is the reading taken.)
+ * rope_dim must be even and > 0; max_pos >= 0.
+ * ------------------------------------------------------------------------ */
+int32_t mla_rope_cos_sin_cache(float* out, int64_t max_pos, int64_t rope_dim,
+                               double base, mla_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * mla_ctx_kv_epilogue -- fused context-KV epilogue for all layers in one
+ * launch: per-layer RMSNorm of kv_c, RoPE of k_pe, bf16 rounding, then the
+ * grouped insert ([P2] 关键源码片段 _precompute_fused_context_kv; [P3]
+ * 关键源码片段 dspark_mla.py grouped path).
+ *
+ * all_kv  device bf16, the projection output viewed as [T, L, kv_lora_rank + pe_dim]:
+ *         element [t, l, i] at t*kv_token_stride + l*kv_layer_stride + i
+ *         (for a [T, L*576] GEMM output: kv_token_stride = L*576, kv_layer_stride = 576).
+ * gamma   device bf16 [num_layers, kv_lora_rank] (row l = layer l's norm weight).
+ * eps     RMSNorm epsilon.
+ * positions device int64 [num_tokens], each in [0, max_pos).
+ * cos_sin device fp32 [max_pos, pe_dim] from mla_rope_cos_sin_cache.
+ * For each (l, t):
+ *   row[0:R]   = bf16(x_i * (mean(x^2) + eps)^(-1/2) * gamma[l, i])  (fp32 math)
+ *   row[R:R+P] = bf16(rotation of k_pe by theta(positions[t]))   (pairs (i, i+P/2))
+ *   then row is inserted exactly as mla_kv_insert_grouped inserts [kv_c | k_pe].
+ * dbg_rows  optional device bf16 [L, T, R+P] contiguous: receives every row
+ *   (also those whose slot is negative); NULL to skip.
+ * Cache, scale, slot and alignment arguments as mla_kv_insert_grouped; in
+ * addition all_kv and its strides must be 16-byte aligned, kv_lora_rank must
+ * be 512 and pe_dim 64 (MLA_ERR_UNSUPPORTED otherwise).
+ * ------------------------------------------------------------------------ */
+int32_t mla_ctx_kv_epilogue(
+    const void* all_kv, int64_t kv_layer_stride, int64_t kv_token_stride,
+    const void* gamma, float eps, const int64_t* positions, const float* cos_sin,
+    int64_t max_pos,
+    const int64_t* kv_cache_ptrs, const float* kv_scales,
+    const int64_t* slot_mapping, int64_t slot_layer_stride,
+    int64_t num_layers, int64_t num_tokens, int64_t kv_lora_rank, int64_t pe_dim,
+    int64_t block_size, int64_t block_stride, int64_t entry_stride,
+    int32_t kv_cache_dtype, void* dbg_rows, mla_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * mla_ctx_kv_proj -- the fused KV-only context projection: one GEMM producing
+ * the latent KV of every draft layer at once ([P2] 功能与动机, 实现拆解 item 2:
+ * hidden -> L * 576 instead of L projections hidden -> 2112).
+ *   Y[t, n] = bf16( sum_k X[t, k] * W[n, k] )   fp32 accumulation (MFMA)
+ * X device bf16 [T, K] row-major (row stride x_row_stride, elements).
+ * W device bf16 [N, K] row-major: the linear layer's [out, in] weight
+ *   storage, i.e. the transpose of the [K, N] matrix X is multiplied by.
+ * Y device bf16 [T, N] row-major (row stride y_row_stride).
+ * K must be a multiple of 64 and N a multiple of 16; pointers and row
+ * strides 16-byte aligned.  T may be any value >= 0.
+ * ------------------------------------------------------------------------ */
+int32_t mla_ctx_kv_proj(const void* X, int64_t x_row_stride, int64_t T,
+                        int64_t K, const void* W, int64_t N, void* Y,
+                        int64_t y_row_stride, mla_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * mla_ctx_latent_gather -- read one sequence's context rows out of a paged
+ * latent cache into a contiguous bf16 workspace ([P1] 实现拆解 item 2:
+ * _gather_context_latent before kv_b_proj; the plain-fp8 cache case must feed
+ * a bf16 kv_b_proj, as the second commit's fix in 实现拆解 item 5 requires).
+ *   s = src_slots[j]; row = cache + (s / block_size) * block_stride
+ *                               + (s % block_size) * entry_stride
+ *   out[j, i] = bf16(fl32(e4m3fn(row[i])) * cache_scale[0])   (FP8_E4M3)
+ *   out[j, i] = row[i]  bit for bit                            (AUTO/BF16)
+ * cache       device, element type from cache_dtype.
+ * cache_scale device fp32 [1] for FP8 (read at kernel time), NULL otherwise.
+ * src_slots   device int64 [num_tokens]; every entry >= 0 and inside the cache
+ *             (precondition).
+ * out         device bf16 [num_tokens, width] contiguous; width must be a
+ *             multiple of 16 and <= entry_stride.
+ * max_blocks  grid cap (0 = library default); the kernel loops grid-stride.
+ * ------------------------------------------------------------------------ */
+int32_t mla_ctx_latent_gather(const void* cache, int32_t cache_dtype,
+                              const float* cache_scale, int64_t block_size,
+                              int64_t block_stride, int64_t entry_stride,
+                              const int64_t* src_slots, int64_t num_tokens,
+                              int64_t width, void* out, int64_t max_blocks,
+                              mla_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * mla_ctx_kv_pack -- build the contiguous full key [k_nope | k_pe] (and, in
+ * fp8 mode, the contiguous fp8 V) of one context chunk in one launch, reading
+ * k_nope / v straight from the strided kv_b_proj output and k_pe straight
+ * from the gather workspace ([P1] 实现拆解 item 1, 关键源码片段
+ * fused_mla_key_concat_kv_cache.py).
+ *   key[t, h, 0:nope]         = k_nope[t, h, :]
+ *   key[t, h, nope:nope+rope] = k_pe[t, :]           (same for every head)
+ *   v_out[t, h, :]            = v[t, h, :]            (KEY_V_FP8 only)
+ * KEY_BF16:   key_out bf16 [T, H, nope+rope]; v, v_out, scales must be NULL.
+ * KEY_V_FP8:  key_out and v_out fp8 [T, H, nope+rope] / [T, H, vdim]; each
+ *   element x becomes e4m3fn(fl32(x) / scale), RNE, saturating at +-448;
+ *   k_scale / v_scale are device fp32 [1] or NULL for 1.0 (a plain cast,
+ *   bit-identical to torch's float8_e4m3fn cast -- the page's op has no scale).
+ * k_nope  device bf16: [t, h, i] at t*kn_tok_stride + h*kn_head_stride + i
+ * k_pe    device bf16: [t, j]    at t*kpe_tok_stride + j
+ * v       device bf16: [t, h, i] at t*v_tok_stride + h*v_head_stride + i
+ * nope, rope, vdim must be multiples of 16; pointers and strides 16-byte
+ * aligned.  max_blocks caps the grid (0 = default); the kernel loops
+ * grid-stride over T * H rows, so any T fits.
+ * ------------------------------------------------------------------------ */
+int32_t mla_ctx_kv_pack(const void* k_nope, int64_t kn_tok_stride,
+                        int64_t kn_head_stride, const void* k_pe,
+                        int64_t kpe_tok_stride, const void* v,
+                        int64_t v_tok_stride, int64_t v_head_stride,
+                        int64_t num_tokens, int64_t num_heads, int64_t nope,
+                        int64_t rope, int64_t vdim, int32_t mode,
+                        const float* k_scale, const float* v_scale,
+                        void* key_out, void* v_out, int64_t max_blocks,
+                        mla_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_KV_H */

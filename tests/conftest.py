@@ -18,3 +18,15 @@ def orc():
 
     oracle.build(force=False)
     return oracle
+
+
+@pytest.fixture(scope="session")
+def mk():
+    """The product binding; builds libmla_kv.so first if it is missing."""
+    import fp8_paged_insert_amd as mk_
+    from fp8_paged_insert_amd import build as hipbuild
+
+    if not os.path.exists(mk_.LIB_PATH):
+        hipbuild.build()
+    mk_.lib()
+    return mk_

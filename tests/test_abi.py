@@ -1,0 +1,177 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol the header
+declares, parses cache dtypes, and rejects bad arguments on the host before
+anything is enqueued (no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_kv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports(mk):
+    assert declared_functions() == sorted(mk.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(mk):
+    h = ctypes.CDLL(mk.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(h, name), name
+
+
+def test_version(mk):
+    assert "gfx950" in mk.version()
+
+
+@pytest.mark.parametrize("s,code", [("auto", 0), ("bfloat16", 1), ("fp8", 2), ("fp8_e4m3", 2)])
+def test_parse_dtype_accepts_whitelist(mk, s, code):
+    assert mk.parse_kv_cache_dtype(s) == code
+
+
+def test_parse_dtype_rejects(mk):
+    with pytest.raises(mk.MlaError) as e:
+        mk.parse_kv_cache_dtype("fp8_e5m2")
+    assert e.value.status == mk.MLA_ERR_UNSUPPORTED
+    with pytest.raises(mk.MlaError) as e:
+        mk.parse_kv_cache_dtype("int8")
+    assert e.value.status == mk.MLA_ERR_INVALID_ARGUMENT
+
+
+# Raw C calls with host-side argument errors.  Dummy non-NULL addresses are
+# never dereferenced: validation fails first.
+P16 = 0x10000  # 16-byte aligned dummy address
+P_ODD = 0x10008
+
+
+def insert_call(mk, **kw):
+    a = dict(kv_c=P16, kv_ls=512, kv_ts=2560, k_pe=P16, pe_ls=64, pe_ts=320, ptrs=P16,
+             scales=P16, slots=P16, sls=0, L=5, T=4, R=512, P=64, bs=64, bstride=64 * 576,
+             estride=576, dt=mk.MLA_KV_FP8_E4M3)
+    a.update(kw)
+    return mk.lib().mla_kv_insert_grouped(
+        a["kv_c"], a["kv_ls"], a["kv_ts"], a["k_pe"], a["pe_ls"], a["pe_ts"], a["ptrs"],
+        a["scales"], a["slots"], a["sls"], a["L"], a["T"], a["R"], a["P"], a["bs"],
+        a["bstride"], a["estride"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(dt=3), 2, "fp8_e5m2"),
+    (dict(dt=9), 1, "unknown KV cache dtype"),
+    (dict(scales=None), 1, "needs kv_scales"),
+    (dict(dt=0), 1, "takes no kv_scales"),
+    (dict(dt=1), 1, "takes no kv_scales"),
+    (dict(T=-1), 1, "negative"),
+    (dict(bs=0), 1, "positive"),
+    (dict(estride=500), 1, "smaller than the entry width"),
+    (dict(bstride=100), 1, "overlap"),
+    (dict(ptrs=None), 1, "must not be NULL"),
+    (dict(slots=None), 1, "must not be NULL"),
+    (dict(kv_c=None), 1, "must not be NULL"),
+    (dict(kv_c=P_ODD), 3, "multiples of 16 bytes"),
+    (dict(kv_ts=2564), 3, "multiples of 16 bytes"),
+    (dict(estride=584, bstride=64 * 584), 3, "multiples of 16 bytes"),
+    (dict(R=520, estride=592, bstride=64 * 592), 2, "multiples of 16"),
+])
+def test_insert_rejects_bad_arguments(mk, kw, status, msg):
+    assert insert_call(mk, **kw) == status
+    assert msg in mk.last_error()
+
+
+def test_insert_zero_tokens_or_layers_is_a_noop(mk):
+    assert insert_call(mk, T=0) == mk.MLA_OK
+    assert insert_call(mk, L=0) == mk.MLA_OK
+    assert insert_call(mk, T=0, kv_c=None, k_pe=None, ptrs=None, slots=None) == mk.MLA_OK
+
+
+def epilogue_call(mk, **kw):
+    a = dict(all_kv=P16, kls=576, kts=2880, gamma=P16, eps=1e-6, pos=P16, cs=P16, max_pos=4096,
+             ptrs=P16, scales=P16, slots=P16, sls=4096, L=5, T=4096, R=512, P=64, bs=64,
+             bstride=64 * 576, estride=576, dt=mk.MLA_KV_FP8_E4M3, dbg=None)
+    a.update(kw)
+    return mk.lib().mla_ctx_kv_epilogue(
+        a["all_kv"], a["kls"], a["kts"], a["gamma"], a["eps"], a["pos"], a["cs"], a["max_pos"],
+        a["ptrs"], a["scales"], a["slots"], a["sls"], a["L"], a["T"], a["R"], a["P"], a["bs"],
+        a["bstride"], a["estride"], a["dt"], a["dbg"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(dt=3), 2, "fp8_e5m2"),
+    (dict(scales=None), 1, "needs kv_scales"),
+    (dict(R=256, estride=320, bstride=64 * 320), 2, "kv_lora_rank 512"),
+    (dict(gamma=None), 1, "NULL"),
+    (dict(max_pos=0), 1, "max_pos"),
+    (dict(eps=-1.0), 1, "eps"),
+    (dict(kts=2881), 3, "multiples of 16 bytes"),
+    (dict(dbg=P_ODD), 3, "multiples of 16 bytes"),
+])
+def test_epilogue_rejects_bad_arguments(mk, kw, status, msg):
+    assert epilogue_call(mk, **kw) == status
+    assert msg in mk.last_error()
+
+
+def pack_call(mk, **kw):
+    a = dict(kn=P16, kn_ts=16384, kn_hs=256, kpe=P16, kpe_ts=576, v=P16, v_ts=16384,
+             v_hs=256, T=8192, H=64, nope=128, rope=64, vdim=128, mode=mk.MLA_PACK_KEY_V_FP8,
+             ks=None, vs=None, key=P16, vo=P16, maxb=0)
+    a.update(kw)
+    return mk.lib().mla_ctx_kv_pack(
+        a["kn"], a["kn_ts"], a["kn_hs"], a["kpe"], a["kpe_ts"], a["v"], a["v_ts"], a["v_hs"],
+        a["T"], a["H"], a["nope"], a["rope"], a["vdim"], a["mode"], a["ks"], a["vs"],
+        a["key"], a["vo"], a["maxb"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(mode=7), 1, "unknown mode"),
+    (dict(mode=0), 1, "takes no v"),
+    (dict(T=-1), 1, "negative"),
+    (dict(maxb=-1), 1, "negative"),
+    (dict(key=None), 1, "NULL"),
+    (dict(nope=120), 2, "multiples of 16"),
+    (dict(kn_hs=257), 3, "multiples of 16 bytes"),
+    (dict(vo=P_ODD), 3, "multiples of 16 bytes"),
+])
+def test_pack_rejects_bad_arguments(mk, kw, status, msg):
+    assert pack_call(mk, **kw) == status
+    assert msg in mk.last_error()
+
+
+def test_pack_zero_tokens_is_a_noop(mk):
+    assert pack_call(mk, T=0) == mk.MLA_OK
+    assert pack_call(mk, H=0) == mk.MLA_OK
+
+
+def gather_call(mk, **kw):
+    a = dict(cache=P16, dt=mk.MLA_KV_FP8_E4M3, scale=P16, bs=64, bstride=64 * 576,
+             estride=576, slots=P16, T=8192, width=576, out=P16, maxb=0)
+    a.update(kw)
+    return mk.lib().mla_ctx_latent_gather(
+        a["cache"], a["dt"], a["scale"], a["bs"], a["bstride"], a["estride"], a["slots"],
+        a["T"], a["width"], a["out"], a["maxb"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(scale=None), 1, "needs cache_scale"),
+    (dict(dt=1), 1, "takes no cache_scale"),
+    (dict(dt=3), 2, "fp8_e5m2"),
+    (dict(width=600), 1, "exceeds entry_stride"),
+    (dict(width=40), 2, "multiple of 16"),
+    (dict(out=None), 1, "NULL"),
+    (dict(out=P_ODD), 3, "multiples of 16 bytes"),
+])
+def test_gather_rejects_bad_arguments(mk, kw, status, msg):
+    assert gather_call(mk, **kw) == status
+    assert msg in mk.last_error()
+
+
+def test_rope_table_rejects(mk):
+    assert mk.lib().mla_rope_cos_sin_cache(P16, 10, 63, 10000.0, None) == mk.MLA_ERR_INVALID_ARGUMENT
+    assert mk.lib().mla_rope_cos_sin_cache(P16, 10, 64, -1.0, None) == mk.MLA_ERR_INVALID_ARGUMENT
+    assert mk.lib().mla_rope_cos_sin_cache(None, 0, 64, 10000.0, None) == mk.MLA_OK

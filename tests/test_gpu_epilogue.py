@@ -1,0 +1,150 @@
+"""GPU parity of mla_rope_cos_sin_cache and mla_ctx_kv_epilogue against the
+CPU oracle.
+
+Tolerances (RMSNorm / RoPE are computed in fp32 on the GPU and in float64 in
+the oracle): every normed / rotated bf16 value within 1 bf16 ulp; every fp8
+cache code within 1 code; and wherever the GPU's bf16 row value equals the
+oracle's, the fp8 code is identical (the quantisation itself is exact).
+
+Workload: the fused context-KV epilogue shape (5 layers x 4096 tokens, rows
+read straight from a [T, 5, 576] projection output, gamma ~ U(0.8, 1.2),
+eps 1e-6, positions 0..4095, per-layer fp8 scales ~ U(0.5, 2), 5 caches
+[512, 64, 576], per-layer distinct slots), fed here with a seeded stand-in for
+the projection output so that the epilogue is checked on its own inputs.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_paged_insert_amd import synth
+from gpu_util import (DEV, announce, bf16_ulps, check_slots, fp8_codes_apart, requires_gpu,
+                      to_dev, u16, u8)
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+def test_rope_table_matches_f64(mk):
+    announce("rope table")
+    P, maxp = 64, 4096
+    cs = torch.empty(maxp, P, dtype=torch.float32, device=DEV)
+    mk.mla_rope_cos_sin_cache(cs, maxp, P, 10000.0)
+    got = cs.cpu().numpy()
+    p = np.arange(maxp, dtype=np.float64)[:, None]
+    i = np.arange(P // 2, dtype=np.float64)[None, :]
+    theta = p * np.power(10000.0, -2.0 * i / P)
+    ref = np.concatenate([np.cos(theta), np.sin(theta)], axis=1).astype(np.float32)
+    ulp = np.abs(got.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+    assert (got == ref).mean() > 0.999 and np.abs(got - ref).max() <= 1.2e-7
+
+
+def run_epilogue(mk, d, dtype, dbg=True):
+    g = to_dev(d)
+    L, T = d["num_layers"], d["num_tokens"]
+    maxp = int(d["positions"].max()) + 1
+    cs = torch.empty(maxp, 64, dtype=torch.float32, device=DEV)
+    mk.mla_rope_cos_sin_cache(cs, maxp, 64, d["rope_base"])
+    rows = torch.empty(L, T, 576, dtype=torch.bfloat16, device=DEV) if dbg else None
+    caches = g["caches"]
+    check_slots(d["slot_mapping"], d["caches"][0].shape[0] * d["block_size"])
+    mk.mla_ctx_kv_epilogue(g["all_kv"], g["gamma"], d["eps"], g["positions"], cs,
+                           caches, g["slot_mapping"], d["block_size"],
+                           caches[0].stride(0), caches[0].stride(1),
+                           g["scales"] if dtype == "fp8" else None, dtype, dbg_rows=rows)
+    torch.cuda.synchronize()
+    return caches, rows
+
+
+def check(d, caches, rows, dtype):
+    L, T = d["num_layers"], d["num_tokens"]
+    ref_caches = [(u8(c) if dtype == "fp8" else u16(c)).copy() for c in d["caches"]]
+    ref_rows = oracle.ctx_kv_epilogue(u16(d["all_kv"]), u16(d["gamma"]), d["eps"],
+                                      d["positions"].numpy(), d["slot_mapping"].numpy(),
+                                      ref_caches, d["scales"].numpy() if dtype == "fp8" else None,
+                                      rope_base=d["rope_base"])
+    got_rows = u16(rows)
+    ulps = bf16_ulps(got_rows, ref_rows)
+    assert ulps.max() <= 1, f"rows differ by up to {ulps.max()} bf16 ulp"
+    sm = d["slot_mapping"].numpy()
+    same_codes = 0
+    total = 0
+    for l in range(L):
+        got = (u8(caches[l]) if dtype == "fp8" else u16(caches[l])).reshape(-1, 576)
+        ref = ref_caches[l].reshape(-1, 576)
+        init = (u8(d["caches"][l]) if dtype == "fp8" else u16(d["caches"][l])).reshape(-1, 576)
+        valid = sm[l] >= 0
+        touched = np.zeros(got.shape[0], bool)
+        touched[sm[l][valid]] = True
+        assert np.array_equal(got[~touched], init[~touched]), f"layer {l}: stray writes"
+        g_rows = got[sm[l][valid]]
+        r_rows = ref[sm[l][valid]]
+        if dtype == "fp8":
+            apart = fp8_codes_apart(g_rows, r_rows)
+            assert apart.max() <= 1, f"layer {l}: codes up to {apart.max()} apart"
+            # where the bf16 rows agree exactly, the codes must be identical
+            agree = got_rows[l][valid] == ref_rows[l][valid]
+            assert np.array_equal(g_rows[agree], r_rows[agree]), f"layer {l}"
+        else:
+            assert bf16_ulps(g_rows, r_rows).max() <= 1
+        same_codes += int((g_rows == r_rows).sum())
+        total += g_rows.size
+    announce(f"rows: {int((ulps == 0).sum())}/{ulps.size} identical, "
+             f"cache elements: {same_codes}/{total} identical")
+
+
+@pytest.mark.parametrize("dtype", ["fp8", "auto"])
+def test_epilogue_context_shape(mk, dtype):
+    announce("epilogue C3 shape", dtype)
+    d = synth.context_epilogue(with_gemm=False, fp8=dtype == "fp8")
+    caches, rows = run_epilogue(mk, d, dtype)
+    check(d, caches, rows, dtype)
+
+
+def test_epilogue_shared_slots_negative_and_random_positions(mk):
+    announce("epilogue shared/-1/positions")
+    d = synth.context_epilogue(num_tokens=300, num_blocks=8, with_gemm=False, seed=31)
+    g = torch.Generator().manual_seed(32)
+    sm = d["slot_mapping"][0].clone()
+    sm[::5] = -1
+    d["slot_mapping"] = sm.reshape(1, -1).expand(5, 300)
+    d["positions"] = torch.randint(0, 100000, (300,), generator=g, dtype=torch.int64)
+    caches, rows = run_epilogue(mk, d, "fp8")
+    check(d, caches, rows, "fp8")
+
+
+def test_epilogue_without_debug_rows_matches(mk):
+    announce("epilogue no dbg")
+    d = synth.context_epilogue(num_tokens=128, num_blocks=4, with_gemm=False, seed=41)
+    c1, rows = run_epilogue(mk, d, "fp8", dbg=True)
+    c2, _ = run_epilogue(mk, d, "fp8", dbg=False)
+    for a, b in zip(c1, c2):
+        assert torch.equal(a, b)
+
+
+def test_epilogue_one_hot_rows(mk):
+    """Closed forms through the GPU path: a one-hot kv_c row normalises to
+    sqrt(512) * gamma at its index, and k_pe one-hot at pair 0 rotates to
+    (cos pos, sin pos)."""
+    announce("epilogue one-hot")
+    T, L = 8, 5
+    all_kv = torch.zeros(T, L, 576, dtype=torch.bfloat16)
+    for t in range(T):
+        for l in range(L):
+            all_kv[t, l, (13 * t + 97 * l) % 512] = 2.0
+            all_kv[t, l, 512] = 1.0
+    d = dict(all_kv=all_kv, gamma=torch.ones(L, 512, dtype=torch.bfloat16),
+             positions=torch.arange(T, dtype=torch.int64) * 11,
+             caches=[torch.zeros(1, 64, 576, dtype=torch.bfloat16) for _ in range(L)],
+             slot_mapping=torch.arange(T, dtype=torch.int64).reshape(1, T).expand(L, T),
+             scales=torch.ones(L), num_layers=L, num_tokens=T, block_size=64, eps=0.0,
+             rope_base=10000.0)
+    _, rows = run_epilogue(mk, d, "auto")
+    r = u16(rows)
+    bf = lambda v: int(oracle.f64_to_bf16(np.array([v]))[0])
+    for t in range(T):
+        for l in range(L):
+            assert r[l, t, (13 * t + 97 * l) % 512] == bf(math.sqrt(512.0))
+            assert r[l, t, 512] == bf(math.cos(11 * t)) or bf16_ulps(r[l, t, 512], bf(math.cos(11 * t))) <= 1
+            assert bf16_ulps(r[l, t, 544], bf(math.sin(11 * t))) <= 1
