@@ -1,0 +1,446 @@
+#!/usr/bin/env python3
+"""Benchmark of the MLA latent-KV insert / gather / pack path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step = the long-context workload, end to end, on inputs already resident
+in HBM:
+  * grouped fp8 insert of 5 layers x 16384 tokens ([kv_c | k_pe] bf16 ->
+    e4m3fn with per-layer scales) into five [4096, 64, 576] paged caches;
+  * 16 chunks of 8192 context tokens (131072 in all) from a [4096, 64, 576]
+    fp8 cache: latent gather (dequantised to bf16) then the fp8 full-key + V
+    pack of that chunk's kv_b_proj output [8192, 64 heads, 128 + 128].
+The metric is effective HBM bandwidth: the algorithmic bytes every kernel of a
+step must read and write, divided by the step time.  The JSON line also
+carries the roofline of the dominant kernel (the fp8 pack), the CPU oracle
+timed on a bounded sample, and per-kernel figures of the other workloads
+(small-batch insert latency, context epilogue, chunked-context pack).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+L, R, P, W = 5, 512, 64, 576
+
+
+# ------------------------------------------------------------ byte counts --
+def insert_bytes(layers, tokens, valid_rows=None, cache_elem=1):
+    """Algorithmic bytes of one grouped insert: read bf16 kv_c + k_pe of every
+    (layer, token), the slot of every (layer, token), the per-layer scale and
+    cache pointer; write one cache entry per valid slot."""
+    valid = layers * tokens if valid_rows is None else valid_rows
+    return (layers * tokens * W * 2 + layers * tokens * 8 + layers * 12
+            + valid * W * cache_elem)
+
+
+def gather_bytes(tokens, width=W):
+    """Read one fp8 cache row and one slot per token; write a bf16 row."""
+    return tokens * width + tokens * 8 + 4 + tokens * width * 2
+
+
+def pack_fp8_bytes(tokens, heads, nope=128, rope=64, vdim=128):
+    """Read the whole kv_b_proj output (k_nope and v halves) and k_pe once per
+    token; write the fp8 key and the fp8 V."""
+    return (tokens * heads * (nope + vdim) * 2 + tokens * rope * 2
+            + tokens * heads * (nope + rope) + tokens * heads * vdim)
+
+
+def pack_bf16_bytes(tokens, heads, nope=128, rope=64):
+    return tokens * heads * nope * 2 + tokens * rope * 2 + tokens * heads * (nope + rope) * 2
+
+
+def epilogue_bytes(layers, tokens):
+    """Read the [T, L, 576] projection output, slots, positions, gamma, the
+    cos/sin rows of the positions used; write one fp8 entry per row."""
+    return (tokens * layers * W * 2 + layers * tokens * 8 + tokens * 8 + layers * R * 2
+            + tokens * P * 4 + layers * 8 + layers * tokens * W)
+
+
+# --------------------------------------------------------------- workload --
+class LongContext:
+    """Inputs of one step, generated on the device from fixed seeds."""
+
+    def __init__(self, torch, mk, dev, num_tokens=16384, num_ctx=131072, chunk=8192, heads=64):
+        from fp8_paged_insert_amd import synth
+
+        self.torch, self.mk, self.dev = torch, mk, dev
+        self.T, self.num_ctx, self.chunk, self.heads = num_tokens, num_ctx, chunk, heads
+        g = synth.gen(5, dev)
+        self.kv_c = synth.bf16_normal((L, num_tokens, R), g, dev)
+        self.k_pe = synth.bf16_normal((L, num_tokens, P), g, dev)
+        self.caches = [synth.random_bytes((4096, 64, W), g, dev) for _ in range(L)]
+        self.scales = synth.f32_uniform((L,), 0.5, 2.0, g, dev)
+        self.slots = torch.stack([synth.randperm(4096 * 64, g, dev)[:num_tokens]
+                                  for _ in range(L)])
+        self.ptrs = mk.cache_ptr_table(self.caches)
+        c = synth.context_cache(dev, seed=55, num_blocks=4096, num_ctx=num_ctx)
+        self.ctx_cache, self.src_slots = c["cache"], c["src_slots"]
+        self.ctx_scale = torch.tensor([0.5], dtype=torch.float32, device=dev)
+        g2 = synth.gen(56, dev)
+        self.kvb = [synth.kv_b_proj_output(chunk, g2, dev, heads=heads)
+                    for _ in range(num_ctx // chunk)]
+        self.ws = torch.empty(chunk, W, dtype=torch.bfloat16, device=dev)
+        self.key = torch.empty(chunk, heads, 192, dtype=torch.uint8, device=dev)
+        self.v8 = torch.empty(chunk, heads, 128, dtype=torch.uint8, device=dev)
+        self.pack_events = []
+
+    def bytes_per_step(self):
+        n = self.num_ctx // self.chunk
+        return (insert_bytes(L, self.T) + n * gather_bytes(self.chunk)
+                + n * pack_fp8_bytes(self.chunk, self.heads))
+
+    def step(self, time_pack=False):
+        mk, torch = self.mk, self.torch
+        mk.mla_kv_insert_grouped(self.kv_c, self.k_pe, self.ptrs, self.slots, 64, 64 * W, W,
+                                 self.scales, "fp8")
+        for c, kvb in enumerate(self.kvb):
+            mk.mla_ctx_latent_gather(self.ctx_cache,
+                                     self.src_slots[c * self.chunk:(c + 1) * self.chunk],
+                                     self.ws, self.ctx_scale, "fp8")
+            if time_pack:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+            mk.mla_ctx_kv_pack(kvb[..., :128], self.ws[:, 512:], self.key, v=kvb[..., 128:],
+                               v_out=self.v8, mode=mk.MLA_PACK_KEY_V_FP8)
+            if time_pack:
+                e1.record()
+                self.pack_events.append((e0, e1))
+
+
+def time_kernel(torch, fn, reps=50, warmup=5):
+    """Median device time (us) of fn() bracketed by events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    times = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    return statistics.median(times)
+
+
+def flush_llc(torch, buf):
+    buf.add_(1)  # touches 1 GiB: evicts the 256 MB last-level cache
+
+
+# ------------------------------------------------------------- components --
+def small_batch(torch, mk, dev):
+    """Small-batch grouped fp8 insert (5 layers x 4 tokens, one -1 slot)."""
+    import ctypes
+
+    from fp8_paged_insert_amd import synth
+
+    d = synth.small_batch_fp8(dev)
+    caches = d["caches"]
+    ptrs = mk.cache_ptr_table(caches)
+    sm = d["slot_mapping"]
+    kv, pe, sc = d["kv_c"], d["k_pe"], d["scales"]
+
+    def call():
+        mk.mla_kv_insert_grouped(kv, pe, ptrs, sm, 64, 64 * W, W, sc, "fp8")
+
+    lib = mk.lib()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    raw_args = (kv.data_ptr(), kv.stride(0), kv.stride(1), pe.data_ptr(), pe.stride(0),
+                pe.stride(1), ptrs.data_ptr(), sc.data_ptr(), sm.data_ptr(), 0, L, 4, R, P, 64,
+                64 * W, W, mk.MLA_KV_FP8_E4M3, stream)
+
+    def raw():
+        lib.mla_kv_insert_grouped(*raw_args)
+
+    def per_call_us(fn, n=1000):
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / n * 1e6
+
+    wall_binding = per_call_us(call)
+    wall_raw = per_call_us(raw)
+    kernel = time_kernel(torch, raw, reps=200)
+    # graph replay: 100 inserts captured once
+    graph_us = None
+    try:
+        s = torch.cuda.Stream(dev)
+        s.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(s):
+            for _ in range(3):
+                call()
+        torch.cuda.current_stream(dev).wait_stream(s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(100):
+                call()
+        torch.cuda.synchronize()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(10):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_us = (time.perf_counter() - t0) / 1000 * 1e6
+    except Exception as e:  # pragma: no cover - reported, not fatal
+        graph_us = f"unavailable: {e}"
+    # the same 20 rows as five single-layer launches
+    per_layer = []
+    for l in range(L):
+        per_layer.append((kv[l:l + 1], pe[l:l + 1], mk.cache_ptr_table([caches[l]]),
+                          sm[l].contiguous(), sc[l:l + 1]))
+
+    def five():
+        for a in per_layer:
+            mk.mla_kv_insert_grouped(a[0], a[1], a[2], a[3], 64, 64 * W, W, a[4], "fp8")
+
+    five_us = per_call_us(five, n=300)
+    return {"workload": "grouped fp8 insert, 5 layers x 4 tokens (one -1 slot)",
+            "us_per_launch_wall": round(wall_binding, 2),
+            "us_per_launch_wall_raw_abi": round(wall_raw, 2),
+            "us_kernel": round(kernel, 2),
+            "us_per_launch_graph_replay": graph_us if isinstance(graph_us, str) else round(graph_us, 2),
+            "us_five_single_layer_launches": round(five_us, 2),
+            "target_us": 10.0,
+            "bytes": insert_bytes(L, 4, valid_rows=15)}
+
+
+def context_pack_component(torch, mk, dev, flush):
+    from fp8_paged_insert_amd import synth
+
+    d = synth.context_pack(dev)
+    ws = torch.empty(8192, W, dtype=torch.bfloat16, device=dev)
+    sc = torch.tensor([0.5], device=dev)
+    kvb = d["kvb"]
+    key8 = torch.empty(8192, 64, 192, dtype=torch.uint8, device=dev)
+    v8 = torch.empty(8192, 64, 128, dtype=torch.uint8, device=dev)
+    keyb = torch.empty(8192, 64, 192, dtype=torch.bfloat16, device=dev)
+
+    def gather():
+        mk.mla_ctx_latent_gather(d["cache"], d["src_slots"], ws, sc, "fp8")
+
+    def pack8():
+        mk.mla_ctx_kv_pack(kvb[..., :128], ws[:, 512:], key8, v=kvb[..., 128:], v_out=v8,
+                           mode=mk.MLA_PACK_KEY_V_FP8)
+
+    def packb():
+        mk.mla_ctx_kv_pack(kvb[..., :128], ws[:, 512:], keyb)
+
+    out = {"workload": "chunked-context pack, 8192 tokens x 64 heads"}
+    for name, fn, nbytes in (("gather", gather, gather_bytes(8192)),
+                             ("pack_fp8", pack8, pack_fp8_bytes(8192, 64)),
+                             ("pack_bf16", packb, pack_bf16_bytes(8192, 64))):
+        # time only the kernel: events around fn, after a cache flush
+        times = []
+        for i in range(25):
+            flush_llc(torch, flush)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            if i >= 3:
+                times.append(e0.elapsed_time(e1) * 1e3)
+        us = statistics.median(times)
+        out[name] = {"us": round(us, 2), "bytes": nbytes, "GBps": round(nbytes / us / 1e3, 1),
+                     "frac_of_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+    return out
+
+
+def epilogue_component(torch, mk, dev, flush):
+    from fp8_paged_insert_amd import synth
+
+    d = synth.context_epilogue(dev, with_gemm=False)
+    T = d["num_tokens"]
+    cs = torch.empty(T, P, dtype=torch.float32, device=dev)
+    mk.mla_rope_cos_sin_cache(cs, T, P, 10000.0)
+    ptrs = mk.cache_ptr_table(d["caches"])
+
+    def epi():
+        mk.mla_ctx_kv_epilogue(d["all_kv"], d["gamma"], d["eps"], d["positions"], cs, ptrs,
+                               d["slot_mapping"], 64, 64 * W, W, d["scales"], "fp8")
+
+    times = []
+    for i in range(25):
+        flush_llc(torch, flush)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        epi()
+        e1.record()
+        e1.synchronize()
+        if i >= 3:
+            times.append(e0.elapsed_time(e1) * 1e3)
+    us = statistics.median(times)
+    nb = epilogue_bytes(L, T)
+    res = {"workload": "context-KV epilogue, 5 layers x 4096 tokens (norm+rope+fp8+scatter)",
+           "us": round(us, 2), "bytes": nb, "GBps": round(nb / us / 1e3, 1),
+           "frac_of_peak": round(nb / us / 1e3 / HBM_PEAK_GBS, 4)}
+    return res
+
+
+def projection_component(torch, mk, dev):
+    from fp8_paged_insert_amd import synth
+
+    g = synth.gen(3, dev)
+    x = synth.bf16_normal((4096, 7168), g, dev)
+    w_nk = synth.bf16_normal((7168, L * W), g, dev, std=0.02).t().contiguous()
+    y = torch.empty(4096, L * W, dtype=torch.bfloat16, device=dev)
+    try:
+        us = time_kernel(torch, lambda: mk.mla_ctx_kv_proj(x, w_nk, y), reps=30)
+    except mk.MlaError as e:
+        return {"workload": "context_kv_proj 4096x7168 . 7168x2880", "status": str(e)}
+    flops = 2 * 4096 * 7168 * L * W
+    return {"workload": "context_kv_proj 4096x7168 . 7168x2880 (bf16 MFMA, fp32 acc)",
+            "us": round(us, 2), "TFLOPs": round(flops / us / 1e6, 1),
+            "frac_of_peak": round(flops / us / 1e6 / 2500.0, 4)}
+
+
+# ----------------------------------------------------------- CPU baseline --
+def cpu_baseline(torch):
+    """The oracle (plain serial C) on a bounded sample of one step's work:
+    the grouped fp8 insert of 5 layers x 4096 tokens, one gather of 8192
+    tokens and the fp8 pack of 1024 tokens x 64 heads (about 10 s serial)."""
+    import numpy as np
+
+    import oracle
+    from fp8_paged_insert_amd import synth
+
+    oracle.build(force=False)
+    g = synth.gen(5)
+    n, npk = 4096, 1024
+    kv = synth.bf16_normal((L, n, R), g).view(torch.int16).numpy().view(np.uint16)
+    pe = synth.bf16_normal((L, n, P), g).view(torch.int16).numpy().view(np.uint16)
+    caches = [np.zeros((128, 64, W), np.uint8) for _ in range(L)]
+    sm = np.stack([np.random.default_rng(l).permutation(128 * 64)[:n]
+                   for l in range(L)]).astype(np.int64)
+    scales = np.linspace(0.5, 2.0, L).astype(np.float32)
+    c = synth.context_cache(seed=55, num_blocks=256, num_ctx=8192)
+    cache_np, slots_np = c["cache"].numpy(), c["src_slots"].numpy()
+    kvb = synth.bf16_normal((npk, 64, 256), g).view(torch.int16).numpy().view(np.uint16)
+
+    t0 = time.perf_counter()
+    oracle.insert_grouped(kv, pe, sm, caches, scales)
+    t1 = time.perf_counter()
+    ws = oracle.gather(cache_np, slots_np, 0.5)
+    t2 = time.perf_counter()
+    oracle.pack(kvb[..., :128], ws[:npk, 512:], kvb[..., 128:], mode=oracle.PACK_KEY_V_FP8)
+    t3 = time.perf_counter()
+    nbytes = insert_bytes(L, n) + gather_bytes(8192) + pack_fp8_bytes(npk, 64)
+    secs = t3 - t0
+    return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"insert 5x{n} tokens ({t1 - t0:.2f}s) + gather 8192 tokens "
+                      f"({t2 - t1:.2f}s) + fp8 pack {npk} tokens x 64 heads ({t3 - t2:.2f}s); "
+                      f"{nbytes} algorithmic bytes in {secs:.2f}s, serial C",
+            "host_cpu": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip() + f" ({os.cpu_count()} logical CPUs visible)"
+    except OSError:
+        pass
+    return None
+
+
+# ------------------------------------------------------------------- main --
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-components", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device-to-device copy 3 times (reference "
+                         "kernel of known traffic for the HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this path has no "
+              "multi-GPU leg: each rank would run the same kernels on its own share.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import fp8_paged_insert_amd as mk
+
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": 1 << 30,
+                          "copy_calibration_bytes_written": 1 << 30, "launches": 3}))
+        return
+    mk.lib()
+    wl = LongContext(torch, mk, dev)
+    for _ in range(args.warmup):
+        wl.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        wl.step(time_pack=True)
+    torch.cuda.synchronize()
+    secs = time.perf_counter() - t0
+    ms_per_step = secs / args.steps * 1e3
+    nbytes = wl.bytes_per_step()
+    value = nbytes * args.steps / secs / 1e9
+
+    pack_us = statistics.mean(e0.elapsed_time(e1) * 1e3 for e0, e1 in wl.pack_events)
+    pack_b = pack_fp8_bytes(wl.chunk, wl.heads)
+    achieved = pack_b / pack_us / 1e3
+    roofline = {"bound": "hbm", "kernel": "pack_fp8_kernel", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None, "bytes_per_launch": pack_b,
+                "avg_launch_us": round(pack_us, 2), "launches": len(wl.pack_events)}
+
+    result = {
+        "metric": "grouped MLA KV insert/pack: effective HBM GB/s (% of peak); "
+                  "µs/launch small batch",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16->fp8_e4m3 (fp32 math)",
+        "data": "synthetic (seeded, generated on the device)",
+        "config": {"workload": "long-context stress: grouped fp8 insert 5 layers x 16384 tokens "
+                               "into [4096,64,576] caches + 16 chunks x 8192 tokens of fp8 gather "
+                               "and fp8 full-key/V pack (64 heads, [8192,64,256] kv_b_proj output)",
+                   "bytes_per_step": nbytes, "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
+        "roofline": roofline,
+    }
+    del wl
+    torch.cuda.empty_cache()
+    if not args.no_components:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        comps = {"small_batch_insert": small_batch(torch, mk, dev),
+                 "context_pack": context_pack_component(torch, mk, dev, flush),
+                 "context_epilogue": epilogue_component(torch, mk, dev, flush),
+                 "context_kv_proj": projection_component(torch, mk, dev)}
+        result["components"] = comps
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(torch)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

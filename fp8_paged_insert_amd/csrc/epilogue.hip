@@ -49,8 +49,12 @@ __global__ __launch_bounds__(256) void rope_table_kernel(float* out, int64_t max
 }
 
 // ---------------------------------------------------------------- epilogue --
-constexpr int kR = 512;  // kv_lora_rank handled by one wavefront (64 x 8)
-constexpr int kP = 64;   // rope dim handled by lanes 0-3 (4 x 2 x 8)
+constexpr int kR = 512;  // kv_lora_rank: lane i owns kv_c[8i, 8i + 8)
+constexpr int kP = 64;   // rope dim: lane i owns k_pe[i]; lanes i and i ^ 32 pair up
+#ifndef MLA_EPI_LAYERS
+#define MLA_EPI_LAYERS 5
+#endif
+constexpr int kMaxLayers = MLA_EPI_LAYERS;  // layers one wavefront keeps in flight
 constexpr int kWavesPerBlock = 4;
 
 struct EpiArgs {
@@ -67,8 +71,8 @@ struct EpiArgs {
   int64_t sls;
   int64_t block_size, block_stride, entry_stride;
   uint16_t* dbg;
-  FastDiv tokens, bsize;
-  uint32_t rows;  // L * T
+  FastDiv bsize;
+  uint32_t layers, tokens;
 };
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -77,104 +81,106 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+__device__ __forceinline__ int64_t entry_offset(int64_t s, const EpiArgs& a) {
+  if (s < 0x80000000LL) {
+    const uint32_t b32 = fdiv(static_cast<uint32_t>(s), a.bsize);
+    return int64_t(b32) * a.block_stride +
+           int64_t(static_cast<uint32_t>(s) - b32 * a.bsize.d) * a.entry_stride;
+  }
+  const int64_t blk = s / a.block_size;
+  return blk * a.block_stride + (s - blk * a.block_size) * a.entry_stride;
+}
+
+// One wavefront owns one token and walks its layers in groups of up to
+// kMaxLayers: every load of the group (the token's rows of all_kv are
+// adjacent in the [T, L, 576] projection output) is issued before the first
+// reduction.  RoPE pairs (i, i + 32) live in lanes i and i ^ 32, which swap
+// values with one cross-half shuffle; the token's cos/sin row is read once
+// (lane i holds cos_i for i < 32 and sin_{i-32} above) and shared by all
+// layers.
 template <bool kFp8>
 __global__ __launch_bounds__(256) void epilogue_kernel(const EpiArgs a) {
   const int lane = threadIdx.x & 63;
   const uint32_t wave = threadIdx.x >> 6;
-  const uint32_t stride = gridDim.x * kWavesPerBlock;
-  for (uint32_t row = blockIdx.x * kWavesPerBlock + wave; row < a.rows; row += stride) {
-    const uint32_t l = fdiv(row, a.tokens);
-    const uint32_t t = row - l * a.tokens.d;
-    const uint16_t* src = a.all_kv + int64_t(t) * a.kts + int64_t(l) * a.kls;
-
-    // ---- RMSNorm of kv_c: lane owns elements [8 lane, 8 lane + 8)
-    const uint4 xv = ld16(src + lane * 8);
-    const uint4 gv = ld16(a.gamma + int64_t(l) * kR + lane * 8);
-    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-    const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
-    float x[8], g[8];
+  const bool lo_half = lane < 32;
+  for (uint32_t t = blockIdx.x * kWavesPerBlock + wave; t < a.tokens;
+       t += gridDim.x * kWavesPerBlock) {
+    const uint16_t* tok = a.all_kv + int64_t(t) * a.kts;
+    // positions outside [0, max_pos) break the precondition; clamp so the
+    // table read stays inside the table.
+    const int64_t pos = min(max(a.positions[t], int64_t(0)), a.max_pos - 1);
+    const float mine = a.cos_sin[pos * kP + lane];
+    const float other = __shfl_xor(mine, 32, 64);
+    const float c = lo_half ? mine : other;          // cos(theta_{lane mod 32})
+    const float sn = lo_half ? -other : mine;        // -sin for the first half
+    for (uint32_t l0 = 0; l0 < a.layers; l0 += kMaxLayers) {
+      const int nl = min(kMaxLayers, int(a.layers - l0));
+      uint4 xv[kMaxLayers], gv[kMaxLayers];
+      uint32_t pe[kMaxLayers];
+      int64_t sl[kMaxLayers], cb[kMaxLayers];
+      float sc[kMaxLayers];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = bf16_lo(xw[i]);
-      x[2 * i + 1] = bf16_hi(xw[i]);
-      g[2 * i] = bf16_lo(gw[i]);
-      g[2 * i + 1] = bf16_hi(gw[i]);
-    }
-    float ss = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(x[i], x[i], ss);
-    ss = wave_sum(ss);
-    const float rinv = 1.0f / __builtin_sqrtf(ss * (1.0f / kR) + a.eps);
-    uint32_t yw[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      yw[i] = pack_bf16x2(x[2 * i] * rinv * g[2 * i], x[2 * i + 1] * rinv * g[2 * i + 1]);
-
-    // ---- RoPE of k_pe: lane < 4 owns pairs (8 lane + k, 8 lane + k + 32)
-    uint32_t pa[4] = {0, 0, 0, 0}, pb[4] = {0, 0, 0, 0};
-    if (lane < 4) {
-      const uint4 av = ld16(src + kR + lane * 8);
-      const uint4 bv = ld16(src + kR + kP / 2 + lane * 8);
-      // positions outside [0, max_pos) break the precondition; clamp so the
-      // table read stays inside the table.
-      const int64_t pos = min(max(a.positions[t], int64_t(0)), a.max_pos - 1);
-      const float* cs = a.cos_sin + pos * kP + lane * 8;
-      const float4 c0 = *reinterpret_cast<const float4*>(cs);
-      const float4 c1 = *reinterpret_cast<const float4*>(cs + 4);
-      const float4 s0 = *reinterpret_cast<const float4*>(cs + kP / 2);
-      const float4 s1 = *reinterpret_cast<const float4*>(cs + kP / 2 + 4);
-      const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-      const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-      const uint32_t aw[4] = {av.x, av.y, av.z, av.w};
-      const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x1a = bf16_lo(aw[i]), x1b = bf16_hi(aw[i]);
-        const float x2a = bf16_lo(bw[i]), x2b = bf16_hi(bw[i]);
-        const float ca = cv[2 * i], cb = cv[2 * i + 1], sa = sv[2 * i], sb = sv[2 * i + 1];
-        pa[i] = pack_bf16x2(x1a * ca - x2a * sa, x1b * cb - x2b * sb);
-        pb[i] = pack_bf16x2(x2a * ca + x1a * sa, x2b * cb + x1b * sb);
+      for (int k = 0; k < kMaxLayers; ++k) {
+        if (k >= nl) break;
+        const uint32_t l = l0 + k;
+        const uint16_t* row = tok + int64_t(l) * a.kls;
+        xv[k] = ld16(row + lane * 8);
+        gv[k] = ld16(a.gamma + int64_t(l) * kR + lane * 8);
+        pe[k] = row[kR + lane];
+        sl[k] = a.slots[int64_t(l) * a.sls + t];
+        cb[k] = a.cache_ptrs[l];
+        if constexpr (kFp8) sc[k] = a.scales[l];
       }
-    }
+#pragma unroll
+      for (int k = 0; k < kMaxLayers; ++k) {
+        if (k >= nl) break;
+        const uint32_t l = l0 + k;
+        // ---- RMSNorm: fp32 sum of squares over the wavefront
+        const uint32_t xw[4] = {xv[k].x, xv[k].y, xv[k].z, xv[k].w};
+        const uint32_t gw[4] = {gv[k].x, gv[k].y, gv[k].z, gv[k].w};
+        float x[8], g[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[2 * i] = bf16_lo(xw[i]);
+          x[2 * i + 1] = bf16_hi(xw[i]);
+          g[2 * i] = bf16_lo(gw[i]);
+          g[2 * i + 1] = bf16_hi(gw[i]);
+        }
+        float ss = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(x[i], x[i], ss);
+        ss = wave_sum(ss);
+        const float rinv = 1.0f / __builtin_sqrtf(ss * (1.0f / kR) + a.eps);
+        uint32_t yw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          yw[i] = cvt_bf16x2(x[2 * i] * rinv * g[2 * i], x[2 * i + 1] * rinv * g[2 * i + 1]);
 
-    if (a.dbg) {
-      uint16_t* d = a.dbg + int64_t(row) * (kR + kP);
-      st16(d + lane * 8, make_uint4(yw[0], yw[1], yw[2], yw[3]));
-      if (lane < 4) {
-        st16(d + kR + lane * 8, make_uint4(pa[0], pa[1], pa[2], pa[3]));
-        st16(d + kR + kP / 2 + lane * 8, make_uint4(pb[0], pb[1], pb[2], pb[3]));
-      }
-    }
+        // ---- RoPE: y_i = x_i cos - x_{i+32} sin, y_{i+32} = x_{i+32} cos + x_i sin
+        const float xp = bf16_lo(pe[k]);
+        const float xq = __shfl_xor(xp, 32, 64);
+        const uint32_t yp = cvt_bf16x2(xp * c + xq * sn, 0.0f) & 0xFFFFu;
 
-    // ---- insert ([P3] addressing: slot -> block, offset; negative = skip)
-    const int64_t s = a.slots[int64_t(l) * a.sls + t];
-    if (s < 0) continue;
-    int64_t blk, off;
-    if (s < 0x80000000LL) {
-      const uint32_t b32 = fdiv(static_cast<uint32_t>(s), a.bsize);
-      blk = b32;
-      off = static_cast<uint32_t>(s) - b32 * a.bsize.d;
-    } else {
-      blk = s / a.block_size;
-      off = s - blk * a.block_size;
-    }
-    const int64_t entry = blk * a.block_stride + off * a.entry_stride;
-    if constexpr (kFp8) {
-      const float sc = a.scales[l];
-      const float rc = 1.0f / sc;
-      uint8_t* dst = reinterpret_cast<uint8_t*>(a.cache_ptrs[l]) + entry;
-      st8(dst + lane * 8, quant8<true>(make_uint4(yw[0], yw[1], yw[2], yw[3]), sc, rc));
-      if (lane < 4) {
-        st8(dst + kR + lane * 8, quant8<true>(make_uint4(pa[0], pa[1], pa[2], pa[3]), sc, rc));
-        st8(dst + kR + kP / 2 + lane * 8,
-            quant8<true>(make_uint4(pb[0], pb[1], pb[2], pb[3]), sc, rc));
-      }
-    } else {
-      uint16_t* dst = reinterpret_cast<uint16_t*>(a.cache_ptrs[l]) + entry;
-      st16(dst + lane * 8, make_uint4(yw[0], yw[1], yw[2], yw[3]));
-      if (lane < 4) {
-        st16(dst + kR + lane * 8, make_uint4(pa[0], pa[1], pa[2], pa[3]));
-        st16(dst + kR + kP / 2 + lane * 8, make_uint4(pb[0], pb[1], pb[2], pb[3]));
+        if (a.dbg) {
+          uint16_t* d = a.dbg + (int64_t(l) * a.tokens + t) * (kR + kP);
+          st16(d + lane * 8, make_uint4(yw[0], yw[1], yw[2], yw[3]));
+          d[kR + lane] = static_cast<uint16_t>(yp);
+        }
+        // ---- insert (slot -> block, offset; a negative slot skips the row)
+        if (sl[k] < 0) continue;
+        const int64_t entry = entry_offset(sl[k], a);
+        if constexpr (kFp8) {
+          const float rc = 1.0f / sc[k];
+          const uint32_t flip = sign_flip_of(sc[k]);
+          uint8_t* dst = reinterpret_cast<uint8_t*>(cb[k]) + entry;
+          st8<kEpiStream>(dst + lane * 8,
+                          quant8<true>(make_uint4(yw[0], yw[1], yw[2], yw[3]), sc[k], rc, flip));
+          dst[kR + lane] = static_cast<uint8_t>(quant1(bf16_lo(yp), sc[k], rc, flip));
+        } else {
+          uint16_t* dst = reinterpret_cast<uint16_t*>(cb[k]) + entry;
+          st16<kEpiStream>(dst + lane * 8, make_uint4(yw[0], yw[1], yw[2], yw[3]));
+          dst[kR + lane] = static_cast<uint16_t>(yp);
+        }
       }
     }
   }
@@ -246,11 +252,11 @@ extern "C" int32_t mla_ctx_kv_epilogue(
   a.block_stride = block_stride;
   a.entry_stride = entry_stride;
   a.dbg = static_cast<uint16_t*>(dbg_rows);
-  a.tokens = make_fastdiv(static_cast<uint32_t>(num_tokens));
   a.bsize = make_fastdiv(static_cast<uint32_t>(block_size));
-  a.rows = static_cast<uint32_t>(rows);
+  a.layers = static_cast<uint32_t>(num_layers);
+  a.tokens = static_cast<uint32_t>(num_tokens);
   const int64_t blocks =
-      std::min<int64_t>(ceil_div(rows, kWavesPerBlock), default_grid_cap());
+      std::min<int64_t>(ceil_div(num_tokens, kWavesPerBlock), default_grid_cap());
   auto s = static_cast<hipStream_t>(stream);
   if (is_fp8(kv_cache_dtype))
     hipLaunchKernelGGL(epilogue_kernel<true>, dim3(blocks), dim3(256), 0, s, a);

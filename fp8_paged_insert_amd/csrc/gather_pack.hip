@@ -33,55 +33,90 @@ struct GatherArgs {
   uint32_t total;
 };
 
-template <bool kFp8>
+// Each thread takes U chunks per pass (item, item + stride, ...): the U slot
+// loads go out together, then the U cache-row loads, then the conversions,
+// so the slot -> row dependence is paid once per U chunks.
+template <bool kFp8, int U>
 __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
   constexpr int E = kFp8 ? 16 : 8;  // elements per chunk
   const uint32_t stride = gridDim.x * blockDim.x;
   float sc = 1.0f;
   if constexpr (kFp8) sc = a.scale[0];
-  for (uint32_t item = blockIdx.x * blockDim.x + threadIdx.x; item < a.total; item += stride) {
-    const uint32_t j = fdiv(item, a.per_row);
-    const uint32_t c = item - j * a.per_row.d;
-    const int64_t s = a.slots[j];
-    int64_t blk, off;
-    if (s < 0x80000000LL) {
-      const uint32_t b32 = fdiv(static_cast<uint32_t>(s), a.bsize);
-      blk = b32;
-      off = static_cast<uint32_t>(s) - b32 * a.bsize.d;
-    } else {
-      blk = s / a.block_size;
-      off = s - blk * a.block_size;
+  for (uint32_t base = blockIdx.x * blockDim.x + threadIdx.x; base < a.total;
+       base += U * stride) {
+    int64_t s[U];
+    uint32_t jj[U], cc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t item = base + u * stride;
+      jj[u] = fdiv(item < a.total ? item : 0, a.per_row);
+      cc[u] = item - jj[u] * a.per_row.d;
+      s[u] = item < a.total ? a.slots[jj[u]] : 0;
     }
-    const int64_t src_el = blk * a.block_stride + off * a.entry_stride + int64_t(c) * E;
-    uint16_t* dst = a.out + int64_t(j) * a.width + int64_t(c) * E;
-    if constexpr (kFp8) {
-      const uint4 q = ld16(a.cache + src_el);
-      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-      uint32_t o[8];
+    uint4 q[U];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float f[4];
-        dec4_e4m3(w[i], f);
-        uint32_t b[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          // The converter's NaN does not keep the code's sign: rebuild it.
-          const uint32_t code = (w[i] >> (8 * k)) & 0xFFu;
-          b[k] = (code & 0x7Fu) == 0x7Fu ? (0x7FC0u | ((code & 0x80u) << 8))
-                                         : f32_to_bf16_bits(f[k] * sc);
+    for (int u = 0; u < U; ++u) {
+      if (base + u * stride < a.total) {
+        int64_t blk, off;
+        if (s[u] < 0x80000000LL) {
+          const uint32_t b32 = fdiv(static_cast<uint32_t>(s[u]), a.bsize);
+          blk = b32;
+          off = static_cast<uint32_t>(s[u]) - b32 * a.bsize.d;
+        } else {
+          blk = s[u] / a.block_size;
+          off = s[u] - blk * a.block_size;
         }
-        o[2 * i] = b[0] | (b[1] << 16);
-        o[2 * i + 1] = b[2] | (b[3] << 16);
+        const int64_t src_el = blk * a.block_stride + off * a.entry_stride + int64_t(cc[u]) * E;
+        q[u] = kFp8 ? ld16(a.cache + src_el)
+                    : ld16(reinterpret_cast<const uint16_t*>(a.cache) + src_el);
       }
-      st16(dst, make_uint4(o[0], o[1], o[2], o[3]));
-      st16(dst + 8, make_uint4(o[4], o[5], o[6], o[7]));
-    } else {
-      st16(dst, ld16(reinterpret_cast<const uint16_t*>(a.cache) + src_el));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (base + u * stride >= a.total) continue;
+      uint16_t* dst = a.out + int64_t(jj[u]) * a.width + int64_t(cc[u]) * E;
+      if constexpr (kFp8) {
+        const uint32_t w[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+        uint32_t o[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float f[4];
+          dec4_e4m3(w[i], f);
+          // fl32(value * scale) rounded to bf16; the converter's NaN does not
+          // keep the code's sign, so NaN codes are rebuilt (a rare branch).
+          uint32_t lo = cvt_bf16x2(f[0] * sc, f[1] * sc);
+          uint32_t hi = cvt_bf16x2(f[2] * sc, f[3] * sc);
+          const bool nan4 = (((w[i] & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u) != 0;
+          if (__builtin_expect(__builtin_amdgcn_ballot_w64(nan4) != 0, 0)) {
+            uint32_t b[4] = {lo & 0xFFFFu, lo >> 16, hi & 0xFFFFu, hi >> 16};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const uint32_t code = (w[i] >> (8 * k)) & 0xFFu;
+              if ((code & 0x7Fu) == 0x7Fu) b[k] = 0x7FC0u | ((code & 0x80u) << 8);
+            }
+            lo = b[0] | (b[1] << 16);
+            hi = b[2] | (b[3] << 16);
+          }
+          o[2 * i] = lo;
+          o[2 * i + 1] = hi;
+        }
+        st16<kGatherStream>(dst, make_uint4(o[0], o[1], o[2], o[3]));
+        st16<kGatherStream>(dst + 8, make_uint4(o[4], o[5], o[6], o[7]));
+      } else {
+        st16<kGatherStream>(dst, q[u]);
+      }
     }
   }
 }
 
 // ------------------------------------------------------------------- pack --
+// One workgroup converts one token at a time (grid-stride over tokens).  The
+// token's outputs are contiguous: H key rows [nope + rope] then, in fp8 mode,
+// H V rows [vdim]; they are cut into 16-byte output chunks and thread i takes
+// chunks i, i + 256, ..., issuing every load of its chunks before converting
+// any of them, so each thread keeps up to kU x 32 bytes of reads in flight.
+// The token's 512-byte head rows [k_nope | v] are read by one workgroup
+// within a short window, which keeps the HBM pages they sit in open.
 struct PackArgs {
   const uint16_t* k_nope;
   int64_t kn_ts, kn_hs;
@@ -93,72 +128,102 @@ struct PackArgs {
   const float* v_scale;
   void* key_out;
   uint8_t* v_out;
-  FastDiv key_per_row;  // output chunks per (t, h) key row
-  FastDiv v_per_row;    // output chunks per (t, h) V row
-  FastDiv heads;
+  FastDiv key_per_row;   // output chunks per key row
+  FastDiv v_per_row;     // output chunks per V row (fp8 mode)
   uint32_t nope_chunks;  // key chunks taken from k_nope
-  uint32_t key_total;    // T * H * key_per_row
-  uint32_t total;        // key_total (+ T * H * v_per_row in fp8 mode)
+  uint32_t key_chunks;   // key chunks of one token: H * key_per_row
+  uint32_t chunks;       // all chunks of one token
+  int64_t key_row_elems; // H * (nope + rope)
+  int64_t v_row_elems;   // H * vdim
+  uint32_t tokens;
 };
 
-__global__ __launch_bounds__(256) void pack_bf16_kernel(const PackArgs a) {
+constexpr int kPackThreads = 256;
+
+template <int U>
+__global__ __launch_bounds__(kPackThreads) void pack_bf16_kernel(const PackArgs a) {
   constexpr int E = 8;
-  const uint32_t stride = gridDim.x * blockDim.x;
-  uint16_t* key = static_cast<uint16_t*>(a.key_out);
-  for (uint32_t item = blockIdx.x * blockDim.x + threadIdx.x; item < a.total; item += stride) {
-    const uint32_t row = fdiv(item, a.key_per_row);
-    const uint32_t c = item - row * a.key_per_row.d;
-    const uint32_t t = fdiv(row, a.heads);
-    const uint32_t h = row - t * a.heads.d;
-    const uint16_t* src = c < a.nope_chunks
-                              ? a.k_nope + int64_t(t) * a.kn_ts + int64_t(h) * a.kn_hs + c * E
-                              : a.k_pe + int64_t(t) * a.pe_ts + (c - a.nope_chunks) * E;
-    st16(key + int64_t(item) * E, ld16(src));
+  for (uint32_t t = blockIdx.x; t < a.tokens; t += gridDim.x) {
+    const uint16_t* kn = a.k_nope + int64_t(t) * a.kn_ts;
+    const uint16_t* pe = a.k_pe + int64_t(t) * a.pe_ts;
+    uint16_t* key = static_cast<uint16_t*>(a.key_out) + int64_t(t) * a.key_row_elems;
+    for (uint32_t c0 = threadIdx.x; c0 < a.chunks; c0 += kPackThreads * U) {
+      uint4 x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t c = c0 + u * kPackThreads;
+        if (c < a.chunks) {
+          const uint32_t h = fdiv(c, a.key_per_row);
+          const uint32_t j = c - h * a.key_per_row.d;
+          x[u] = j < a.nope_chunks ? ld16(kn + int64_t(h) * a.kn_hs + j * E)
+                                   : ld16(pe + (j - a.nope_chunks) * E);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t c = c0 + u * kPackThreads;
+        if (c < a.chunks) st16<kPackStream>(key + int64_t(c) * E, x[u]);
+      }
+    }
   }
 }
 
-template <bool kScaled>
-__global__ __launch_bounds__(256) void pack_fp8_kernel(const PackArgs a) {
+template <bool kScaled, int U>
+__global__ __launch_bounds__(kPackThreads) void pack_fp8_kernel(const PackArgs a) {
   constexpr int E = 16;
-  const uint32_t stride = gridDim.x * blockDim.x;
   float ks = 1.0f, vs = 1.0f;
   if constexpr (kScaled) {
     if (a.k_scale) ks = a.k_scale[0];
     if (a.v_scale) vs = a.v_scale[0];
   }
   const float kr = 1.0f / ks, vr = 1.0f / vs;
-  uint8_t* key = static_cast<uint8_t*>(a.key_out);
-  for (uint32_t item = blockIdx.x * blockDim.x + threadIdx.x; item < a.total; item += stride) {
-    const uint16_t* src;
-    uint8_t* dst;
-    float s, r;
-    if (item < a.key_total) {
-      const uint32_t row = fdiv(item, a.key_per_row);
-      const uint32_t c = item - row * a.key_per_row.d;
-      const uint32_t t = fdiv(row, a.heads);
-      const uint32_t h = row - t * a.heads.d;
-      src = c < a.nope_chunks
-                ? a.k_nope + int64_t(t) * a.kn_ts + int64_t(h) * a.kn_hs + c * E
-                : a.k_pe + int64_t(t) * a.pe_ts + (c - a.nope_chunks) * E;
-      dst = key + int64_t(item) * E;
-      s = ks;
-      r = kr;
-    } else {
-      const uint32_t vi = item - a.key_total;
-      const uint32_t row = fdiv(vi, a.v_per_row);
-      const uint32_t c = vi - row * a.v_per_row.d;
-      const uint32_t t = fdiv(row, a.heads);
-      const uint32_t h = row - t * a.heads.d;
-      src = a.v + int64_t(t) * a.v_ts + int64_t(h) * a.v_hs + c * E;
-      dst = a.v_out + int64_t(vi) * E;
-      s = vs;
-      r = vr;
+  const uint32_t kf = sign_flip_of(ks), vf = sign_flip_of(vs);
+  for (uint32_t t = blockIdx.x; t < a.tokens; t += gridDim.x) {
+    const uint16_t* kn = a.k_nope + int64_t(t) * a.kn_ts;
+    const uint16_t* pe = a.k_pe + int64_t(t) * a.pe_ts;
+    const uint16_t* vv = a.v + int64_t(t) * a.v_ts;
+    uint8_t* key = static_cast<uint8_t*>(a.key_out) + int64_t(t) * a.key_row_elems;
+    uint8_t* vo = a.v_out + int64_t(t) * a.v_row_elems;
+    for (uint32_t c0 = threadIdx.x; c0 < a.chunks; c0 += kPackThreads * U) {
+      uint4 x0[U], x1[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t c = c0 + u * kPackThreads;
+        if (c < a.chunks) {
+          const uint16_t* src;
+          if (c < a.key_chunks) {
+            const uint32_t h = fdiv(c, a.key_per_row);
+            const uint32_t j = c - h * a.key_per_row.d;
+            src = j < a.nope_chunks ? kn + int64_t(h) * a.kn_hs + j * E
+                                    : pe + (j - a.nope_chunks) * E;
+          } else {
+            const uint32_t cv = c - a.key_chunks;
+            const uint32_t h = fdiv(cv, a.v_per_row);
+            const uint32_t j = cv - h * a.v_per_row.d;
+            src = vv + int64_t(h) * a.v_hs + j * E;
+          }
+          x0[u] = ld16(src);
+          x1[u] = ld16(src + 8);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t c = c0 + u * kPackThreads;
+        if (c < a.chunks) {
+          const bool is_key = c < a.key_chunks;
+          uint8_t* dst = is_key ? key + int64_t(c) * E : vo + int64_t(c - a.key_chunks) * E;
+          st16<kPackStream>(dst, quant16<kScaled>(x0[u], x1[u], is_key ? ks : vs,
+                                                  is_key ? kr : vr, is_key ? kf : vf));
+        }
+      }
     }
-    const uint4 x0 = ld16(src);
-    const uint4 x1 = ld16(src + 8);
-    st16(dst, quant16<kScaled>(x0, x1, s, r));
   }
 }
+
+#ifndef MLA_GATHER_UNROLL
+#define MLA_GATHER_UNROLL 1
+#endif
+constexpr int kGatherUnroll = MLA_GATHER_UNROLL;
 
 int64_t grid_for(int64_t total, int64_t max_blocks) {
   const int64_t cap = max_blocks > 0 ? max_blocks : default_grid_cap();
@@ -229,11 +294,11 @@ extern "C" int32_t mla_ctx_latent_gather(const void* cache, int32_t cache_dtype,
   a.bsize = make_fastdiv(static_cast<uint32_t>(block_size));
   a.total = static_cast<uint32_t>(total);
   auto s = static_cast<hipStream_t>(stream);
-  const int64_t blocks = grid_for(total, max_blocks);
+  const int64_t blocks = grid_for(ceil_div(total, kGatherUnroll), max_blocks);
   if (fp8)
-    hipLaunchKernelGGL(gather_kernel<true>, dim3(blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gather_kernel<true, kGatherUnroll>), dim3(blocks), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(gather_kernel<false>, dim3(blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gather_kernel<false, kGatherUnroll>), dim3(blocks), dim3(256), 0, s, a);
   return launch_status(fn);
 }
 
@@ -270,11 +335,9 @@ extern "C" int32_t mla_ctx_kv_pack(const void* k_nope, int64_t kn_tok_stride,
   const int64_t E = fp8 ? 16 : 8;
   const int64_t key_per_row = (nope + rope) / E;
   const int64_t v_per_row = fp8 ? vdim / E : 0;
-  const int64_t rows = num_tokens * num_heads;
-  const int64_t key_total = rows * key_per_row;
-  const int64_t total = key_total + rows * v_per_row;
-  if (total >= (int64_t(1) << 31) || num_heads > 0x7FFFFFFF)
-    return fail(MLA_ERR_UNSUPPORTED, "%s: too many rows for one launch; split the chunk", fn);
+  const int64_t chunks = num_heads * (key_per_row + v_per_row);
+  if (chunks >= (int64_t(1) << 31) || num_tokens >= (int64_t(1) << 31))
+    return fail(MLA_ERR_UNSUPPORTED, "%s: too many heads or tokens for one launch", fn);
   PackArgs a;
   a.k_nope = static_cast<const uint16_t*>(k_nope);
   a.kn_ts = kn_tok_stride;
@@ -290,17 +353,20 @@ extern "C" int32_t mla_ctx_kv_pack(const void* k_nope, int64_t kn_tok_stride,
   a.v_out = static_cast<uint8_t*>(v_out);
   a.key_per_row = make_fastdiv(static_cast<uint32_t>(key_per_row));
   a.v_per_row = make_fastdiv(static_cast<uint32_t>(v_per_row > 0 ? v_per_row : 1));
-  a.heads = make_fastdiv(static_cast<uint32_t>(num_heads));
   a.nope_chunks = static_cast<uint32_t>(nope / E);
-  a.key_total = static_cast<uint32_t>(key_total);
-  a.total = static_cast<uint32_t>(total);
+  a.key_chunks = static_cast<uint32_t>(num_heads * key_per_row);
+  a.chunks = static_cast<uint32_t>(chunks);
+  a.key_row_elems = num_heads * (nope + rope);
+  a.v_row_elems = num_heads * vdim;
+  a.tokens = static_cast<uint32_t>(num_tokens);
   auto s = static_cast<hipStream_t>(stream);
-  const int64_t blocks = grid_for(total, max_blocks);
+  const int64_t cap = max_blocks > 0 ? max_blocks : default_grid_cap();
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(num_tokens, cap));
   if (!fp8)
-    hipLaunchKernelGGL(pack_bf16_kernel, dim3(blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(pack_bf16_kernel<6>, dim3(blocks), dim3(kPackThreads), 0, s, a);
   else if (k_scale || v_scale)
-    hipLaunchKernelGGL(pack_fp8_kernel<true>, dim3(blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((pack_fp8_kernel<true, 5>), dim3(blocks), dim3(kPackThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(pack_fp8_kernel<false>, dim3(blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((pack_fp8_kernel<false, 5>), dim3(blocks), dim3(kPackThreads), 0, s, a);
   return launch_status(fn);
 }

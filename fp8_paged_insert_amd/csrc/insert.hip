@@ -38,47 +38,61 @@ struct InsertArgs {
 };
 
 // kFp8: 16 bf16 in -> 16 e4m3fn codes out per chunk; else 8 bf16 copied.
-template <bool kFp8>
+// Each thread takes U chunks per pass (item, item + stride, ...): the slot,
+// cache-base and scale loads and the source loads of all U chunks are issued
+// before the first store, so the slot -> store dependence overlaps U times.
+template <bool kFp8, int U>
 __global__ __launch_bounds__(256) void grouped_insert_kernel(const InsertArgs a) {
   constexpr int E = kFp8 ? 16 : 8;
   const uint32_t stride = gridDim.x * blockDim.x;
-  for (uint32_t item = blockIdx.x * blockDim.x + threadIdx.x; item < a.total; item += stride) {
-    const uint32_t row = fdiv(item, a.per_row);
-    const uint32_t j = item - row * a.per_row.d;
-    const uint32_t l = fdiv(row, a.tokens);
-    const uint32_t t = row - l * a.tokens.d;
-    const int64_t s = a.slots[int64_t(l) * a.sls + t];
-    if (s < 0) continue;  // padding token: nothing is written for this layer
-    int64_t blk, off;
-    if (s < 0x80000000LL) {
-      const uint32_t b32 = fdiv(static_cast<uint32_t>(s), a.bsize);
-      blk = b32;
-      off = static_cast<uint32_t>(s) - b32 * a.bsize.d;
-    } else {
-      blk = s / a.block_size;
-      off = s - blk * a.block_size;
+  for (uint32_t base = blockIdx.x * blockDim.x + threadIdx.x; base < a.total;
+       base += U * stride) {
+    int64_t s[U], col[U], cbase[U];
+    float sc[U];
+    uint4 v0[U], v1[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t item = base + u * stride;
+      if (item >= a.total) continue;
+      const uint32_t row = fdiv(item, a.per_row);
+      const uint32_t j = item - row * a.per_row.d;
+      const uint32_t l = fdiv(row, a.tokens);
+      const uint32_t t = row - l * a.tokens.d;
+      s[u] = a.slots[int64_t(l) * a.sls + t];
+      cbase[u] = a.cache_ptrs[l];
+      if constexpr (kFp8) sc[u] = a.scales[l];
+      const uint16_t* src;
+      if (j < a.chunks_r) {
+        col[u] = int64_t(j) * E;
+        src = a.kv_c + int64_t(l) * a.kv_ls + int64_t(t) * a.kv_ts + col[u];
+      } else {
+        const int64_t jj = int64_t(j - a.chunks_r) * E;
+        src = a.k_pe + int64_t(l) * a.pe_ls + int64_t(t) * a.pe_ts + jj;
+        col[u] = a.R + jj;
+      }
+      v0[u] = ld16(src);
+      if constexpr (kFp8) v1[u] = ld16(src + 8);
     }
-    const uint16_t* src;
-    int64_t col;
-    if (j < a.chunks_r) {
-      col = int64_t(j) * E;
-      src = a.kv_c + int64_t(l) * a.kv_ls + int64_t(t) * a.kv_ts + col;
-    } else {
-      const int64_t jj = int64_t(j - a.chunks_r) * E;
-      src = a.k_pe + int64_t(l) * a.pe_ls + int64_t(t) * a.pe_ts + jj;
-      col = a.R + jj;
-    }
-    const int64_t dst_off = blk * a.block_stride + off * a.entry_stride + col;
-    if constexpr (kFp8) {
-      const float sc = a.scales[l];
-      const float rc = 1.0f / sc;  // IEEE division: RN(1 / scale)
-      const uint4 v0 = ld16(src);
-      const uint4 v1 = ld16(src + 8);
-      uint8_t* cache = reinterpret_cast<uint8_t*>(a.cache_ptrs[l]);
-      st16(cache + dst_off, quant16<true>(v0, v1, sc, rc));
-    } else {
-      uint16_t* cache = reinterpret_cast<uint16_t*>(a.cache_ptrs[l]);
-      st16(cache + dst_off, ld16(src));
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (base + u * stride >= a.total || s[u] < 0) continue;  // negative slot: skip
+      int64_t blk, off;
+      if (s[u] < 0x80000000LL) {
+        const uint32_t b32 = fdiv(static_cast<uint32_t>(s[u]), a.bsize);
+        blk = b32;
+        off = static_cast<uint32_t>(s[u]) - b32 * a.bsize.d;
+      } else {
+        blk = s[u] / a.block_size;
+        off = s[u] - blk * a.block_size;
+      }
+      const int64_t dst_off = blk * a.block_stride + off * a.entry_stride + col[u];
+      if constexpr (kFp8) {
+        const float rc = 1.0f / sc[u];  // IEEE division: RN(1 / scale)
+        st16<kInsertStream>(reinterpret_cast<uint8_t*>(cbase[u]) + dst_off,
+                            quant16<true>(v0[u], v1[u], sc[u], rc, sign_flip_of(sc[u])));
+      } else {
+        st16<kInsertStream>(reinterpret_cast<uint16_t*>(cbase[u]) + dst_off, v0[u]);
+      }
     }
   }
 }
@@ -174,11 +188,15 @@ extern "C" int32_t mla_kv_insert_grouped(
   a.chunks_r = static_cast<uint32_t>(kv_lora_rank / E);
   a.total = static_cast<uint32_t>(total);
 
-  const int64_t blocks = std::min<int64_t>(ceil_div(total, 256), default_grid_cap());
+#ifndef MLA_INSERT_UNROLL
+#define MLA_INSERT_UNROLL 1
+#endif
+  constexpr int U = MLA_INSERT_UNROLL;
+  const int64_t blocks = std::min<int64_t>(ceil_div(total, 256 * U), default_grid_cap());
   auto s = static_cast<hipStream_t>(stream);
   if (fp8)
-    hipLaunchKernelGGL(grouped_insert_kernel<true>, dim3(blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((grouped_insert_kernel<true, U>), dim3(blocks), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(grouped_insert_kernel<false>, dim3(blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((grouped_insert_kernel<false, U>), dim3(blocks), dim3(256), 0, s, a);
   return launch_status(fn);
 }

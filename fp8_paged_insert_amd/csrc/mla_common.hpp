@@ -60,74 +60,112 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
-// Correctly rounded fp32 quotient x / s from r = RN(1/s): q0 = RN(x*r) is
-// within one ulp, the remainder x - q0*s is exact under FMA, and one
-// correction step rounds correctly (Markstein).  Checked exhaustively on the
-// CPU for every bf16 significand against every fp32 significand of s.  For
-// zeros, infinities, NaN and fp32 subnormals q0 is kept: those quotients all
-// encode to a signed zero, a saturated +-448 or NaN in e4m3fn, and q0 carries
-// the right sign (the correction would turn -0 into +0 and Inf into NaN).
+// fp32 -> bf16 with the gfx950 converter (round to nearest even), two at a
+// time.  Used where a NaN's payload and sign are not part of the contract.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// ---------------------------------------------------------------------------
+// bf16 -> e4m3fn with a per-tensor dequantisation scale s:
+//   code = e4m3fn_RNE(fl32(x) / s), saturating at +-448, NaN -> 0x7F | sign.
+// Exactness argument, step by step:
+//  * quotient: r = RN(1/s) once; q0 = RN(x*r) is within one ulp of x/s, the
+//    remainder x - q0*s is exact under FMA, and q = RN(q0 + rem*r) is the
+//    correctly rounded x/s (Markstein; checked exhaustively on the CPU for
+//    every bf16 significand against every fp32 significand of s).  Where
+//    the step degenerates -- x = +-0 (the sum of signed zeros gives +0),
+//    x = +-Inf or an overflowing quotient (Inf - Inf gives NaN) -- only the
+//    sign of the final code can be wrong, and it is rewritten below.
+//  * saturation: v_med3 clamps to [-448, 448]; it also maps NaN onto a
+//    bound, which is what turns the degenerate Inf cases into +-448.
+//  * the packed converter rounds to nearest even in OCP e4m3fn.
+//  * sign: every code's sign bit is set to sign(x) xor sign(s) (v_perm
+//    gathers the bf16 high bytes, v_bfi merges them) -- exact for all
+//    non-NaN inputs, including zeros, subnormal quotients and saturation.
+//  * NaN inputs (rare; a branch no lane takes otherwise) get 0x7F | sign(x).
+// ---------------------------------------------------------------------------
 __device__ __forceinline__ float div_by_scale(float x, float s, float r) {
   const float q0 = x * r;
   const float e = __builtin_fmaf(-q0, s, x);
-  const float q1 = __builtin_fmaf(e, r, q0);
-  // v_cmp_class mask: snan|qnan|-inf|-denorm|-zero|+zero|+denorm|+inf
-  return __builtin_amdgcn_classf(q0, 0x2F7) ? q0 : q1;
+  return __builtin_fmaf(e, r, q0);
 }
 
-// Saturate finite values (and +-Inf) to the e4m3fn range; NaN passes through.
 __device__ __forceinline__ float sat448(float q) {
-  const float c = __builtin_amdgcn_fmed3f(q, -448.0f, 448.0f);
-  return (q != q) ? q : c;
+  return __builtin_amdgcn_fmed3f(q, -448.0f, 448.0f);
 }
 
-// Byte k of w := the e4m3fn NaN code carrying the sign of x.
+// Codes of 4 clamped values (byte k = value k).
+__device__ __forceinline__ uint32_t cvt4_raw(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return static_cast<uint32_t>(w);
+}
+
+// Byte k of w := NaN code with the sign of x.
 __device__ __forceinline__ uint32_t put_nan(uint32_t w, float x, int k) {
   const uint32_t code = 0x7Fu | ((__float_as_uint(x) >> 24) & 0x80u);
   return (w & ~(0xFFu << (8 * k))) | (code << (8 * k));
 }
 
-// Four fp32 values -> four e4m3fn codes (byte k = value k), RNE, saturating
-// at +-448.  On gfx950 the packed converter produces the OCP e4m3fn
-// encoding; its NaN output does not keep the input's sign, so NaN bytes are
-// rewritten (a branch that no lane takes unless an input is NaN).
-__device__ __forceinline__ uint32_t cvt4_e4m3(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), w, true);
-  uint32_t r = static_cast<uint32_t>(w);
-  if (__builtin_expect((a != a) | (b != b) | (c != c) | (d != d), 0)) {
-    if (a != a) r = put_nan(r, a, 0);
-    if (b != b) r = put_nan(r, b, 1);
-    if (c != c) r = put_nan(r, c, 2);
-    if (d != d) r = put_nan(r, d, 3);
-  }
-  return r;
-}
-
-// 8 bf16 (one uint4) -> 8 e4m3fn codes (uint2), dividing by s (r = RN(1/s)).
+// 8 bf16 (one uint4: element 2i in the low half of word i) -> 8 codes.
+// sign_flip is 0x80808080 when s < 0, else 0.
 template <bool kScaled>
-__device__ __forceinline__ uint2 quant8(uint4 v, float s, float r) {
-  float f[8];
+__device__ __forceinline__ uint2 quant8(uint4 v, float s, float r, uint32_t sign_flip) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float f[8], q[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     f[2 * i] = bf16_lo(w[i]);
     f[2 * i + 1] = bf16_hi(w[i]);
   }
-  if constexpr (kScaled) {
+  bool nan = false;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] = div_by_scale(f[i], s, r);
+  for (int i = 0; i < 8; ++i) {
+    nan |= f[i] != f[i];
+    q[i] = sat448(kScaled ? div_by_scale(f[i], s, r) : f[i]);
   }
-  return make_uint2(cvt4_e4m3(f[0], f[1], f[2], f[3]), cvt4_e4m3(f[4], f[5], f[6], f[7]));
+  uint32_t c0 = cvt4_raw(q[0], q[1], q[2], q[3]);
+  uint32_t c1 = cvt4_raw(q[4], q[5], q[6], q[7]);
+  // bf16 high bytes (bit 7 = sign) of elements 0-3 and 4-7
+  const uint32_t s0 = __builtin_amdgcn_perm(w[1], w[0], 0x07050301u) ^ sign_flip;
+  const uint32_t s1 = __builtin_amdgcn_perm(w[3], w[2], 0x07050301u) ^ sign_flip;
+  c0 = (c0 & 0x7F7F7F7Fu) | (s0 & 0x80808080u);
+  c1 = (c1 & 0x7F7F7F7Fu) | (s1 & 0x80808080u);
+  // A wave-uniform branch (the NaN flag voted across the wavefront) keeps
+  // the patch out of the straight-line path.
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(nan) != 0, 0)) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (f[k] != f[k]) c0 = put_nan(c0, f[k], k);
+      if (f[k + 4] != f[k + 4]) c1 = put_nan(c1, f[k + 4], k);
+    }
+  }
+  return make_uint2(c0, c1);
 }
 
-// 16 bf16 (two uint4) -> 16 e4m3fn codes (uint4).
+// 16 bf16 (two uint4) -> 16 codes (uint4).
 template <bool kScaled>
-__device__ __forceinline__ uint4 quant16(uint4 a, uint4 b, float s, float r) {
-  const uint2 lo = quant8<kScaled>(a, s, r);
-  const uint2 hi = quant8<kScaled>(b, s, r);
+__device__ __forceinline__ uint4 quant16(uint4 a, uint4 b, float s, float r, uint32_t flip) {
+  const uint2 lo = quant8<kScaled>(a, s, r, flip);
+  const uint2 hi = quant8<kScaled>(b, s, r, flip);
   return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
+
+// One bf16 value (as fp32) -> its code in the low byte.
+__device__ __forceinline__ uint32_t quant1(float x, float s, float r, uint32_t sign_flip) {
+  const float q = sat448(div_by_scale(x, s, r));
+  uint32_t c = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(q, q, 0, false)) & 0x7Fu;
+  c |= ((__float_as_uint(x) >> 24) ^ sign_flip) & 0x80u;
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(x != x) != 0, 0))
+    c = x != x ? 0x7Fu | ((__float_as_uint(x) >> 24) & 0x80u) : c;
+  return c;
+}
+
+__device__ __forceinline__ uint32_t sign_flip_of(float s) { return s < 0.0f ? 0x80808080u : 0u; }
 
 // Four e4m3fn codes (one word) -> four fp32 values (exact).
 __device__ __forceinline__ void dec4_e4m3(uint32_t w, float* out) {
@@ -155,9 +193,51 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
   return (__umulhi(n, f.m) + n) >> f.l;
 }
 
-// Vector loads / stores of 16 bytes.
+// Vector loads / stores.  kStream selects non-temporal (streaming) stores for
+// outputs that no later step of the same kernel reads.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
-__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
-__device__ __forceinline__ void st8(void* p, uint2 v) { *reinterpret_cast<uint2*>(p) = v; }
+
+template <bool kStream = false>
+__device__ __forceinline__ void st16(void* p, uint4 v) {
+  if constexpr (kStream) {
+    u32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+  } else {
+    *reinterpret_cast<uint4*>(p) = v;
+  }
+}
+template <bool kStream = false>
+__device__ __forceinline__ void st8(void* p, uint2 v) {
+  if constexpr (kStream) {
+    u32x2 w = {v.x, v.y};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(p));
+  } else {
+    *reinterpret_cast<uint2*>(p) = v;
+  }
+}
+
+// Store policy per kernel (measured on MI355X): the pack and gather write
+// large contiguous outputs that the next kernel of a chunk loop does not
+// re-read from cache, so they stream; the insert and epilogue scatter
+// 576-byte rows, where ordinary stores let the last-level cache merge lines.
+#ifndef MLA_PACK_STREAM
+#define MLA_PACK_STREAM 1
+#endif
+#ifndef MLA_GATHER_STREAM
+#define MLA_GATHER_STREAM 1
+#endif
+#ifndef MLA_INSERT_STREAM
+#define MLA_INSERT_STREAM 0
+#endif
+#ifndef MLA_EPI_STREAM
+#define MLA_EPI_STREAM 0
+#endif
+constexpr bool kPackStream = MLA_PACK_STREAM != 0;
+constexpr bool kGatherStream = MLA_GATHER_STREAM != 0;
+constexpr bool kInsertStream = MLA_INSERT_STREAM != 0;
+constexpr bool kEpiStream = MLA_EPI_STREAM != 0;
 
 }  // namespace mla

@@ -121,7 +121,7 @@ def test_exhaustive_bf16_patterns_through_fp8_converter(mk):
     """All 65536 bf16 bit patterns (NaN, Inf, subnormals, +-0 included),
     quantised with several per-layer scales, equal the oracle bit for bit."""
     announce("exhaustive_converter")
-    scales = torch.tensor([1.0, 0.5, 0.05, 0.25, 0.7312, 1.9999, 1.3, 0.1], dtype=torch.float32)
+    scales = torch.tensor([1.0, 0.5, 0.05, 0.25, 0.7312, 1.9999, 1.3, -0.7312], dtype=torch.float32)
     L = scales.numel()
     rows = 65536 // 512 + 1
     bits = np.arange(rows * 576, dtype=np.int64) % 65536
