@@ -99,6 +99,9 @@ class LongContext:
                 + n * pack_fp8_bytes(self.chunk, self.heads))
 
     def step(self, time_pack=False):
+        """One pass over the workload, in order on the current stream.  (Issuing
+        chunk c + 1's gather on a side stream during chunk c's pack measured
+        slower on MI355X: the cross-stream waits cost more than they hide.)"""
         mk, torch = self.mk, self.torch
         mk.mla_kv_insert_grouped(self.kv_c, self.k_pe, self.ptrs, self.slots, 64, 64 * W, W,
                                  self.scales, "fp8")

@@ -110,13 +110,13 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
 }
 
 // ------------------------------------------------------------------- pack --
-// One workgroup converts one token at a time (grid-stride over tokens).  The
-// token's outputs are contiguous: H key rows [nope + rope] then, in fp8 mode,
-// H V rows [vdim]; they are cut into 16-byte output chunks and thread i takes
-// chunks i, i + 256, ..., issuing every load of its chunks before converting
-// any of them, so each thread keeps up to kU x 32 bytes of reads in flight.
-// The token's 512-byte head rows [k_nope | v] are read by one workgroup
-// within a short window, which keeps the HBM pages they sit in open.
+// The outputs are cut into 16-byte chunks, numbered key chunks of every
+// token first (row (t, h), chunk j), then V chunks; chunk i is written at
+// byte 16 i of its output, so consecutive lanes write consecutive addresses.
+// The default grid has one thread per chunk (no loop): the workgroups in
+// flight then sweep the strided kv_b_proj output and the contiguous outputs
+// as one advancing window, which measured faster on MI355X than a capped
+// grid; a caller-given max_blocks turns the grid-stride loop on.
 struct PackArgs {
   const uint16_t* k_nope;
   int64_t kn_ts, kn_hs;
@@ -128,48 +128,35 @@ struct PackArgs {
   const float* v_scale;
   void* key_out;
   uint8_t* v_out;
-  FastDiv key_per_row;   // output chunks per key row
-  FastDiv v_per_row;     // output chunks per V row (fp8 mode)
+  FastDiv key_per_row;  // output chunks per key row
+  FastDiv v_per_row;    // output chunks per V row (fp8 mode)
+  FastDiv heads;
   uint32_t nope_chunks;  // key chunks taken from k_nope
-  uint32_t key_chunks;   // key chunks of one token: H * key_per_row
-  uint32_t chunks;       // all chunks of one token
-  int64_t key_row_elems; // H * (nope + rope)
-  int64_t v_row_elems;   // H * vdim
-  uint32_t tokens;
+  uint32_t key_total;    // T * H * key_per_row
+  uint32_t total;        // key_total + T * H * v_per_row
 };
 
-constexpr int kPackThreads = 256;
-
-template <int U>
-__global__ __launch_bounds__(kPackThreads) void pack_bf16_kernel(const PackArgs a) {
-  constexpr int E = 8;
-  for (uint32_t t = blockIdx.x; t < a.tokens; t += gridDim.x) {
-    const uint16_t* kn = a.k_nope + int64_t(t) * a.kn_ts;
-    const uint16_t* pe = a.k_pe + int64_t(t) * a.pe_ts;
-    uint16_t* key = static_cast<uint16_t*>(a.key_out) + int64_t(t) * a.key_row_elems;
-    for (uint32_t c0 = threadIdx.x; c0 < a.chunks; c0 += kPackThreads * U) {
-      uint4 x[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const uint32_t c = c0 + u * kPackThreads;
-        if (c < a.chunks) {
-          const uint32_t h = fdiv(c, a.key_per_row);
-          const uint32_t j = c - h * a.key_per_row.d;
-          x[u] = j < a.nope_chunks ? ld16(kn + int64_t(h) * a.kn_hs + j * E)
-                                   : ld16(pe + (j - a.nope_chunks) * E);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const uint32_t c = c0 + u * kPackThreads;
-        if (c < a.chunks) st16<kPackStream>(key + int64_t(c) * E, x[u]);
-      }
-    }
-  }
+// Source of key chunk `item` (row (t, h) = item / key_per_row).
+template <int E>
+__device__ __forceinline__ const uint16_t* key_src(const PackArgs& a, uint32_t item) {
+  const uint32_t row = fdiv(item, a.key_per_row);
+  const uint32_t j = item - row * a.key_per_row.d;
+  const uint32_t t = fdiv(row, a.heads);
+  const uint32_t h = row - t * a.heads.d;
+  return j < a.nope_chunks ? a.k_nope + int64_t(t) * a.kn_ts + int64_t(h) * a.kn_hs + j * E
+                           : a.k_pe + int64_t(t) * a.pe_ts + (j - a.nope_chunks) * E;
 }
 
-template <bool kScaled, int U>
-__global__ __launch_bounds__(kPackThreads) void pack_fp8_kernel(const PackArgs a) {
+__global__ __launch_bounds__(256) void pack_bf16_kernel(const PackArgs a) {
+  constexpr int E = 8;
+  uint16_t* key = static_cast<uint16_t*>(a.key_out);
+  for (uint32_t item = blockIdx.x * blockDim.x + threadIdx.x; item < a.total;
+       item += gridDim.x * blockDim.x)
+    st16<kPackStream>(key + int64_t(item) * E, ld16(key_src<E>(a, item)));
+}
+
+template <bool kScaled>
+__global__ __launch_bounds__(256) void pack_fp8_kernel(const PackArgs a) {
   constexpr int E = 16;
   float ks = 1.0f, vs = 1.0f;
   if constexpr (kScaled) {
@@ -178,45 +165,27 @@ __global__ __launch_bounds__(kPackThreads) void pack_fp8_kernel(const PackArgs a
   }
   const float kr = 1.0f / ks, vr = 1.0f / vs;
   const uint32_t kf = sign_flip_of(ks), vf = sign_flip_of(vs);
-  for (uint32_t t = blockIdx.x; t < a.tokens; t += gridDim.x) {
-    const uint16_t* kn = a.k_nope + int64_t(t) * a.kn_ts;
-    const uint16_t* pe = a.k_pe + int64_t(t) * a.pe_ts;
-    const uint16_t* vv = a.v + int64_t(t) * a.v_ts;
-    uint8_t* key = static_cast<uint8_t*>(a.key_out) + int64_t(t) * a.key_row_elems;
-    uint8_t* vo = a.v_out + int64_t(t) * a.v_row_elems;
-    for (uint32_t c0 = threadIdx.x; c0 < a.chunks; c0 += kPackThreads * U) {
-      uint4 x0[U], x1[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const uint32_t c = c0 + u * kPackThreads;
-        if (c < a.chunks) {
-          const uint16_t* src;
-          if (c < a.key_chunks) {
-            const uint32_t h = fdiv(c, a.key_per_row);
-            const uint32_t j = c - h * a.key_per_row.d;
-            src = j < a.nope_chunks ? kn + int64_t(h) * a.kn_hs + j * E
-                                    : pe + (j - a.nope_chunks) * E;
-          } else {
-            const uint32_t cv = c - a.key_chunks;
-            const uint32_t h = fdiv(cv, a.v_per_row);
-            const uint32_t j = cv - h * a.v_per_row.d;
-            src = vv + int64_t(h) * a.v_hs + j * E;
-          }
-          x0[u] = ld16(src);
-          x1[u] = ld16(src + 8);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const uint32_t c = c0 + u * kPackThreads;
-        if (c < a.chunks) {
-          const bool is_key = c < a.key_chunks;
-          uint8_t* dst = is_key ? key + int64_t(c) * E : vo + int64_t(c - a.key_chunks) * E;
-          st16<kPackStream>(dst, quant16<kScaled>(x0[u], x1[u], is_key ? ks : vs,
-                                                  is_key ? kr : vr, is_key ? kf : vf));
-        }
-      }
+  for (uint32_t item = blockIdx.x * blockDim.x + threadIdx.x; item < a.total;
+       item += gridDim.x * blockDim.x) {
+    const uint16_t* src;
+    uint8_t* dst;
+    const bool is_key = item < a.key_total;
+    if (is_key) {
+      src = key_src<E>(a, item);
+      dst = static_cast<uint8_t*>(a.key_out) + int64_t(item) * E;
+    } else {
+      const uint32_t vi = item - a.key_total;
+      const uint32_t row = fdiv(vi, a.v_per_row);
+      const uint32_t j = vi - row * a.v_per_row.d;
+      const uint32_t t = fdiv(row, a.heads);
+      const uint32_t h = row - t * a.heads.d;
+      src = a.v + int64_t(t) * a.v_ts + int64_t(h) * a.v_hs + j * E;
+      dst = a.v_out + int64_t(vi) * E;
     }
+    const uint4 x0 = ld16(src);
+    const uint4 x1 = ld16(src + 8);
+    st16<kPackStream>(dst, quant16<kScaled>(x0, x1, is_key ? ks : vs, is_key ? kr : vr,
+                                            is_key ? kf : vf));
   }
 }
 
@@ -335,9 +304,11 @@ extern "C" int32_t mla_ctx_kv_pack(const void* k_nope, int64_t kn_tok_stride,
   const int64_t E = fp8 ? 16 : 8;
   const int64_t key_per_row = (nope + rope) / E;
   const int64_t v_per_row = fp8 ? vdim / E : 0;
-  const int64_t chunks = num_heads * (key_per_row + v_per_row);
-  if (chunks >= (int64_t(1) << 31) || num_tokens >= (int64_t(1) << 31))
-    return fail(MLA_ERR_UNSUPPORTED, "%s: too many heads or tokens for one launch", fn);
+  const int64_t rows = num_tokens * num_heads;
+  const int64_t key_total = rows * key_per_row;
+  const int64_t total = key_total + rows * v_per_row;
+  if (total >= (int64_t(1) << 31) || num_heads > 0x7FFFFFFF)
+    return fail(MLA_ERR_UNSUPPORTED, "%s: more than 2^31 output chunks; split the chunk", fn);
   PackArgs a;
   a.k_nope = static_cast<const uint16_t*>(k_nope);
   a.kn_ts = kn_tok_stride;
@@ -353,20 +324,18 @@ extern "C" int32_t mla_ctx_kv_pack(const void* k_nope, int64_t kn_tok_stride,
   a.v_out = static_cast<uint8_t*>(v_out);
   a.key_per_row = make_fastdiv(static_cast<uint32_t>(key_per_row));
   a.v_per_row = make_fastdiv(static_cast<uint32_t>(v_per_row > 0 ? v_per_row : 1));
+  a.heads = make_fastdiv(static_cast<uint32_t>(num_heads));
   a.nope_chunks = static_cast<uint32_t>(nope / E);
-  a.key_chunks = static_cast<uint32_t>(num_heads * key_per_row);
-  a.chunks = static_cast<uint32_t>(chunks);
-  a.key_row_elems = num_heads * (nope + rope);
-  a.v_row_elems = num_heads * vdim;
-  a.tokens = static_cast<uint32_t>(num_tokens);
+  a.key_total = static_cast<uint32_t>(key_total);
+  a.total = static_cast<uint32_t>(total);
   auto s = static_cast<hipStream_t>(stream);
-  const int64_t cap = max_blocks > 0 ? max_blocks : default_grid_cap();
-  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(num_tokens, cap));
+  const int64_t full = ceil_div(total, 256);
+  const int64_t blocks = max_blocks > 0 ? std::min(full, max_blocks) : full;
   if (!fp8)
-    hipLaunchKernelGGL(pack_bf16_kernel<6>, dim3(blocks), dim3(kPackThreads), 0, s, a);
+    hipLaunchKernelGGL(pack_bf16_kernel, dim3(blocks), dim3(256), 0, s, a);
   else if (k_scale || v_scale)
-    hipLaunchKernelGGL((pack_fp8_kernel<true, 5>), dim3(blocks), dim3(kPackThreads), 0, s, a);
+    hipLaunchKernelGGL(pack_fp8_kernel<true>, dim3(blocks), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((pack_fp8_kernel<false, 5>), dim3(blocks), dim3(kPackThreads), 0, s, a);
+    hipLaunchKernelGGL(pack_fp8_kernel<false>, dim3(blocks), dim3(256), 0, s, a);
   return launch_status(fn);
 }

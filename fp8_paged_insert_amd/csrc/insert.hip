@@ -192,7 +192,12 @@ extern "C" int32_t mla_kv_insert_grouped(
 #define MLA_INSERT_UNROLL 1
 #endif
   constexpr int U = MLA_INSERT_UNROLL;
-  const int64_t blocks = std::min<int64_t>(ceil_div(total, 256 * U), default_grid_cap());
+#ifndef MLA_INSERT_CAP
+#define MLA_INSERT_CAP 0
+#endif
+  const int64_t cap = MLA_INSERT_CAP > 0 ? MLA_INSERT_CAP * int64_t(cu_count())
+                                         : int64_t(0x7FFFFFFF);
+  const int64_t blocks = std::min<int64_t>(ceil_div(total, 256 * U), cap);
   auto s = static_cast<hipStream_t>(stream);
   if (fp8)
     hipLaunchKernelGGL((grouped_insert_kernel<true, U>), dim3(blocks), dim3(256), 0, s, a);
