@@ -31,5 +31,6 @@ from ._binding import (  # noqa: F401
     mla_kv_insert_grouped,
     mla_rope_cos_sin_cache,
     parse_kv_cache_dtype,
+    set_launch_events,
     version,
 )

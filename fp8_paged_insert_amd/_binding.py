@@ -33,7 +33,7 @@ MLA_PACK_KEY_V_FP8 = 1
 
 # Every symbol include/mla_kv.h declares.
 EXPORTS = (
-    "mla_last_error", "mla_version", "mla_parse_kv_cache_dtype",
+    "mla_last_error", "mla_version", "mla_parse_kv_cache_dtype", "mla_set_launch_events",
     "mla_kv_insert_grouped", "mla_rope_cos_sin_cache", "mla_ctx_kv_epilogue",
     "mla_ctx_kv_proj", "mla_ctx_latent_gather", "mla_ctx_kv_pack",
 )
@@ -52,6 +52,7 @@ _SIGS = {
     "mla_last_error": (ctypes.c_char_p, []),
     "mla_version": (ctypes.c_char_p, []),
     "mla_parse_kv_cache_dtype": (_i32, [ctypes.c_char_p, ctypes.POINTER(_i32)]),
+    "mla_set_launch_events": (_i32, [_vp, _vp]),
     "mla_kv_insert_grouped": (_i32, [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _i64,
                                      _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i32, _vp]),
     "mla_rope_cos_sin_cache": (_i32, [_vp, _i64, _i64, _f64, _vp]),
@@ -104,6 +105,15 @@ def parse_kv_cache_dtype(s: str) -> int:
     _check(lib().mla_parse_kv_cache_dtype(s.encode(), ctypes.byref(out)),
            "mla_parse_kv_cache_dtype")
     return out.value
+
+
+def set_launch_events(start=None, stop=None):
+    """Arm timing events for the next kernel this thread launches through the
+    library: torch.cuda.Event objects (already recorded once, so that their
+    HIP events exist) or raw hipEvent_t handles; None, None disarms."""
+    h0 = getattr(start, "cuda_event", start)
+    h1 = getattr(stop, "cuda_event", stop)
+    _check(lib().mla_set_launch_events(h0 or None, h1 or None), "mla_set_launch_events")
 
 
 def _stream(t: torch.Tensor):

@@ -203,7 +203,7 @@ extern "C" int32_t mla_rope_cos_sin_cache(float* out, int64_t max_pos, int64_t r
   if (!out) return fail(MLA_ERR_INVALID_ARGUMENT, "%s: out is NULL", fn);
   const int64_t n = max_pos * (rope_dim / 2);
   const int64_t blocks = std::min<int64_t>(ceil_div(n, 256), default_grid_cap());
-  hipLaunchKernelGGL(rope_table_kernel, dim3(blocks), dim3(256), 0,
+  launch(rope_table_kernel, dim3(blocks), dim3(256), 0,
                      static_cast<hipStream_t>(stream), out, max_pos, rope_dim, base);
   return launch_status(fn);
 }
@@ -259,8 +259,8 @@ extern "C" int32_t mla_ctx_kv_epilogue(
       std::min<int64_t>(ceil_div(num_tokens, kWavesPerBlock), default_grid_cap());
   auto s = static_cast<hipStream_t>(stream);
   if (is_fp8(kv_cache_dtype))
-    hipLaunchKernelGGL(epilogue_kernel<true>, dim3(blocks), dim3(256), 0, s, a);
+    launch(epilogue_kernel<true>, dim3(blocks), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(epilogue_kernel<false>, dim3(blocks), dim3(256), 0, s, a);
+    launch(epilogue_kernel<false>, dim3(blocks), dim3(256), 0, s, a);
   return launch_status(fn);
 }

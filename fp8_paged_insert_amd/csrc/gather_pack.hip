@@ -265,9 +265,9 @@ extern "C" int32_t mla_ctx_latent_gather(const void* cache, int32_t cache_dtype,
   auto s = static_cast<hipStream_t>(stream);
   const int64_t blocks = grid_for(ceil_div(total, kGatherUnroll), max_blocks);
   if (fp8)
-    hipLaunchKernelGGL((gather_kernel<true, kGatherUnroll>), dim3(blocks), dim3(256), 0, s, a);
+    launch((gather_kernel<true, kGatherUnroll>), dim3(blocks), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((gather_kernel<false, kGatherUnroll>), dim3(blocks), dim3(256), 0, s, a);
+    launch((gather_kernel<false, kGatherUnroll>), dim3(blocks), dim3(256), 0, s, a);
   return launch_status(fn);
 }
 
@@ -332,10 +332,10 @@ extern "C" int32_t mla_ctx_kv_pack(const void* k_nope, int64_t kn_tok_stride,
   const int64_t full = ceil_div(total, 256);
   const int64_t blocks = max_blocks > 0 ? std::min(full, max_blocks) : full;
   if (!fp8)
-    hipLaunchKernelGGL(pack_bf16_kernel, dim3(blocks), dim3(256), 0, s, a);
+    launch(pack_bf16_kernel, dim3(blocks), dim3(256), 0, s, a);
   else if (k_scale || v_scale)
-    hipLaunchKernelGGL(pack_fp8_kernel<true>, dim3(blocks), dim3(256), 0, s, a);
+    launch(pack_fp8_kernel<true>, dim3(blocks), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(pack_fp8_kernel<false>, dim3(blocks), dim3(256), 0, s, a);
+    launch(pack_fp8_kernel<false>, dim3(blocks), dim3(256), 0, s, a);
   return launch_status(fn);
 }

@@ -195,7 +195,7 @@ extern "C" int32_t mla_ctx_kv_proj(const void* X, int64_t x_row_stride, int64_t 
       return fail(MLA_ERR_DEVICE, "%s: cannot reserve %zu bytes of LDS", fn, kLdsBytes);
     attr_set = true;
   }
-  hipLaunchKernelGGL(kv_proj_kernel, dim3(tiles), dim3(kThreads), kLdsBytes,
+  launch(kv_proj_kernel, dim3(tiles), dim3(kThreads), kLdsBytes,
                      static_cast<hipStream_t>(stream), a);
   return launch_status(fn);
 }

@@ -200,8 +200,8 @@ extern "C" int32_t mla_kv_insert_grouped(
   const int64_t blocks = std::min<int64_t>(ceil_div(total, 256 * U), cap);
   auto s = static_cast<hipStream_t>(stream);
   if (fp8)
-    hipLaunchKernelGGL((grouped_insert_kernel<true, U>), dim3(blocks), dim3(256), 0, s, a);
+    launch((grouped_insert_kernel<true, U>), dim3(blocks), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((grouped_insert_kernel<false, U>), dim3(blocks), dim3(256), 0, s, a);
+    launch((grouped_insert_kernel<false, U>), dim3(blocks), dim3(256), 0, s, a);
   return launch_status(fn);
 }

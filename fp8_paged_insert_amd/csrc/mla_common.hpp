@@ -3,6 +3,7 @@
 // geometry).  Nothing here is shared with the CPU oracle.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -25,6 +26,23 @@ int cu_count();
 
 // Status after a launch: MLA_ERR_DEVICE if the runtime reports an error.
 int32_t launch_status(const char* what);
+
+// The timing events set by mla_set_launch_events for this thread, if any;
+// taking them clears them.
+bool take_launch_events(hipEvent_t* start, hipEvent_t* stop);
+
+// Every kernel of the library is enqueued through here: a plain launch, or,
+// when the caller armed timing events, one whose start and stop events
+// bracket the kernel's own execution.
+template <typename Kernel, typename... Args>
+void launch(Kernel kernel, dim3 grid, dim3 block, uint32_t shmem, hipStream_t stream,
+            Args... args) {
+  hipEvent_t e0, e1;
+  if (take_launch_events(&e0, &e1))
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, e0, e1, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, args...);
+}
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool bytes16(int64_t elems, int64_t elem_bytes) { return ((elems * elem_bytes) & 15) == 0; }

@@ -10,6 +10,8 @@ namespace mla {
 
 namespace {
 thread_local char g_error[512] = {0};
+thread_local hipEvent_t g_launch_start = nullptr;
+thread_local hipEvent_t g_launch_stop = nullptr;
 constexpr int kMaxDevices = 64;
 int g_cu_count[kMaxDevices] = {0};
 }  // namespace
@@ -41,6 +43,14 @@ int32_t launch_status(const char* what) {
   if (e != hipSuccess)
     return fail(MLA_ERR_DEVICE, "%s: kernel launch failed: %s", what, hipGetErrorString(e));
   return MLA_OK;
+}
+
+bool take_launch_events(hipEvent_t* start, hipEvent_t* stop) {
+  if (!g_launch_start || !g_launch_stop) return false;
+  *start = g_launch_start;
+  *stop = g_launch_stop;
+  g_launch_start = g_launch_stop = nullptr;
+  return true;
 }
 
 int32_t check_cache_dtype(const char* fn, int32_t dt, const float* scales) {
@@ -83,4 +93,14 @@ extern "C" int32_t mla_parse_kv_cache_dtype(const char* s, int32_t* out) {
   }
   return mla::fail(MLA_ERR_INVALID_ARGUMENT,
                    "unknown KV cache dtype '%s' (expected auto, bfloat16, fp8 or fp8_e4m3)", s);
+}
+
+extern "C" int32_t mla_set_launch_events(void* start_event, void* stop_event) {
+  mla::clear_error();
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return mla::fail(MLA_ERR_INVALID_ARGUMENT,
+                     "mla_set_launch_events: pass both events or neither");
+  mla::g_launch_start = static_cast<hipEvent_t>(start_event);
+  mla::g_launch_stop = static_cast<hipEvent_t>(stop_event);
+  return MLA_OK;
 }

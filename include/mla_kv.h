@@ -74,6 +74,15 @@ const char* mla_last_error(void);
 /* Library version string, e.g. "mla_kv 0.1.0 gfx950". */
 const char* mla_version(void);
 
+/* Diagnostics: the next kernel this thread enqueues through the library
+ * records start_event as it begins executing and stop_event as it ends
+ * (hipEvent_t handles created by the caller; hipExtLaunchKernel semantics),
+ * so the pair brackets that kernel alone, without the dispatch gap that
+ * events recorded on the stream around the call would include.  The setting
+ * is consumed by that one launch; pass NULL, NULL to clear it.  Both or
+ * neither must be NULL (MLA_ERR_INVALID_ARGUMENT otherwise). */
+int32_t mla_set_launch_events(void* start_event, void* stop_event);
+
 /* Parse a KV-cache dtype string into *out.  Accepts "auto", "bfloat16",
  * "fp8", "fp8_e4m3" (MLA_OK); "fp8_e5m2" gives MLA_ERR_UNSUPPORTED; anything
  * else MLA_ERR_INVALID_ARGUMENT.  Same whitelist as [P3] 关键源码片段

@@ -198,3 +198,25 @@ def test_long_context_pack_16_chunks_sampled(mk):
         torch.cuda.synchronize()
         assert np.array_equal(u8(key[pick.to(DEV)]), rk), c
         assert np.array_equal(u8(vo[pick.to(DEV)]), rv), c
+
+
+def test_launch_events_bracket_one_kernel(mk):
+    """mla_set_launch_events: the next launch records the pair, later ones don't."""
+    announce("launch events")
+    g = torch.Generator().manual_seed(21)
+    kvb = synth.bf16_normal((2048, 16, 256), g).to(DEV)
+    ws = synth.bf16_normal((2048, 576), g).to(DEV)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    e1.record()
+    torch.cuda.synchronize()
+    mk.set_launch_events(e0, e1)
+    key, _ = gpu_pack(mk, kvb, ws[:, 512:], False)
+    torch.cuda.synchronize()
+    t1 = e0.elapsed_time(e1)
+    assert t1 > 0.0
+    gpu_pack(mk, kvb, ws[:, 512:], False)        # not armed: the pair is untouched
+    torch.cuda.synchronize()
+    assert e0.elapsed_time(e1) == t1
+    with pytest.raises(mk.MlaError):
+        mk.set_launch_events(e0, None)
