@@ -219,7 +219,9 @@ def small_batch(torch, mk, dev):
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) / n * 1e6
 
+    plan = mk.prepare_insert_grouped(kv, pe, ptrs, sm, 64, 64 * W, W, sc, "fp8")
     wall_binding = per_call_us(call)
+    wall_prepared = per_call_us(plan)
     wall_raw = per_call_us(raw)
     kernel = time_kernel(torch, raw, reps=200)
     # graph replay: 100 inserts captured once
@@ -259,6 +261,7 @@ def small_batch(torch, mk, dev):
     five_us = per_call_us(five, n=300)
     return {"workload": "grouped fp8 insert, 5 layers x 4 tokens (one -1 slot)",
             "us_per_launch_wall": round(wall_binding, 2),
+            "us_per_launch_wall_prepared": round(wall_prepared, 2),
             "us_per_launch_wall_raw_abi": round(wall_raw, 2),
             "us_kernel": round(kernel, 2),
             "us_per_launch_graph_replay": graph_us if isinstance(graph_us, str) else round(graph_us, 2),

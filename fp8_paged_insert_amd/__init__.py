@@ -31,6 +31,8 @@ from ._binding import (  # noqa: F401
     mla_kv_insert_grouped,
     mla_rope_cos_sin_cache,
     parse_kv_cache_dtype,
+    prepare_insert_grouped,
+    PreparedInsert,
     set_launch_events,
     version,
 )

@@ -116,9 +116,16 @@ def set_launch_events(start=None, stop=None):
     _check(lib().mla_set_launch_events(h0 or None, h1 or None), "mla_set_launch_events")
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(t: torch.Tensor):
+    """torch's current HIP stream on the tensor's device (a hipStream_t)."""
     if t.device.type != "cuda":
         raise RuntimeError(f"tensor on {t.device}, expected a GPU tensor")
+    if _raw_stream is not None:
+        return _raw_stream(t.device.index if t.device.index is not None else
+                           torch.cuda.current_device())
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
@@ -148,9 +155,17 @@ def _check_scales(scales, n, ref, name="kv_scales"):
         raise RuntimeError(f"{name} must be contiguous")
 
 
+_dtype_codes = {}
+
+
 def _cache_dtype_code(kv_cache_dtype) -> int:
+    """Dtype string -> code through the library's parser (memoised)."""
     if isinstance(kv_cache_dtype, str):
-        return parse_kv_cache_dtype(kv_cache_dtype)
+        code = _dtype_codes.get(kv_cache_dtype)
+        if code is None:
+            code = parse_kv_cache_dtype(kv_cache_dtype)
+            _dtype_codes[kv_cache_dtype] = code
+        return code
     return int(kv_cache_dtype)
 
 
@@ -211,16 +226,10 @@ def _slots_2d(slot_mapping, L, T):
 
 
 # ---------------------------------------------------------------------------
-def mla_kv_insert_grouped(kv_c, k_pe, kv_cache_ptrs, slot_mapping, block_size,
-                          block_stride, entry_stride, kv_scales=None,
-                          kv_cache_dtype="auto"):
-    """Grouped insert of [kv_c | k_pe] rows of every layer into its paged cache.
-
-    kv_c [L, T, R] / k_pe [L, T, P] bf16 views (innermost dim contiguous);
-    kv_cache_ptrs int64 [L] device table; slot_mapping int64 [L, T] (layer
-    stride 0 allowed) or [T] shared; block/entry strides in cache elements;
-    kv_scales fp32 [L] for fp8 caches, None otherwise.
-    """
+def _insert_args(kv_c, k_pe, kv_cache_ptrs, slot_mapping, block_size, block_stride,
+                 entry_stride, kv_scales, kv_cache_dtype):
+    """Check and marshal the grouped-insert arguments; returns the C argument
+    tuple and the device pointer table it refers to."""
     _need(kv_c, (torch.bfloat16,), "kv_c")
     _need(k_pe, (torch.bfloat16,), "k_pe")
     if kv_c.dim() != 3 or k_pe.dim() != 3:
@@ -243,11 +252,56 @@ def mla_kv_insert_grouped(kv_c, k_pe, kv_cache_ptrs, slot_mapping, block_size,
         _check_scales(kv_scales, L, kv_c)
     elif kv_scales is not None:
         raise RuntimeError("a bf16 cache takes no kv_scales")
-    st = lib().mla_kv_insert_grouped(
-        _ptr(kv_c), kv_c.stride(0), kv_c.stride(1), _ptr(k_pe), k_pe.stride(0), k_pe.stride(1),
-        _ptr(kv_cache_ptrs), _ptr(kv_scales), _ptr(sm), sls, L, T, R, P,
-        int(block_size), int(block_stride), int(entry_stride), dt, _stream(kv_c))
-    _check(st, "mla_kv_insert_grouped")
+    args = (_ptr(kv_c), kv_c.stride(0), kv_c.stride(1), _ptr(k_pe), k_pe.stride(0),
+            k_pe.stride(1), _ptr(kv_cache_ptrs), _ptr(kv_scales), _ptr(sm), sls, L, T, R, P,
+            int(block_size), int(block_stride), int(entry_stride), dt, _stream(kv_c))
+    return args, kv_cache_ptrs
+
+
+def mla_kv_insert_grouped(kv_c, k_pe, kv_cache_ptrs, slot_mapping, block_size,
+                          block_stride, entry_stride, kv_scales=None,
+                          kv_cache_dtype="auto"):
+    """Grouped insert of [kv_c | k_pe] rows of every layer into its paged cache.
+
+    kv_c [L, T, R] / k_pe [L, T, P] bf16 views (innermost dim contiguous);
+    kv_cache_ptrs: int64 [L] device table of cache bases, or the list of L
+    cache tensors (then checked against the dtype and layout arguments);
+    slot_mapping int64 [L, T] (layer stride 0 allowed) or [T] shared;
+    block/entry strides in cache elements; kv_scales fp32 [L] for fp8 caches,
+    None otherwise.
+    """
+    args, _ = _insert_args(kv_c, k_pe, kv_cache_ptrs, slot_mapping, block_size, block_stride,
+                           entry_stride, kv_scales, kv_cache_dtype)
+    _check(lib().mla_kv_insert_grouped(*args), "mla_kv_insert_grouped")
+
+
+class PreparedInsert:
+    """mla_kv_insert_grouped with its arguments checked once.  Calling the
+    object enqueues the same insert again on the current stream of the
+    tensors' device: their contents may change between calls, their storage
+    and layout may not.  Meant for decode loops inserting a few tokens per
+    step, where the per-call checks would cost more than the kernel."""
+
+    def __init__(self, kv_c, k_pe, kv_cache_ptrs, slot_mapping, block_size, block_stride,
+                 entry_stride, kv_scales=None, kv_cache_dtype="auto"):
+        args, table = _insert_args(kv_c, k_pe, kv_cache_ptrs, slot_mapping, block_size,
+                                   block_stride, entry_stride, kv_scales, kv_cache_dtype)
+        self._keep = (kv_c, k_pe, table, slot_mapping, kv_scales)  # keep storage alive
+        self._args = list(args)
+        self._index = kv_c.device.index if kv_c.device.index is not None else \
+            torch.cuda.current_device()
+        self._fn = lib().mla_kv_insert_grouped
+
+    def __call__(self):
+        self._args[-1] = (_raw_stream(self._index) if _raw_stream is not None else
+                          torch.cuda.current_stream(self._index).cuda_stream)
+        st = self._fn(*self._args)
+        if st != MLA_OK:
+            _check(st, "mla_kv_insert_grouped")
+
+
+def prepare_insert_grouped(*args, **kwargs) -> PreparedInsert:
+    return PreparedInsert(*args, **kwargs)
 
 
 def mla_rope_cos_sin_cache(out, max_pos, rope_dim, base=10000.0):

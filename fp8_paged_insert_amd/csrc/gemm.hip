@@ -41,13 +41,15 @@ constexpr int kAChunks = kBM * kBK / 8 / kThreads;  // 16-byte loads per thread 
 constexpr int kBChunks = kBN * kBK / 8 / kThreads;  // and for W
 constexpr size_t kLdsBytes = size_t(2) * (kBM + kBN) * kLdsRow * 2;
 
+constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, one L2 each
+
 struct GemmArgs {
   const uint16_t* x;
   const uint16_t* w;
   uint16_t* y;
   int64_t ldx, ldy;
   int32_t T, K, N;
-  int32_t tiles_n;
+  int32_t tiles_n, tiles, tiles_per_xcd;
 };
 
 __global__ __launch_bounds__(kThreads, 1) void kv_proj_kernel(const GemmArgs a) {
@@ -59,8 +61,18 @@ __global__ __launch_bounds__(kThreads, 1) void kv_proj_kernel(const GemmArgs a) 
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = (blockIdx.x / a.tiles_n) * kBM;
-  const int n0 = (blockIdx.x % a.tiles_n) * kBN;
+  // Workgroups are dispatched round-robin over the XCDs; give XCD x the run
+  // of tiles [x * per, (x + 1) * per) in row-major tile order, so the
+  // workgroups sharing one L2 also share their X row blocks (for the
+  // 16 x 15 tile workload: 2 tile rows per XCD, 15 workgroups per X block).
+#ifndef MLA_GEMM_XCD_REMAP
+#define MLA_GEMM_XCD_REMAP 1
+#endif
+  const int tile = MLA_GEMM_XCD_REMAP ? (blockIdx.x % kXcds) * a.tiles_per_xcd + blockIdx.x / kXcds
+                                      : static_cast<int>(blockIdx.x);
+  if (tile >= a.tiles) return;
+  const int m0 = (tile / a.tiles_n) * kBM;
+  const int n0 = (tile % a.tiles_n) * kBN;
 
   // this thread's global chunks: row = (tid >> 3) + 32 i, 16-byte column c
   const int c = tid & 7;
@@ -117,20 +129,27 @@ __global__ __launch_bounds__(kThreads, 1) void kv_proj_kernel(const GemmArgs a) 
     if (kb + 1 < stages) load_stage((kb + 1) * kBK);
     const uint16_t* as = As + buf * kBM * kLdsRow + (wm * kWaveM + frow) * kLdsRow + fk;
     const uint16_t* bs = Bs + buf * kBN * kLdsRow + (wn * kWaveN + frow) * kLdsRow + fk;
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      bf16x8_t fa[kSubM], fb[kSubN];
+    // fragments of k step kk + 1 are read while the MFMAs of step kk run
+    bf16x8_t fa[2][kSubM], fb[2][kSubN];
+    auto read_frags = [&](int slot, int kk) {
 #pragma unroll
       for (int i = 0; i < kSubM; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8_t*>(as + i * 32 * kLdsRow + kk * 16);
+        fa[slot][i] = *reinterpret_cast<const bf16x8_t*>(as + i * 32 * kLdsRow + kk * 16);
 #pragma unroll
       for (int j = 0; j < kSubN; ++j)
-        fb[j] = *reinterpret_cast<const bf16x8_t*>(bs + j * 32 * kLdsRow + kk * 16);
+        fb[slot][j] = *reinterpret_cast<const bf16x8_t*>(bs + j * 32 * kLdsRow + kk * 16);
+    };
+    read_frags(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      const int cur = kk & 1;
+      if (kk + 1 < kBK / 16) read_frags(cur ^ 1, kk + 1);
 #pragma unroll
       for (int i = 0; i < kSubM; ++i)
 #pragma unroll
         for (int j = 0; j < kSubN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j],
+                                                              0, 0, 0);
     }
     if (kb + 1 < stages) store_stage(buf ^ 1);
     __syncthreads();
@@ -187,6 +206,9 @@ extern "C" int32_t mla_ctx_kv_proj(const void* X, int64_t x_row_stride, int64_t 
   a.N = static_cast<int32_t>(N);
   a.tiles_n = static_cast<int32_t>(ceil_div(N, kBN));
   const int64_t tiles = ceil_div(T, kBM) * a.tiles_n;
+  a.tiles = static_cast<int32_t>(tiles);
+  a.tiles_per_xcd = static_cast<int32_t>(ceil_div(tiles, kXcds));
+  const int64_t grid = int64_t(a.tiles_per_xcd) * kXcds;
   static bool attr_set = false;
   if (!attr_set) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kv_proj_kernel),
@@ -195,7 +217,7 @@ extern "C" int32_t mla_ctx_kv_proj(const void* X, int64_t x_row_stride, int64_t 
       return fail(MLA_ERR_DEVICE, "%s: cannot reserve %zu bytes of LDS", fn, kLdsBytes);
     attr_set = true;
   }
-  launch(kv_proj_kernel, dim3(tiles), dim3(kThreads), kLdsBytes,
+  launch(kv_proj_kernel, dim3(grid), dim3(kThreads), kLdsBytes,
                      static_cast<hipStream_t>(stream), a);
   return launch_status(fn);
 }

@@ -217,3 +217,28 @@ def test_long_context_insert_full_size(mk):
                              np.arange(len(pick), dtype=np.int64), ref,
                              scale=float(d["scales"][l]))
         assert np.array_equal(got[slots[pick]], ref[:, 0]), f"layer {l}"
+
+
+def test_prepared_insert_matches_and_follows_contents(mk):
+    """PreparedInsert re-enqueues the checked insert; new input contents are
+    picked up on every call."""
+    announce("prepared insert")
+    d = to_dev(synth.small_batch_fp8())
+    caches = d["caches"]
+    a = [c.clone() for c in caches]
+    plan = mk.prepare_insert_grouped(d["kv_c"], d["k_pe"], a, d["slot_mapping"], 64,
+                                     a[0].stride(0), a[0].stride(1), d["scales"], "fp8")
+    plan()
+    b = [c.clone() for c in caches]
+    mk.mla_kv_insert_grouped(d["kv_c"], d["k_pe"], b, d["slot_mapping"], 64, b[0].stride(0),
+                             b[0].stride(1), d["scales"], "fp8")
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    d["kv_c"].mul_(-1)            # same storage, new contents
+    plan()
+    mk.mla_kv_insert_grouped(d["kv_c"], d["k_pe"], b, d["slot_mapping"], 64, b[0].stride(0),
+                             b[0].stride(1), d["scales"], "fp8")
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
