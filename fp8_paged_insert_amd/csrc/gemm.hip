@@ -16,12 +16,17 @@
 //  * both operands are K-contiguous (W is the linear layer's [out, in]
 //    storage), so one 16-byte LDS read gives a lane its 8 consecutive K
 //    values for either MFMA operand;
-//  * LDS rows are padded to 144 bytes: 16 consecutive rows then start on
-//    16 distinct 4-bank groups, so the 16-byte fragment reads of a
-//    half-wavefront are conflict-free;
-//  * two LDS stages; the next stage's global loads are issued into registers
-//    before the current stage's MFMAs and written to the other LDS buffer
-//    after them, with one barrier per stage;
+//  * operand tiles go from global memory straight into LDS
+//    (global_load_lds_dwordx4, 1 KiB per wavefront instruction), no
+//    register staging; LDS rows are 128 bytes with an XOR swizzle of the
+//    16-byte chunks, so the fragment reads are bank-conflict free;
+//  * two LDS stages and one barrier per stage, placed before the last of
+//    the four K steps: that step's MFMAs hide both the next stage's first
+//    fragment reads and the copy of the stage after it, and every other
+//    step's MFMAs hide the next step's fragment reads (the issue order is
+//    pinned with sched_group_barrier);
+//  * tiles are grouped per XCD so the workgroups sharing an L2 share their
+//    X and W blocks;
 //  * rows beyond T and columns beyond N are clamped on load and masked on
 //    store, so any T >= 1 and any N that is a multiple of 16 work.
 #include "mla_common.hpp"
@@ -31,17 +36,24 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void global_void_t;
 
 constexpr int kBM = 256, kBN = 192, kBK = 64;
-constexpr int kLdsRow = kBK + 8;  // bf16 elements per LDS row (144 bytes)
 constexpr int kThreads = 256;
-constexpr int kWaveM = 128, kWaveN = 96;   // per-wavefront tile
+constexpr int kRowBytes = kBK * 2;                      // one tile row of K values in LDS
+constexpr int kStageBytes = (kBM + kBN) * kRowBytes;    // X tile then W tile
+constexpr size_t kLdsBytes = size_t(2) * kStageBytes;   // two stages: 114688 bytes
+constexpr int kWaveM = 128, kWaveN = 96;                // per-wavefront tile
 constexpr int kSubM = kWaveM / 32, kSubN = kWaveN / 32;
-constexpr int kAChunks = kBM * kBK / 8 / kThreads;  // 16-byte loads per thread for X
-constexpr int kBChunks = kBN * kBK / 8 / kThreads;  // and for W
-constexpr size_t kLdsBytes = size_t(2) * (kBM + kBN) * kLdsRow * 2;
+constexpr int kXBlocks = kBM / 8 / 4;  // 1 KiB (8-row) LDS blocks of X each wavefront fills
+constexpr int kWBlocks = kBN / 8 / 4;  // and of W
+
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedLdsRead = 0x100;
 
 constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, one L2 each
+constexpr int kGroupRows = 4;
 
 struct GemmArgs {
   const uint16_t* x;
@@ -52,60 +64,65 @@ struct GemmArgs {
   int32_t tiles_n, tiles, tiles_per_xcd;
 };
 
+// The 16-byte chunk c of tile row r sits in LDS slot c ^ swz(r) of that row.
+// Rows are 128 bytes, so without the swizzle the fragment reads (32 rows,
+// one chunk each) would all hit the same 4 banks; with it, any 8 consecutive
+// rows, and the 8 even or the 8 odd rows of any 16, cover 8 distinct slots.
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+// One wavefront-wide direct copy of 16 bytes per lane from global memory into
+// LDS; lane l's bytes land at dst + 16 l (dst is wavefront-uniform).
+__device__ __forceinline__ void copy_to_lds(const uint16_t* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds((global_void_t*)src, (lds_void_t*)dst, 16, 0, 0);
+}
+
 __global__ __launch_bounds__(kThreads, 1) void kv_proj_kernel(const GemmArgs a) {
-  extern __shared__ __align__(16) uint16_t lds[];
-  uint16_t* As = lds;                                  // [2][kBM][kLdsRow]
-  uint16_t* Bs = lds + 2 * kBM * kLdsRow;              // [2][kBN][kLdsRow]
+  extern __shared__ __align__(16) uint8_t lds[];   // [2 stages][kBM + kBN rows][128 B]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  // Workgroups are dispatched round-robin over the XCDs; give XCD x the run
-  // of tiles [x * per, (x + 1) * per) in row-major tile order, so the
-  // workgroups sharing one L2 also share their X row blocks (for the
-  // 16 x 15 tile workload: 2 tile rows per XCD, 15 workgroups per X block).
-#ifndef MLA_GEMM_XCD_REMAP
-#define MLA_GEMM_XCD_REMAP 1
-#endif
-  const int tile = MLA_GEMM_XCD_REMAP ? (blockIdx.x % kXcds) * a.tiles_per_xcd + blockIdx.x / kXcds
-                                      : static_cast<int>(blockIdx.x);
-  if (tile >= a.tiles) return;
-  const int m0 = (tile / a.tiles_n) * kBM;
-  const int n0 = (tile % a.tiles_n) * kBN;
+  // Workgroups are dispatched round-robin over the XCDs.  Tiles are
+  // numbered in groups of kGroupRows tile rows, column by column inside a
+  // group, and XCD x takes the run [x * per, (x + 1) * per) of that order:
+  // the workgroups sharing one L2 then cover a compact block of tiles (for
+  // the 16 x 15 tile workload: 4 tile rows by 7 or 8 tile columns), which
+  // reads fewer distinct X and W bytes per L2 than whole tile rows would.
+  const int t = (blockIdx.x % kXcds) * a.tiles_per_xcd + blockIdx.x / kXcds;
+  if (t >= a.tiles) return;
+  const int tiles_m = a.tiles / a.tiles_n;
+  const int group = t / (kGroupRows * a.tiles_n);
+  const int in_group = t - group * kGroupRows * a.tiles_n;
+  const int group_rows = min(kGroupRows, tiles_m - group * kGroupRows);
+  const int m0 = (group * kGroupRows + in_group % group_rows) * kBM;
+  const int n0 = (in_group / group_rows) * kBN;
 
-  // this thread's global chunks: row = (tid >> 3) + 32 i, 16-byte column c
-  const int c = tid & 7;
-  const int r0 = tid >> 3;
-  const uint16_t* xg[kAChunks];
-  const uint16_t* wg[kBChunks];
+  // Loading: each 1 KiB block of a stage holds 8 tile rows; lane l of the
+  // copy fills slot (l & 7) of row (l >> 3), so it fetches chunk
+  // (l & 7) ^ swz(row).  Rows beyond T or N are clamped (masked on store).
+  const uint16_t* xsrc[kXBlocks];
+  const uint16_t* wsrc[kWBlocks];
 #pragma unroll
-  for (int i = 0; i < kAChunks; ++i) {
-    const int m = min(m0 + r0 + 32 * i, a.T - 1);
-    xg[i] = a.x + int64_t(m) * a.ldx + c * 8;
+  for (int i = 0; i < kXBlocks; ++i) {
+    const int r = (wave * kXBlocks + i) * 8 + (lane >> 3);
+    const int m = min(m0 + r, a.T - 1);
+    xsrc[i] = a.x + int64_t(m) * a.ldx + ((lane & 7) ^ swz(r)) * 8;
   }
 #pragma unroll
-  for (int i = 0; i < kBChunks; ++i) {
-    const int n = min(n0 + r0 + 32 * i, a.N - 1);
-    wg[i] = a.w + int64_t(n) * a.K + c * 8;
+  for (int i = 0; i < kWBlocks; ++i) {
+    const int r = (wave * kWBlocks + i) * 8 + (lane >> 3);
+    const int n = min(n0 + r, a.N - 1);
+    wsrc[i] = a.w + int64_t(n) * a.K + ((lane & 7) ^ swz(r)) * 8;
   }
-
-  uint4 ra[kAChunks], rb[kBChunks];
-  auto load_stage = [&](int k0) {
+  auto issue_stage = [&](int kb, int buf) {
+    uint8_t* base = lds + buf * kStageBytes;
 #pragma unroll
-    for (int i = 0; i < kAChunks; ++i) ra[i] = ld16(xg[i] + k0);
+    for (int i = 0; i < kXBlocks; ++i)
+      copy_to_lds(xsrc[i] + kb * kBK, base + (wave * kXBlocks + i) * 1024);
 #pragma unroll
-    for (int i = 0; i < kBChunks; ++i) rb[i] = ld16(wg[i] + k0);
-  };
-  auto store_stage = [&](int buf) {
-    uint16_t* as = As + buf * kBM * kLdsRow;
-    uint16_t* bs = Bs + buf * kBN * kLdsRow;
-#pragma unroll
-    for (int i = 0; i < kAChunks; ++i)
-      *reinterpret_cast<uint4*>(as + (r0 + 32 * i) * kLdsRow + c * 8) = ra[i];
-#pragma unroll
-    for (int i = 0; i < kBChunks; ++i)
-      *reinterpret_cast<uint4*>(bs + (r0 + 32 * i) * kLdsRow + c * 8) = rb[i];
+    for (int i = 0; i < kWBlocks; ++i)
+      copy_to_lds(wsrc[i] + kb * kBK, base + kBM * kRowBytes + (wave * kWBlocks + i) * 1024);
   };
 
   f32x16_t acc[kSubM][kSubN];
@@ -116,44 +133,101 @@ __global__ __launch_bounds__(kThreads, 1) void kv_proj_kernel(const GemmArgs a) 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // fragment addressing: lane -> row (lane & 31), k group (lane >> 5) * 8
-  const int frow = lane & 31;
-  const int fk = (lane >> 5) * 8;
-
-  const int stages = a.K / kBK;
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-  for (int kb = 0; kb < stages; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < stages) load_stage((kb + 1) * kBK);
-    const uint16_t* as = As + buf * kBM * kLdsRow + (wm * kWaveM + frow) * kLdsRow + fk;
-    const uint16_t* bs = Bs + buf * kBN * kLdsRow + (wn * kWaveN + frow) * kLdsRow + fk;
-    // fragments of k step kk + 1 are read while the MFMAs of step kk run
-    bf16x8_t fa[2][kSubM], fb[2][kSubN];
-    auto read_frags = [&](int slot, int kk) {
+  // Fragments: lane l takes tile row (l & 31) of a 32-row block and the
+  // 8 K values of chunk 2 kk + (l >> 5).
+  const int hi = lane >> 5;
+  auto frag_off = [&](int row, int kk) {
+    return row * kRowBytes + (((2 * kk + hi) ^ swz(row)) << 4);
+  };
+  int xoff[kSubM][kBK / 16], woff[kSubN][kBK / 16];
 #pragma unroll
-      for (int i = 0; i < kSubM; ++i)
-        fa[slot][i] = *reinterpret_cast<const bf16x8_t*>(as + i * 32 * kLdsRow + kk * 16);
+  for (int kk = 0; kk < kBK / 16; ++kk) {
+#pragma unroll
+    for (int i = 0; i < kSubM; ++i) xoff[i][kk] = frag_off(wm * kWaveM + i * 32 + (lane & 31), kk);
+#pragma unroll
+    for (int j = 0; j < kSubN; ++j)
+      woff[j][kk] = kBM * kRowBytes + frag_off(wn * kWaveN + j * 32 + (lane & 31), kk);
+  }
+
+  // Pipeline, per stage kb computed from buffer b = kb & 1:
+  //   steps 0..2: MFMAs of step kk with the fragments of step kk + 1 read
+  //               under them;
+  //   barrier:    this wavefront's copy of stage kb + 1 (into b ^ 1) has
+  //               landed, every wavefront's has, and all fragment reads of
+  //               buffer b are done (step 3's are already in registers);
+  //   step 3:     MFMAs, with stage kb + 1's step-0 fragments read from
+  //               b ^ 1 and stage kb + 2 copied into b under them.
+  // Each copy thus has one stage of MFMAs to land, and no fragment read
+  // waits right after a barrier.  Copies past the last stage repeat the
+  // last stage into a free buffer, so the loop body has no branches.
+  const int stages = a.K / kBK;
+  bf16x8_t fa[2][kSubM], fb[2][kSubN];
+  auto read_frags = [&](int slot, const uint8_t* base, int kk) {
+#pragma unroll
+    for (int i = 0; i < kSubM; ++i)
+      fa[slot][i] = *reinterpret_cast<const bf16x8_t*>(base + xoff[i][kk]);
+#pragma unroll
+    for (int j = 0; j < kSubN; ++j)
+      fb[slot][j] = *reinterpret_cast<const bf16x8_t*>(base + woff[j][kk]);
+  };
+  auto mfma_step = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < kSubM; ++i)
 #pragma unroll
       for (int j = 0; j < kSubN; ++j)
-        fb[slot][j] = *reinterpret_cast<const bf16x8_t*>(bs + j * 32 * kLdsRow + kk * 16);
-    };
-    read_frags(0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j],
+                                                            0, 0, 0);
+  };
+  constexpr int kFrags = kSubM + kSubN;          // fragment reads per step
+  constexpr int kMfma = kSubM * kSubN;           // MFMAs per step
+  constexpr int kCopies = kXBlocks + kWBlocks;   // copy instructions per stage
+  constexpr int kTail = kMfma - kFrags;          // MFMAs of step 3 with no fragment read
+  constexpr int kCopiesPer = (kCopies + kTail - 1) / kTail;
+
+  issue_stage(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  issue_stage(min(1, stages - 1), 1);
+  read_frags(0, lds, 0);
+  for (int kb = 0; kb < stages; ++kb) {
+    const int buf = kb & 1;
+    const uint8_t* base = lds + buf * kStageBytes;
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      const int cur = kk & 1;
-      if (kk + 1 < kBK / 16) read_frags(cur ^ 1, kk + 1);
-#pragma unroll
-      for (int i = 0; i < kSubM; ++i)
-#pragma unroll
-        for (int j = 0; j < kSubN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j],
-                                                              0, 0, 0);
+    for (int kk = 0; kk < kBK / 16 - 1; ++kk) {
+      read_frags((kk + 1) & 1, base, kk + 1);
+      mfma_step(kk & 1);
     }
-    if (kb + 1 < stages) store_stage(buf ^ 1);
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16 - 1; ++kk) {
+#pragma unroll
+      for (int q = 0; q < kFrags; ++q) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedLdsRead, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, kMfma - kFrags, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // the schedules above and below stay apart
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(0, lds + (buf ^ 1) * kStageBytes, 0);
+    issue_stage(min(kb + 2, stages - 1), buf);
+    mfma_step(1);
+    // the copies write LDS, so they stay behind the fragment reads
+#pragma unroll
+    for (int q = 0; q < kFrags; ++q) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedLdsRead, 1, 0);
+    }
+#pragma unroll
+    for (int q = 0; q + 1 < kTail; ++q) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, kCopiesPer, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, kCopies - kCopiesPer * (kTail - 1), 0);
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // the repeated copies have landed
 
   // accumulator layout: value r of lane l is C[8 (r / 4) + 4 (l / 32) + (r % 4)][l % 32]
 #pragma unroll
