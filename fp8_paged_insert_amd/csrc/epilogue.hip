@@ -14,13 +14,15 @@
 //
 // gfx950 design: the pages run a permute + copy, a grouped RMSNorm, a
 // flatten + RoPE and the grouped insert as separate passes over HBM; here one
-// 64-lane wavefront owns one (layer, token) row end to end.  Each lane loads
-// 8 kv_c values (one 16-byte load straight from the strided [T, L, 576]
-// projection output, so no layer-major copy is made), the sum of squares is
-// reduced across the wavefront, lanes 0-3 rotate the 64 k_pe values in
-// (i, i + 32) pairs, and the row is converted and stored with 8/16-byte
-// vector stores.  The token's position indexes the fp32 cos/sin table
-// directly instead of a repeated-positions buffer.
+// pass reads each (layer, token) row of the strided [T, L, 576] projection
+// output once (no layer-major copy) and writes its cache entry.  A row
+// belongs to 16 lanes (a DPP row), 4 rows per wavefront: lane j holds the
+// kv_c chunks j, j + 16, j + 32, j + 48 (8 values each) and k_pe[4j, 4j + 4),
+// so every load and store instruction covers 128-256 contiguous bytes per
+// row.  The sum of squares is reduced with four in-row DPP steps (no LDS
+// round trip), RoPE's (i, i + 32) pairs sit in lanes j and j ^ 8 and swap
+// with one DPP row rotation, and the token's position indexes the fp32
+// cos/sin table directly instead of a repeated-positions buffer.
 #include "mla_common.hpp"
 
 namespace mla {
@@ -49,13 +51,14 @@ __global__ __launch_bounds__(256) void rope_table_kernel(float* out, int64_t max
 }
 
 // ---------------------------------------------------------------- epilogue --
-constexpr int kR = 512;  // kv_lora_rank: lane i owns kv_c[8i, 8i + 8)
-constexpr int kP = 64;   // rope dim: lane i owns k_pe[i]; lanes i and i ^ 32 pair up
-#ifndef MLA_EPI_LAYERS
-#define MLA_EPI_LAYERS 5
-#endif
-constexpr int kMaxLayers = MLA_EPI_LAYERS;  // layers one wavefront keeps in flight
+constexpr int kR = 512;  // kv_lora_rank
+constexpr int kP = 64;   // rope dim
+constexpr int kRowLanes = 16;                       // lanes per (layer, token) row
+constexpr int kRowsPerWave = 64 / kRowLanes;
+constexpr int kChunks = kR / 8 / kRowLanes;         // 16-byte kv_c chunks per lane
+constexpr int kPe = kP / kRowLanes;                 // k_pe values per lane
 constexpr int kWavesPerBlock = 4;
+constexpr int kRowsPerBlock = kRowsPerWave * kWavesPerBlock;
 
 struct EpiArgs {
   const uint16_t* all_kv;
@@ -71,13 +74,28 @@ struct EpiArgs {
   int64_t sls;
   int64_t block_size, block_stride, entry_stride;
   uint16_t* dbg;
-  FastDiv bsize;
-  uint32_t layers, tokens;
+  FastDiv bsize, nlayers;
+  uint32_t layers, tokens, rows;
 };
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+// DPP moves inside a row of 16 lanes (every source lane is valid).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within each half row
+constexpr int kDppMirror = 0x140;     // lane i <-> 15 - i
+constexpr int kDppRor8 = 0x128;       // lane i <- lane (i + 8) mod 16
+
+// Sum over the 16 lanes of a row; every lane gets the same bits (each step
+// adds two partial sums, and fp32 addition is commutative).
+__device__ __forceinline__ float row_sum(float v) {
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  v += dpp_f<kDppMirror>(v);
   return v;
 }
 
@@ -91,97 +109,118 @@ __device__ __forceinline__ int64_t entry_offset(int64_t s, const EpiArgs& a) {
   return blk * a.block_stride + (s - blk * a.block_size) * a.entry_stride;
 }
 
-// One wavefront owns one token and walks its layers in groups of up to
-// kMaxLayers: every load of the group (the token's rows of all_kv are
-// adjacent in the [T, L, 576] projection output) is issued before the first
-// reduction.  RoPE pairs (i, i + 32) live in lanes i and i ^ 32, which swap
-// values with one cross-half shuffle; the token's cos/sin row is read once
-// (lane i holds cos_i for i < 32 and sin_{i-32} above) and shared by all
-// layers.
+// Rows are numbered token-major (row = t * L + l), the order of the
+// projection output, so the 4 rows of a wavefront are adjacent in memory.
 template <bool kFp8>
 __global__ __launch_bounds__(256) void epilogue_kernel(const EpiArgs a) {
   const int lane = threadIdx.x & 63;
+  const int j = lane & (kRowLanes - 1);       // lane within the row
+  const int grp = lane / kRowLanes;           // row within the wavefront
   const uint32_t wave = threadIdx.x >> 6;
-  const bool lo_half = lane < 32;
-  for (uint32_t t = blockIdx.x * kWavesPerBlock + wave; t < a.tokens;
-       t += gridDim.x * kWavesPerBlock) {
-    const uint16_t* tok = a.all_kv + int64_t(t) * a.kts;
-    // positions outside [0, max_pos) break the precondition; clamp so the
+  const bool first_half = j < kRowLanes / 2;  // holds k_pe[i], i < 32
+  for (uint32_t r0 = (blockIdx.x * kWavesPerBlock + wave) * kRowsPerWave; r0 < a.rows;
+       r0 += gridDim.x * kRowsPerBlock) {
+    const uint32_t r = r0 + grp;
+    const bool active = r < a.rows;
+    const uint32_t rr = active ? r : a.rows - 1;   // idle lanes still load in bounds
+    const uint32_t t = fdiv(rr, a.nlayers);
+    const uint32_t l = rr - t * a.layers;
+    const uint16_t* row = a.all_kv + int64_t(t) * a.kts + int64_t(l) * a.kls;
+    const uint16_t* grow = a.gamma + int64_t(l) * kR;
+
+    // The position is loaded first: the table read that depends on it then
+    // waits only for that load (loads retire in order) and overlaps the row
+    // loads instead of following them.
+    // Positions outside [0, max_pos) break the precondition; clamp so the
     // table read stays inside the table.
-    const int64_t pos = min(max(a.positions[t], int64_t(0)), a.max_pos - 1);
-    const float mine = a.cos_sin[pos * kP + lane];
-    const float other = __shfl_xor(mine, 32, 64);
-    const float c = lo_half ? mine : other;          // cos(theta_{lane mod 32})
-    const float sn = lo_half ? -other : mine;        // -sin for the first half
-    for (uint32_t l0 = 0; l0 < a.layers; l0 += kMaxLayers) {
-      const int nl = min(kMaxLayers, int(a.layers - l0));
-      uint4 xv[kMaxLayers], gv[kMaxLayers];
-      uint32_t pe[kMaxLayers];
-      int64_t sl[kMaxLayers], cb[kMaxLayers];
-      float sc[kMaxLayers];
+    const int64_t pos_in = a.positions[t];
+    __builtin_amdgcn_sched_barrier(0);
+    uint4 xv[kChunks], gv[kChunks];
 #pragma unroll
-      for (int k = 0; k < kMaxLayers; ++k) {
-        if (k >= nl) break;
-        const uint32_t l = l0 + k;
-        const uint16_t* row = tok + int64_t(l) * a.kls;
-        xv[k] = ld16(row + lane * 8);
-        gv[k] = ld16(a.gamma + int64_t(l) * kR + lane * 8);
-        pe[k] = row[kR + lane];
-        sl[k] = a.slots[int64_t(l) * a.sls + t];
-        cb[k] = a.cache_ptrs[l];
-        if constexpr (kFp8) sc[k] = a.scales[l];
-      }
-#pragma unroll
-      for (int k = 0; k < kMaxLayers; ++k) {
-        if (k >= nl) break;
-        const uint32_t l = l0 + k;
-        // ---- RMSNorm: fp32 sum of squares over the wavefront
-        const uint32_t xw[4] = {xv[k].x, xv[k].y, xv[k].z, xv[k].w};
-        const uint32_t gw[4] = {gv[k].x, gv[k].y, gv[k].z, gv[k].w};
-        float x[8], g[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[2 * i] = bf16_lo(xw[i]);
-          x[2 * i + 1] = bf16_hi(xw[i]);
-          g[2 * i] = bf16_lo(gw[i]);
-          g[2 * i + 1] = bf16_hi(gw[i]);
-        }
-        float ss = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(x[i], x[i], ss);
-        ss = wave_sum(ss);
-        const float rinv = 1.0f / __builtin_sqrtf(ss * (1.0f / kR) + a.eps);
-        uint32_t yw[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          yw[i] = cvt_bf16x2(x[2 * i] * rinv * g[2 * i], x[2 * i + 1] * rinv * g[2 * i + 1]);
+    for (int q = 0; q < kChunks; ++q) {
+      xv[q] = ld16(row + 8 * (j + kRowLanes * q));
+      gv[q] = ld16(grow + 8 * (j + kRowLanes * q));
+    }
+    const uint2 pe = *reinterpret_cast<const uint2*>(row + kR + kPe * j);
+    const int64_t slot = a.slots[int64_t(l) * a.sls + t];
+    const int64_t cbase = a.cache_ptrs[l];
+    float sc = 1.0f;
+    if constexpr (kFp8) sc = a.scales[l];
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t pos = min(max(pos_in, int64_t(0)), a.max_pos - 1);
+    const float* cs = a.cos_sin + pos * kP + kPe * (j & 7);
+    const uint4 cv = ld16(cs);
+    const uint4 sv = ld16(cs + kP / 2);
+    // Keep every load of the row here, ahead of the first wait: without this
+    // fence the compiler sinks the loads used only by the stores into the
+    // store branch, after the reduction, adding memory round trips.
+    asm volatile("" ::: "memory");
 
-        // ---- RoPE: y_i = x_i cos - x_{i+32} sin, y_{i+32} = x_{i+32} cos + x_i sin
-        const float xp = bf16_lo(pe[k]);
-        const float xq = __shfl_xor(xp, 32, 64);
-        const uint32_t yp = cvt_bf16x2(xp * c + xq * sn, 0.0f) & 0xFFFFu;
-
-        if (a.dbg) {
-          uint16_t* d = a.dbg + (int64_t(l) * a.tokens + t) * (kR + kP);
-          st16(d + lane * 8, make_uint4(yw[0], yw[1], yw[2], yw[3]));
-          d[kR + lane] = static_cast<uint16_t>(yp);
-        }
-        // ---- insert (slot -> block, offset; a negative slot skips the row)
-        if (sl[k] < 0) continue;
-        const int64_t entry = entry_offset(sl[k], a);
-        if constexpr (kFp8) {
-          const float rc = 1.0f / sc[k];
-          const uint32_t flip = sign_flip_of(sc[k]);
-          uint8_t* dst = reinterpret_cast<uint8_t*>(cb[k]) + entry;
-          st8<kEpiStream>(dst + lane * 8,
-                          quant8<true>(make_uint4(yw[0], yw[1], yw[2], yw[3]), sc[k], rc, flip));
-          dst[kR + lane] = static_cast<uint8_t>(quant1(bf16_lo(yp), sc[k], rc, flip));
-        } else {
-          uint16_t* dst = reinterpret_cast<uint16_t*>(cb[k]) + entry;
-          st16<kEpiStream>(dst + lane * 8, make_uint4(yw[0], yw[1], yw[2], yw[3]));
-          dst[kR + lane] = static_cast<uint16_t>(yp);
-        }
+    // ---- RMSNorm: fp32 sum of squares over the row's 16 lanes
+    float x[8 * kChunks];
+#pragma unroll
+    for (int q = 0; q < kChunks; ++q) {
+      const uint32_t w[4] = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[8 * q + 2 * i] = bf16_lo(w[i]);
+        x[8 * q + 2 * i + 1] = bf16_hi(w[i]);
       }
+    }
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8 * kChunks; ++i) ss = __builtin_fmaf(x[i], x[i], ss);
+    ss = row_sum(ss);
+    const float rinv = 1.0f / __builtin_sqrtf(ss * (1.0f / kR) + a.eps);
+    uint4 y[kChunks];
+#pragma unroll
+    for (int q = 0; q < kChunks; ++q) {
+      const uint32_t gw[4] = {gv[q].x, gv[q].y, gv[q].z, gv[q].w};
+      uint32_t yw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        yw[i] = cvt_bf16x2(x[8 * q + 2 * i] * rinv * bf16_lo(gw[i]),
+                           x[8 * q + 2 * i + 1] * rinv * bf16_hi(gw[i]));
+      y[q] = make_uint4(yw[0], yw[1], yw[2], yw[3]);
+    }
+
+    // ---- RoPE: y_i = x_i cos - x_{i+32} sin, y_{i+32} = x_{i+32} cos + x_i sin
+    const float xp[kPe] = {bf16_lo(pe.x), bf16_hi(pe.x), bf16_lo(pe.y), bf16_hi(pe.y)};
+    const float cc[kPe] = {__uint_as_float(cv.x), __uint_as_float(cv.y), __uint_as_float(cv.z),
+                           __uint_as_float(cv.w)};
+    const float sn[kPe] = {__uint_as_float(sv.x), __uint_as_float(sv.y), __uint_as_float(sv.z),
+                           __uint_as_float(sv.w)};
+    float yp[kPe];
+#pragma unroll
+    for (int e = 0; e < kPe; ++e) {
+      const float xq = dpp_f<kDppRor8>(xp[e]);
+      yp[e] = xp[e] * cc[e] + xq * (first_half ? -sn[e] : sn[e]);
+    }
+    const uint2 ype = make_uint2(cvt_bf16x2(yp[0], yp[1]), cvt_bf16x2(yp[2], yp[3]));
+
+    if (!active) continue;
+    if (a.dbg) {
+      uint16_t* d = a.dbg + (int64_t(l) * a.tokens + t) * (kR + kP);
+#pragma unroll
+      for (int q = 0; q < kChunks; ++q) st16(d + 8 * (j + kRowLanes * q), y[q]);
+      *reinterpret_cast<uint2*>(d + kR + kPe * j) = ype;
+    }
+    // ---- insert (slot -> block, offset; a negative slot skips the row)
+    if (slot < 0) continue;
+    const int64_t entry = entry_offset(slot, a);
+    if constexpr (kFp8) {
+      const float rc = 1.0f / sc;
+      const uint32_t flip = sign_flip_of(sc);
+      uint8_t* dst = reinterpret_cast<uint8_t*>(cbase) + entry;
+#pragma unroll
+      for (int q = 0; q < kChunks; ++q)
+        st8<kEpiStream>(dst + 8 * (j + kRowLanes * q), quant8<true>(y[q], sc, rc, flip));
+      *reinterpret_cast<uint32_t*>(dst + kR + kPe * j) = quant4<true>(ype, sc, rc, flip);
+    } else {
+      uint16_t* dst = reinterpret_cast<uint16_t*>(cbase) + entry;
+#pragma unroll
+      for (int q = 0; q < kChunks; ++q) st16<kEpiStream>(dst + 8 * (j + kRowLanes * q), y[q]);
+      *reinterpret_cast<uint2*>(dst + kR + kPe * j) = ype;
     }
   }
 }
@@ -233,7 +272,7 @@ extern "C" int32_t mla_ctx_kv_epilogue(
     return fail(MLA_ERR_MISALIGNED, "%s: all_kv/gamma/cos_sin/dbg_rows addresses and all_kv "
                 "strides must be multiples of 16 bytes", fn);
   const int64_t rows = num_layers * num_tokens;
-  if (rows >= (int64_t(1) << 31) || block_size > 0x7FFFFFFF)
+  if (rows >= (int64_t(1) << 31) - kRowsPerBlock || block_size > 0x7FFFFFFF)
     return fail(MLA_ERR_UNSUPPORTED, "%s: too many rows for one launch", fn);
   EpiArgs a;
   a.all_kv = static_cast<const uint16_t*>(all_kv);
@@ -253,10 +292,11 @@ extern "C" int32_t mla_ctx_kv_epilogue(
   a.entry_stride = entry_stride;
   a.dbg = static_cast<uint16_t*>(dbg_rows);
   a.bsize = make_fastdiv(static_cast<uint32_t>(block_size));
+  a.nlayers = make_fastdiv(static_cast<uint32_t>(num_layers));
   a.layers = static_cast<uint32_t>(num_layers);
   a.tokens = static_cast<uint32_t>(num_tokens);
-  const int64_t blocks =
-      std::min<int64_t>(ceil_div(num_tokens, kWavesPerBlock), default_grid_cap());
+  a.rows = static_cast<uint32_t>(rows);
+  const int64_t blocks = std::min<int64_t>(ceil_div(rows, kRowsPerBlock), default_grid_cap());
   auto s = static_cast<hipStream_t>(stream);
   if (is_fp8(kv_cache_dtype))
     launch(epilogue_kernel<true>, dim3(blocks), dim3(256), 0, s, a);

@@ -165,6 +165,28 @@ __device__ __forceinline__ uint2 quant8(uint4 v, float s, float r, uint32_t sign
   return make_uint2(c0, c1);
 }
 
+// 4 bf16 (one uint2: element 2i in the low half of word i) -> 4 codes.
+template <bool kScaled>
+__device__ __forceinline__ uint32_t quant4(uint2 v, float s, float r, uint32_t sign_flip) {
+  const float f[4] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y)};
+  bool nan = false;
+  float q[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    nan |= f[i] != f[i];
+    q[i] = sat448(kScaled ? div_by_scale(f[i], s, r) : f[i]);
+  }
+  uint32_t c = cvt4_raw(q[0], q[1], q[2], q[3]);
+  const uint32_t sg = __builtin_amdgcn_perm(v.y, v.x, 0x07050301u) ^ sign_flip;
+  c = (c & 0x7F7F7F7Fu) | (sg & 0x80808080u);
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(nan) != 0, 0)) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (f[k] != f[k]) c = put_nan(c, f[k], k);
+  }
+  return c;
+}
+
 // 16 bf16 (two uint4) -> 16 codes (uint4).
 template <bool kScaled>
 __device__ __forceinline__ uint4 quant16(uint4 a, uint4 b, float s, float r, uint32_t flip) {
