@@ -154,7 +154,7 @@ __global__ __launch_bounds__(256) void epilogue_kernel(const EpiArgs a) {
     // Keep every load of the row here, ahead of the first wait: without this
     // fence the compiler sinks the loads used only by the stores into the
     // store branch, after the reduction, adding memory round trips.
-    asm volatile("" ::: "memory");
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
     // ---- RMSNorm: fp32 sum of squares over the row's 16 lanes
     float x[8 * kChunks];

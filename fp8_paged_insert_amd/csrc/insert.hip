@@ -8,12 +8,11 @@
 // (cache_kernels.cu: slot -> block / offset addressing, negative slot skips,
 // kv_c at element 0 and k_pe at element kv_lora_rank of the entry).
 //
-// gfx950 design (not the page's one-workgroup-per-(token, layer) grid): the
-// work is a flat list of 16-byte output chunks, chunk = (layer, token, j).
-// Consecutive lanes take consecutive chunks of one cache entry, so every
-// entry is read with coalesced 16/32-byte loads and written with 16-byte
-// stores, no lane idles on the 576-element width, and one capped grid walks
-// the list grid-stride for any token count.
+// gfx950 design (not the page's one-workgroup-per-(token, layer) grid): for
+// the MLA row (512 + 64) a row belongs to 16 lanes, so one wavefront moves 4
+// adjacent rows with 128-256-byte contiguous accesses per instruction and
+// issues all of a row's loads, slot included, before its stores; other row
+// shapes take a flat list of 16-byte output chunks, one per thread.
 #include "mla_common.hpp"
 
 namespace mla {
@@ -37,62 +36,142 @@ struct InsertArgs {
   uint32_t total;     // layers * tokens * chunks per row
 };
 
-// kFp8: 16 bf16 in -> 16 e4m3fn codes out per chunk; else 8 bf16 copied.
-// Each thread takes U chunks per pass (item, item + stride, ...): the slot,
-// cache-base and scale loads and the source loads of all U chunks are issued
-// before the first store, so the slot -> store dependence overlaps U times.
-template <bool kFp8, int U>
+// Any other row shape (kv_lora_rank and pe_dim multiples of 16): one thread
+// per 16-byte output chunk.  kFp8: 16 bf16 in -> 16 e4m3fn codes out per
+// chunk; else 8 bf16 copied.
+template <bool kFp8>
 __global__ __launch_bounds__(256) void grouped_insert_kernel(const InsertArgs a) {
   constexpr int E = kFp8 ? 16 : 8;
   const uint32_t stride = gridDim.x * blockDim.x;
-  for (uint32_t base = blockIdx.x * blockDim.x + threadIdx.x; base < a.total;
-       base += U * stride) {
-    int64_t s[U], col[U], cbase[U];
-    float sc[U];
-    uint4 v0[U], v1[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t item = base + u * stride;
-      if (item >= a.total) continue;
-      const uint32_t row = fdiv(item, a.per_row);
-      const uint32_t j = item - row * a.per_row.d;
-      const uint32_t l = fdiv(row, a.tokens);
-      const uint32_t t = row - l * a.tokens.d;
-      s[u] = a.slots[int64_t(l) * a.sls + t];
-      cbase[u] = a.cache_ptrs[l];
-      if constexpr (kFp8) sc[u] = a.scales[l];
-      const uint16_t* src;
-      if (j < a.chunks_r) {
-        col[u] = int64_t(j) * E;
-        src = a.kv_c + int64_t(l) * a.kv_ls + int64_t(t) * a.kv_ts + col[u];
-      } else {
-        const int64_t jj = int64_t(j - a.chunks_r) * E;
-        src = a.k_pe + int64_t(l) * a.pe_ls + int64_t(t) * a.pe_ts + jj;
-        col[u] = a.R + jj;
-      }
-      v0[u] = ld16(src);
-      if constexpr (kFp8) v1[u] = ld16(src + 8);
+  for (uint32_t item = blockIdx.x * blockDim.x + threadIdx.x; item < a.total; item += stride) {
+    const uint32_t row = fdiv(item, a.per_row);
+    const uint32_t j = item - row * a.per_row.d;
+    const uint32_t l = fdiv(row, a.tokens);
+    const uint32_t t = row - l * a.tokens.d;
+    const int64_t s = a.slots[int64_t(l) * a.sls + t];
+    const int64_t cbase = a.cache_ptrs[l];
+    float sc = 1.0f;
+    if constexpr (kFp8) sc = a.scales[l];
+    const uint16_t* src;
+    int64_t col;
+    if (j < a.chunks_r) {
+      col = int64_t(j) * E;
+      src = a.kv_c + int64_t(l) * a.kv_ls + int64_t(t) * a.kv_ts + col;
+    } else {
+      const int64_t jj = int64_t(j - a.chunks_r) * E;
+      src = a.k_pe + int64_t(l) * a.pe_ls + int64_t(t) * a.pe_ts + jj;
+      col = a.R + jj;
     }
+    const uint4 v0 = ld16(src);
+    uint4 v1 = v0;
+    if constexpr (kFp8) v1 = ld16(src + 8);
+    if (s < 0) continue;  // negative slot: skip
+    int64_t blk, off;
+    if (s < 0x80000000LL) {
+      const uint32_t b32 = fdiv(static_cast<uint32_t>(s), a.bsize);
+      blk = b32;
+      off = static_cast<uint32_t>(s) - b32 * a.bsize.d;
+    } else {
+      blk = s / a.block_size;
+      off = s - blk * a.block_size;
+    }
+    const int64_t dst_off = blk * a.block_stride + off * a.entry_stride + col;
+    if constexpr (kFp8) {
+      const float rc = 1.0f / sc;  // IEEE division: RN(1 / scale)
+      st16<kInsertStream>(reinterpret_cast<uint8_t*>(cbase) + dst_off,
+                          quant16<true>(v0, v1, sc, rc, sign_flip_of(sc)));
+    } else {
+      st16<kInsertStream>(reinterpret_cast<uint16_t*>(cbase) + dst_off, v0);
+    }
+  }
+}
+
+// Rows of the MLA shape (kv_lora_rank 512, pe_dim 64): a row belongs to
+// kLanes lanes, lane j moving kv_c chunks j, j + kLanes, ... (8 values each)
+// and k_pe[(64 / kLanes) j, (64 / kLanes) (j + 1)), so each load and store
+// instruction covers 128-256 contiguous bytes of a row.  A wavefront takes
+// 64 / kLanes adjacent rows and issues every load -- slot, cache base, scale
+// and sources -- before its first store.
+constexpr int kRowR = 512, kRowP = 64;
+
+struct RowInsertArgs {
+  const uint16_t* kv_c;
+  int64_t kv_ls, kv_ts;
+  const uint16_t* k_pe;
+  int64_t pe_ls, pe_ts;
+  const int64_t* cache_ptrs;
+  const float* scales;
+  const int64_t* slots;
+  int64_t sls;
+  int64_t block_size, block_stride, entry_stride;  // in cache elements
+  FastDiv tokens, bsize;
+  uint32_t rows;
+};
+
+template <bool kFp8, int kLanes>
+__global__ __launch_bounds__(256) void row_insert_kernel(const RowInsertArgs a) {
+  constexpr int kChunks = kRowR / 8 / kLanes;  // 16-byte kv_c chunks per lane
+  constexpr int kPe = kRowP / kLanes;          // k_pe values per lane (4 or 2)
+  constexpr int kRowsPerWave = 64 / kLanes;
+  static_assert(kPe == 4 || kPe == 2, "k_pe is moved as 4 or 2 values per lane");
+  const int lane = threadIdx.x & 63;
+  const int j = lane % kLanes;
+  const uint32_t wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  for (uint32_t r0 = wave * kRowsPerWave; r0 < a.rows; r0 += gridDim.x * 4 * kRowsPerWave) {
+    const uint32_t r = r0 + lane / kLanes;
+    const uint32_t rr = min(r, a.rows - 1);   // idle lanes load in bounds
+    const uint32_t l = fdiv(rr, a.tokens);
+    const uint32_t t = rr - l * a.tokens.d;
+    const int64_t s = a.slots[int64_t(l) * a.sls + t];
+    const int64_t cb = a.cache_ptrs[l];
+    float sc = 1.0f;
+    if constexpr (kFp8) sc = a.scales[l];
+    const uint16_t* src = a.kv_c + int64_t(l) * a.kv_ls + int64_t(t) * a.kv_ts;
+    uint4 v[kChunks];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (base + u * stride >= a.total || s[u] < 0) continue;  // negative slot: skip
-      int64_t blk, off;
-      if (s[u] < 0x80000000LL) {
-        const uint32_t b32 = fdiv(static_cast<uint32_t>(s[u]), a.bsize);
-        blk = b32;
-        off = static_cast<uint32_t>(s[u]) - b32 * a.bsize.d;
-      } else {
-        blk = s[u] / a.block_size;
-        off = s[u] - blk * a.block_size;
-      }
-      const int64_t dst_off = blk * a.block_stride + off * a.entry_stride + col[u];
-      if constexpr (kFp8) {
-        const float rc = 1.0f / sc[u];  // IEEE division: RN(1 / scale)
-        st16<kInsertStream>(reinterpret_cast<uint8_t*>(cbase[u]) + dst_off,
-                            quant16<true>(v0[u], v1[u], sc[u], rc, sign_flip_of(sc[u])));
-      } else {
-        st16<kInsertStream>(reinterpret_cast<uint16_t*>(cbase[u]) + dst_off, v0[u]);
-      }
+    for (int q = 0; q < kChunks; ++q) v[q] = ld16(src + 8 * (j + kLanes * q));
+    const uint16_t* pesrc = a.k_pe + int64_t(l) * a.pe_ls + int64_t(t) * a.pe_ts + kPe * j;
+    uint2 pe;
+    if constexpr (kPe == 4) {
+      pe = *reinterpret_cast<const uint2*>(pesrc);
+    } else {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(pesrc);
+      pe = make_uint2(w, w);
+    }
+    // Every load stays ahead of the slot test: without this fence the
+    // compiler waits for the slot and issues the source loads in the branch.
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (r >= a.rows || s < 0) continue;  // negative slot: skip
+    int64_t blk, off;
+    if (s < 0x80000000LL) {
+      const uint32_t b32 = fdiv(static_cast<uint32_t>(s), a.bsize);
+      blk = b32;
+      off = static_cast<uint32_t>(s) - b32 * a.bsize.d;
+    } else {
+      blk = s / a.block_size;
+      off = s - blk * a.block_size;
+    }
+    const int64_t entry = blk * a.block_stride + off * a.entry_stride;
+    if constexpr (kFp8) {
+      const float rc = 1.0f / sc;  // IEEE division: RN(1 / scale)
+      const uint32_t flip = sign_flip_of(sc);
+      uint8_t* dst = reinterpret_cast<uint8_t*>(cb) + entry;
+#pragma unroll
+      for (int q = 0; q < kChunks; ++q)
+        st8<kInsertStream>(dst + 8 * (j + kLanes * q), quant8<true>(v[q], sc, rc, flip));
+      const uint32_t c = quant4<true>(pe, sc, rc, flip);
+      if constexpr (kPe == 4)
+        *reinterpret_cast<uint32_t*>(dst + kRowR + 4 * j) = c;
+      else
+        *reinterpret_cast<uint16_t*>(dst + kRowR + 2 * j) = static_cast<uint16_t>(c);
+    } else {
+      uint16_t* dst = reinterpret_cast<uint16_t*>(cb) + entry;
+#pragma unroll
+      for (int q = 0; q < kChunks; ++q) st16<kInsertStream>(dst + 8 * (j + kLanes * q), v[q]);
+      if constexpr (kPe == 4)
+        *reinterpret_cast<uint2*>(dst + kRowR + 4 * j) = pe;
+      else
+        *reinterpret_cast<uint32_t*>(dst + kRowR + 2 * j) = pe.x;
     }
   }
 }
@@ -156,9 +235,9 @@ extern "C" int32_t mla_kv_insert_grouped(
     return fail(MLA_ERR_UNSUPPORTED, "%s: kv_lora_rank and pe_dim must be multiples of 16", fn);
   if (!kv_c || (pe_dim > 0 && !k_pe))
     return fail(MLA_ERR_INVALID_ARGUMENT, "%s: kv_c / k_pe must not be NULL", fn);
-  if (!aligned16(kv_c) || !aligned16(k_pe) || !bytes16(kv_c_layer_stride, 2) ||
-      !bytes16(kv_c_token_stride, 2) || !bytes16(k_pe_layer_stride, 2) ||
-      !bytes16(k_pe_token_stride, 2))
+  if (!aligned16(kv_c) || !bytes16(kv_c_layer_stride, 2) || !bytes16(kv_c_token_stride, 2) ||
+      (pe_dim > 0 && (!aligned16(k_pe) || !bytes16(k_pe_layer_stride, 2) ||
+                      !bytes16(k_pe_token_stride, 2))))
     return fail(MLA_ERR_MISALIGNED,
                 "%s: kv_c / k_pe addresses and strides must be multiples of 16 bytes", fn);
   const int64_t per_row = (kv_lora_rank + pe_dim) / E;
@@ -188,20 +267,39 @@ extern "C" int32_t mla_kv_insert_grouped(
   a.chunks_r = static_cast<uint32_t>(kv_lora_rank / E);
   a.total = static_cast<uint32_t>(total);
 
-#ifndef MLA_INSERT_UNROLL
-#define MLA_INSERT_UNROLL 1
-#endif
-  constexpr int U = MLA_INSERT_UNROLL;
-#ifndef MLA_INSERT_CAP
-#define MLA_INSERT_CAP 0
-#endif
-  const int64_t cap = MLA_INSERT_CAP > 0 ? MLA_INSERT_CAP * int64_t(cu_count())
-                                         : int64_t(0x7FFFFFFF);
-  const int64_t blocks = std::min<int64_t>(ceil_div(total, 256 * U), cap);
   auto s = static_cast<hipStream_t>(stream);
+  if (kv_lora_rank == kRowR && pe_dim == kRowP) {
+    // 16 lanes per row measured faster than 32 lanes, or than 16 lanes
+    // moving 2 or 4 rows each, on the 5 x 16384-row workload
+    constexpr int kLanes = 16;
+    RowInsertArgs b;
+    b.kv_c = a.kv_c;
+    b.kv_ls = a.kv_ls;
+    b.kv_ts = a.kv_ts;
+    b.k_pe = a.k_pe;
+    b.pe_ls = a.pe_ls;
+    b.pe_ts = a.pe_ts;
+    b.cache_ptrs = a.cache_ptrs;
+    b.scales = a.scales;
+    b.slots = a.slots;
+    b.sls = a.sls;
+    b.block_size = a.block_size;
+    b.block_stride = a.block_stride;
+    b.entry_stride = a.entry_stride;
+    b.tokens = a.tokens;
+    b.bsize = a.bsize;
+    b.rows = static_cast<uint32_t>(num_layers * num_tokens);
+    const int64_t blocks = ceil_div(num_layers * num_tokens, 4 * (64 / kLanes));
+    if (fp8)
+      launch((row_insert_kernel<true, kLanes>), dim3(blocks), dim3(256), 0, s, b);
+    else
+      launch((row_insert_kernel<false, kLanes>), dim3(blocks), dim3(256), 0, s, b);
+    return launch_status(fn);
+  }
+  const int64_t blocks = ceil_div(total, 256);
   if (fp8)
-    launch((grouped_insert_kernel<true, U>), dim3(blocks), dim3(256), 0, s, a);
+    launch(grouped_insert_kernel<true>, dim3(blocks), dim3(256), 0, s, a);
   else
-    launch((grouped_insert_kernel<false, U>), dim3(blocks), dim3(256), 0, s, a);
+    launch(grouped_insert_kernel<false>, dim3(blocks), dim3(256), 0, s, a);
   return launch_status(fn);
 }

@@ -119,9 +119,10 @@ int32_t mla_parse_kv_cache_dtype(const char* s, int32_t* out);
  * kv_cache_dtype an mla_kv_dtype_t.
  *
  * Alignment (MLA_ERR_MISALIGNED otherwise): kv_c and k_pe base addresses and
- * their strides (in bytes) multiples of 16; block_stride and entry_stride in
- * bytes multiples of 16.  kv_lora_rank and pe_dim must be multiples of 16
- * (MLA_ERR_UNSUPPORTED otherwise); entry_stride >= kv_lora_rank + pe_dim.
+ * their strides (in bytes) multiples of 16 (k_pe is not read, nor checked,
+ * when pe_dim is 0); block_stride and entry_stride in bytes multiples of 16.
+ * kv_lora_rank and pe_dim must be multiples of 16 (MLA_ERR_UNSUPPORTED
+ * otherwise); entry_stride >= kv_lora_rank + pe_dim.
  * Preconditions (not checked): each cache base is 16-byte aligned and holds
  * every slot used; the valid slots of one layer are distinct; layers' caches
  * do not overlap each other or the inputs.

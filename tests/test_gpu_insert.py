@@ -89,6 +89,25 @@ def test_grouped_test_shape(mk, shared, dtype):
         assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
 
 
+@pytest.mark.parametrize("R,P", [(256, 32), (128, 16), (512, 16), (512, 0)])
+@pytest.mark.parametrize("dtype", ["bfloat16", "fp8"])
+def test_other_row_shapes(mk, R, P, dtype):
+    """Row shapes other than 512 + 64 (any multiples of 16) take the flat
+    chunk kernel; 3 layers x 37 tokens, block 16, one skipped slot per layer."""
+    announce("other_row_shapes", R, P, dtype)
+    g = synth.gen(100 + R + P)
+    L, T, bs, nb = 3, 37, 16, 8
+    fp8 = dtype == "fp8"
+    fill = synth.random_bytes if fp8 else synth.random_bf16_bits
+    slots = torch.stack([synth.randperm(nb * bs, g)[:T] for _ in range(L)])
+    slots[:, 5] = -1
+    d = dict(kv_c=synth.bf16_normal((L, T, R), g), k_pe=synth.bf16_normal((L, T, P), g),
+             caches=[fill((nb, bs, R + P + 16), g) for _ in range(L)],
+             scales=torch.tensor([0.3, 1.7, -0.9], dtype=torch.float32) if fp8 else None,
+             slot_mapping=slots, num_layers=L, num_tokens=T, block_size=bs)
+    assert_same(run_gpu(mk, d, dtype), run_oracle(d, dtype))
+
+
 def test_invalid_scales_raise(mk):
     """Scales on the host, non-contiguous, wrong count or dtype are refused."""
     announce("invalid_scales")
