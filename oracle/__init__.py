@@ -26,6 +26,11 @@ CACHE_BF16 = 0
 CACHE_FP8_E4M3 = 1
 PACK_KEY_BF16 = 0
 PACK_KEY_V_FP8 = 1
+PACK_KEY_V_FP8_KPE_RAW = 2
+SRC_BF16 = 0
+SRC_FP16 = 1
+GATHER_BF16 = 0
+GATHER_FP8_RAW = 1
 
 OK = 0
 EINVAL = -1
@@ -91,9 +96,10 @@ def _load():
                                        _i64, _i64, _i64, _i64, _vp, _vp, _vp,
                                        _i64, _i64, _i64, _i64, _int, _vp]),
         "orc_gather": (_int, [_vp, _int, _f32, _i64, _i64, _i64, _vp, _i64, _i64,
-                              _vp]),
+                              _int, _vp]),
         "orc_pack": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _i64,
-                            _i64, _i64, _i64, _i64, _int, _f32, _f32, _vp, _vp]),
+                            _i64, _i64, _i64, _i64, _int, _int, _f32, _f32, _vp, _vp]),
+        "orc_f16_to_f32_n": (None, [_vp, _i64, _vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -306,33 +312,48 @@ def ctx_kv_epilogue(all_kv, gamma, eps, positions, slot_mapping, caches,
 
 
 # --------------------------------------------------------- gather / pack --
-def gather(cache, src_slots, scale=1.0, width=None) -> np.ndarray:
-    """Contiguous bf16 [T, width] rows read through src_slots (dequantised for fp8)."""
+def gather(cache, src_slots, scale=1.0, width=None, raw=False) -> np.ndarray:
+    """Contiguous [T, width] rows read through src_slots: bf16 (dequantised for
+    an fp8 cache) or, with raw=True (fp8 caches only), the e4m3fn codes."""
     dt = _cache_dtype_code(cache)
     it = cache.itemsize
     src_slots = np.ascontiguousarray(src_slots, np.int64)
     width = cache.shape[2] if width is None else width
-    out = np.empty((src_slots.shape[0], width), np.uint16)
+    out = np.empty((src_slots.shape[0], width), np.uint8 if raw else np.uint16)
     rc = _load().orc_gather(_ptr(cache), dt, float(scale), cache.shape[1],
                             cache.strides[0] // it, cache.strides[1] // it,
-                            _ptr(src_slots), src_slots.shape[0], width, _ptr(out))
+                            _ptr(src_slots), src_slots.shape[0], width,
+                            GATHER_FP8_RAW if raw else GATHER_BF16, _ptr(out))
     _check(rc, "gather")
     return out
 
 
-def pack(k_nope, k_pe, v=None, mode=PACK_KEY_BF16, k_scale=1.0, v_scale=1.0):
+def f16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """IEEE fp16 bit patterns -> float32 values (exact), via the oracle."""
+    _need(bits, np.uint16, "bits")
+    c = np.ascontiguousarray(bits)
+    out = np.empty(c.shape, np.float32)
+    _load().orc_f16_to_f32_n(_ptr(c), c.size, _ptr(out))
+    return out
+
+
+def pack(k_nope, k_pe, v=None, mode=PACK_KEY_BF16, k_scale=1.0, v_scale=1.0, fp16=False):
     """Full key [T, H, nope+rope] (+ fp8 V [T, H, vdim]) from strided inputs.
 
-    k_nope [T, H, nope] uint16 view (last dim contiguous), k_pe [T, rope]
-    uint16 view (last dim contiguous), v [T, H, vdim] uint16 view or None.
+    k_nope [T, H, nope] uint16 view (last dim contiguous); k_pe [T, rope]
+    uint16 view, or uint8 e4m3fn codes in PACK_KEY_V_FP8_KPE_RAW mode (last
+    dim contiguous); v [T, H, vdim] uint16 view or None.  fp16=True reads the
+    16-bit inputs as IEEE fp16 instead of bf16.
     """
     _need(k_nope, np.uint16, "k_nope")
-    _need(k_pe, np.uint16, "k_pe")
+    raw = mode == PACK_KEY_V_FP8_KPE_RAW
+    _need(k_pe, np.uint8 if raw else np.uint16, "k_pe")
     T, H, nope = k_nope.shape
     rope = k_pe.shape[-1]
-    if (k_nope.size and k_nope.strides[2] != 2) or (k_pe.size and k_pe.strides[-1] != 2):
+    esz = k_pe.itemsize
+    if (k_nope.size and k_nope.strides[2] != 2) or (k_pe.size and k_pe.strides[-1] != esz):
         raise ValueError("innermost dimensions must be contiguous")
-    kpe_ts = k_pe.strides[0] // 2
+    kpe_ts = k_pe.strides[0] // esz
     if mode == PACK_KEY_BF16:
         key = np.empty((T, H, nope + rope), np.uint16)
         vout = None
@@ -347,6 +368,7 @@ def pack(k_nope, k_pe, v=None, mode=PACK_KEY_BF16, k_scale=1.0, v_scale=1.0):
         vout = np.empty((T, H, vd), np.uint8)
     rc = _load().orc_pack(_ptr(k_nope), k_nope.strides[0] // 2, k_nope.strides[1] // 2,
                           _ptr(k_pe), kpe_ts, _ptr(v), vts, vhs, T, H, nope, rope, vd,
-                          mode, float(k_scale), float(v_scale), _ptr(key), _ptr(vout))
+                          mode, SRC_FP16 if fp16 else SRC_BF16, float(k_scale),
+                          float(v_scale), _ptr(key), _ptr(vout))
     _check(rc, "pack")
     return key, vout

@@ -138,9 +138,44 @@ uint8_t orc_e4m3_encode(double x) {
  * multiply).
  */
 uint8_t orc_quantize(uint16_t x_bf16, float scale) {
-  const float x = orc_bf16_to_f32(x_bf16);
+  return orc_quantize_f32(orc_bf16_to_f32(x_bf16), scale);
+}
+
+/* The same quantisation for a value already in fp32 (an fp16 source value,
+ * which converts to fp32 exactly). */
+uint8_t orc_quantize_f32(float x, float scale) {
   const float q = x / scale;
   return orc_e4m3_encode((double)q);
+}
+
+/*
+ * IEEE binary16 -> fp32, from the format's definition: sign bit, 5 exponent
+ * bits with bias 15, 10 fraction bits; exponent 0 is subnormal (m * 2^-24),
+ * exponent 31 is infinity (m = 0) or NaN.  Every value is exact in fp32.
+ * Used for the fp16 inputs of the fp8 pack ([P1] 评论区精华: the pack's
+ * bit-level tests cover bf16 and fp16 inputs).
+ */
+float orc_f16_to_f32(uint16_t h) {
+  const int sign = (h >> 15) & 1;
+  const int e = (h >> 10) & 0x1F;
+  const int m = h & 0x3FF;
+  double v;
+  if (e == 0) {
+    v = ldexp((double)m, -24);
+  } else if (e == 31) {
+    if (m != 0) {
+      const float nan = sign ? -NAN : NAN;
+      return nan;
+    }
+    v = INFINITY;
+  } else {
+    v = ldexp((double)(1024 + m), e - 25);
+  }
+  return (float)(sign ? -v : v);
+}
+
+void orc_f16_to_f32_n(const uint16_t* h, int64_t n, float* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_f16_to_f32(h[i]);
 }
 
 /* Dequantise: bf16(fl32(decode(code) * scale)), one fp32 multiply, then one
@@ -417,20 +452,24 @@ int orc_ctx_kv_epilogue(const uint16_t* all_kv, int64_t kv_layer_stride,
 int orc_gather(const void* cache, int cache_dtype, float cache_scale,
                int64_t block_size, int64_t block_stride, int64_t entry_stride,
                const int64_t* src_slots, int64_t num_tokens, int64_t width,
-               uint16_t* out) {
+               int out_kind, void* out) {
   if (num_tokens < 0 || width < 0 || block_size <= 0) return ORC_EINVAL;
+  if (cache_dtype != ORC_CACHE_FP8_E4M3 && cache_dtype != ORC_CACHE_BF16) return ORC_EINVAL;
+  if (out_kind != ORC_GATHER_BF16 && out_kind != ORC_GATHER_FP8_RAW) return ORC_EINVAL;
+  /* the raw output exists only for an fp8 cache: its codes, not dequantised */
+  if (out_kind == ORC_GATHER_FP8_RAW && cache_dtype != ORC_CACHE_FP8_E4M3) return ORC_EINVAL;
   for (int64_t j = 0; j < num_tokens; ++j) {
     const int64_t s = src_slots[j];
     if (s < 0) return ORC_EINVAL;
     const int64_t entry = (s / block_size) * block_stride + (s % block_size) * entry_stride;
     for (int64_t i = 0; i < width; ++i) {
-      if (cache_dtype == ORC_CACHE_FP8_E4M3)
-        out[j * width + i] =
+      if (out_kind == ORC_GATHER_FP8_RAW)
+        ((uint8_t*)out)[j * width + i] = ((const uint8_t*)cache)[entry + i];
+      else if (cache_dtype == ORC_CACHE_FP8_E4M3)
+        ((uint16_t*)out)[j * width + i] =
             orc_dequantize(((const uint8_t*)cache)[entry + i], cache_scale);
-      else if (cache_dtype == ORC_CACHE_BF16)
-        out[j * width + i] = ((const uint16_t*)cache)[entry + i];
       else
-        return ORC_EINVAL;
+        ((uint16_t*)out)[j * width + i] = ((const uint16_t*)cache)[entry + i];
     }
   }
   return ORC_OK;
@@ -444,40 +483,64 @@ int orc_gather(const void* cache, int cache_dtype, float cache_scale,
  *   key[t, h, nope:nope+rope]    = k_pe[t, :]      (same for every head h)
  *   v_out[t, h, :]               = v[t, h, :]      (fp8 mode only)
  * Outputs are contiguous [T, H, nope+rope] and [T, H, v_dim].
- * mode KEY_BF16: key is a bit copy in bf16, v is not used.
+ * mode KEY_BF16: key is a 16-bit copy in the source format, v is not used.
  * mode KEY_V_FP8: every element x of key and of v becomes
  *   encode(fl32(x) / scale) with k_scale for the key and v_scale for V.
+ * mode KEY_V_FP8_KPE_RAW: as KEY_V_FP8, but k_pe holds e4m3fn codes
+ *   (uint8, kpe_tok_stride in bytes) that are copied into the key unchanged.
+ * src_format: the 16-bit format of k_nope, v (and k_pe unless raw): bf16 or
+ *   IEEE fp16 ([P1] 评论区精华: bf16 and fp16 inputs are both tested).
  * Reading: the page's op takes no scale (a plain cast, bit-identical to
  * torch's e4m3fn cast), which is scale = 1.0.
  */
+/* One 16-bit source value as fp32 (bf16 or fp16 bits; both exact). */
+static float src_to_f32(uint16_t x, int src_format) {
+  return src_format == ORC_SRC_FP16 ? orc_f16_to_f32(x) : orc_bf16_to_f32(x);
+}
+
 int orc_pack(const uint16_t* k_nope, int64_t kn_tok_stride, int64_t kn_head_stride,
-             const uint16_t* k_pe, int64_t kpe_tok_stride,
+             const void* k_pe, int64_t kpe_tok_stride,
              const uint16_t* v, int64_t v_tok_stride, int64_t v_head_stride,
              int64_t num_tokens, int64_t num_heads, int64_t nope_dim,
-             int64_t rope_dim, int64_t v_dim, int mode, float k_scale,
-             float v_scale, void* key_out, uint8_t* v_out) {
+             int64_t rope_dim, int64_t v_dim, int mode, int src_format,
+             float k_scale, float v_scale, void* key_out, uint8_t* v_out) {
   if (num_tokens < 0 || num_heads < 0 || nope_dim < 0 || rope_dim < 0 || v_dim < 0)
     return ORC_EINVAL;
-  if (mode != ORC_PACK_KEY_BF16 && mode != ORC_PACK_KEY_V_FP8) return ORC_EINVAL;
+  if (mode != ORC_PACK_KEY_BF16 && mode != ORC_PACK_KEY_V_FP8 &&
+      mode != ORC_PACK_KEY_V_FP8_KPE_RAW)
+    return ORC_EINVAL;
+  if (src_format != ORC_SRC_BF16 && src_format != ORC_SRC_FP16) return ORC_EINVAL;
   const int64_t kw = nope_dim + rope_dim;
   for (int64_t t = 0; t < num_tokens; ++t) {
     for (int64_t h = 0; h < num_heads; ++h) {
       const int64_t ko = (t * num_heads + h) * kw;
       const uint16_t* kn = k_nope + t * kn_tok_stride + h * kn_head_stride;
-      const uint16_t* kp = k_pe + t * kpe_tok_stride;
       if (mode == ORC_PACK_KEY_BF16) {
+        /* a 16-bit copy: the key keeps the source format */
+        const uint16_t* kp = (const uint16_t*)k_pe + t * kpe_tok_stride;
         uint16_t* key = (uint16_t*)key_out + ko;
         for (int64_t i = 0; i < nope_dim; ++i) key[i] = kn[i];
         for (int64_t j = 0; j < rope_dim; ++j) key[nope_dim + j] = kp[j];
-      } else {
-        uint8_t* key = (uint8_t*)key_out + ko;
-        for (int64_t i = 0; i < nope_dim; ++i) key[i] = orc_quantize(kn[i], k_scale);
-        for (int64_t j = 0; j < rope_dim; ++j)
-          key[nope_dim + j] = orc_quantize(kp[j], k_scale);
-        const uint16_t* vs = v + t * v_tok_stride + h * v_head_stride;
-        uint8_t* vo = v_out + (t * num_heads + h) * v_dim;
-        for (int64_t i = 0; i < v_dim; ++i) vo[i] = orc_quantize(vs[i], v_scale);
+        continue;
       }
+      uint8_t* key = (uint8_t*)key_out + ko;
+      for (int64_t i = 0; i < nope_dim; ++i)
+        key[i] = orc_quantize_f32(src_to_f32(kn[i], src_format), k_scale);
+      if (mode == ORC_PACK_KEY_V_FP8_KPE_RAW) {
+        /* [P1] 关键源码片段 (fused_mla_kv_concat_quant_fp8): a k_pe that is
+         * already fp8 (the plain-fp8 gather does not dequantise) is copied
+         * into the key byte for byte. */
+        const uint8_t* kp = (const uint8_t*)k_pe + t * kpe_tok_stride;
+        for (int64_t j = 0; j < rope_dim; ++j) key[nope_dim + j] = kp[j];
+      } else {
+        const uint16_t* kp = (const uint16_t*)k_pe + t * kpe_tok_stride;
+        for (int64_t j = 0; j < rope_dim; ++j)
+          key[nope_dim + j] = orc_quantize_f32(src_to_f32(kp[j], src_format), k_scale);
+      }
+      const uint16_t* vs = v + t * v_tok_stride + h * v_head_stride;
+      uint8_t* vo = v_out + (t * num_heads + h) * v_dim;
+      for (int64_t i = 0; i < v_dim; ++i)
+        vo[i] = orc_quantize_f32(src_to_f32(vs[i], src_format), v_scale);
     }
   }
   return ORC_OK;

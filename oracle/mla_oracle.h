@@ -27,7 +27,9 @@ extern "C" {
 
 enum { ORC_OK = 0, ORC_EINVAL = -1, ORC_EDUPSLOT = -2 };
 enum { ORC_CACHE_BF16 = 0, ORC_CACHE_FP8_E4M3 = 1 };
-enum { ORC_PACK_KEY_BF16 = 0, ORC_PACK_KEY_V_FP8 = 1 };
+enum { ORC_PACK_KEY_BF16 = 0, ORC_PACK_KEY_V_FP8 = 1, ORC_PACK_KEY_V_FP8_KPE_RAW = 2 };
+enum { ORC_SRC_BF16 = 0, ORC_SRC_FP16 = 1 };          /* 16-bit source format of the pack */
+enum { ORC_GATHER_BF16 = 0, ORC_GATHER_FP8_RAW = 1 };  /* gather output */
 
 /* ---- number formats --------------------------------------------------- */
 float    orc_bf16_to_f32(uint16_t b);
@@ -35,6 +37,8 @@ uint16_t orc_f64_to_bf16(double x);
 double   orc_e4m3_decode(uint8_t code);
 uint8_t  orc_e4m3_encode(double x);
 uint8_t  orc_quantize(uint16_t x_bf16, float scale);
+float    orc_f16_to_f32(uint16_t h);
+uint8_t  orc_quantize_f32(float x, float scale);
 uint16_t orc_dequantize(uint8_t code, float scale);
 
 void orc_f64_to_bf16_n(const double* x, int64_t n, uint16_t* out);
@@ -42,6 +46,7 @@ void orc_e4m3_encode_f32_n(const float* x, int64_t n, uint8_t* out);
 void orc_e4m3_decode_n(const uint8_t* c, int64_t n, double* out);
 void orc_quantize_n(const uint16_t* x, int64_t n, float scale, uint8_t* out);
 void orc_dequantize_n(const uint8_t* c, int64_t n, float scale, uint16_t* out);
+void orc_f16_to_f32_n(const uint16_t* h, int64_t n, float* out);
 
 /* ---- insert ------------------------------------------------------------ */
 int orc_insert_single(const uint16_t* kv_c, int64_t kv_c_tok_stride,
@@ -89,14 +94,14 @@ int orc_ctx_kv_epilogue(const uint16_t* all_kv, int64_t kv_layer_stride,
 int orc_gather(const void* cache, int cache_dtype, float cache_scale,
                int64_t block_size, int64_t block_stride, int64_t entry_stride,
                const int64_t* src_slots, int64_t num_tokens, int64_t width,
-               uint16_t* out);
+               int out_kind, void* out);
 
 int orc_pack(const uint16_t* k_nope, int64_t kn_tok_stride, int64_t kn_head_stride,
-             const uint16_t* k_pe, int64_t kpe_tok_stride,
+             const void* k_pe, int64_t kpe_tok_stride,
              const uint16_t* v, int64_t v_tok_stride, int64_t v_head_stride,
              int64_t num_tokens, int64_t num_heads, int64_t nope_dim,
-             int64_t rope_dim, int64_t v_dim, int mode, float k_scale,
-             float v_scale, void* key_out, uint8_t* v_out);
+             int64_t rope_dim, int64_t v_dim, int mode, int src_format,
+             float k_scale, float v_scale, void* key_out, uint8_t* v_out);
 
 #ifdef __cplusplus
 }
