@@ -16,9 +16,11 @@ from ._binding import (  # noqa: F401
     MLA_KV_BF16,
     MLA_KV_FP8_E4M3,
     MLA_KV_FP8_E5M2,
+    MLA_KV_FP16,
     MLA_OK,
     MLA_PACK_KEY_BF16,
     MLA_PACK_KEY_V_FP8,
+    MLA_PACK_KEY_V_FP8_KPE_RAW,
     LIB_PATH,
     MlaError,
     cache_ptr_table,

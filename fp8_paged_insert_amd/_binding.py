@@ -27,9 +27,11 @@ MLA_KV_AUTO = 0
 MLA_KV_BF16 = 1
 MLA_KV_FP8_E4M3 = 2
 MLA_KV_FP8_E5M2 = 3
+MLA_KV_FP16 = 4
 
 MLA_PACK_KEY_BF16 = 0
 MLA_PACK_KEY_V_FP8 = 1
+MLA_PACK_KEY_V_FP8_KPE_RAW = 2
 
 # Every symbol include/mla_kv.h declares.
 EXPORTS = (
@@ -60,10 +62,10 @@ _SIGS = {
                                    _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i32, _vp,
                                    _vp]),
     "mla_ctx_kv_proj": (_i32, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp]),
-    "mla_ctx_latent_gather": (_i32, [_vp, _i32, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp,
-                                     _i64, _vp]),
+    "mla_ctx_latent_gather": (_i32, [_vp, _i32, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i32,
+                                     _vp, _i64, _vp]),
     "mla_ctx_kv_pack": (_i32, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _i64,
-                               _i64, _i64, _i32, _vp, _vp, _vp, _vp, _i64, _vp]),
+                               _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _vp]),
 }
 
 _lib = None
@@ -375,17 +377,29 @@ def mla_ctx_kv_proj(x, w_nk, y):
 
 def mla_ctx_latent_gather(cache, src_slots, out, cache_scale=None, kv_cache_dtype="fp8",
                           max_blocks=0):
-    """out[j, :] = dequant(cache row of src_slots[j]); cache [num_blocks, block_size, E]."""
+    """out[j, :] = cache row of src_slots[j]; cache [num_blocks, block_size, E].
+
+    A bf16 `out` receives bf16 rows (dequantised with cache_scale for an fp8
+    cache); a uint8 / float8_e4m3fn `out` receives an fp8 cache's codes as
+    they are (no cache_scale).
+    """
     _need(src_slots, (torch.int64,), "src_slots")
-    _need(out, (torch.bfloat16,), "out")
+    _need(out, (torch.bfloat16, torch.uint8, torch.float8_e4m3fn), "out")
+    raw = out.dtype != torch.bfloat16
     dt = _cache_dtype_code(kv_cache_dtype)
     if dt == MLA_KV_FP8_E4M3:
         _need(cache, (torch.uint8, torch.float8_e4m3fn), "cache")
-        if cache_scale is None:
-            raise RuntimeError("an fp8 cache needs cache_scale")
-        _check_scales(cache_scale, 1, cache, "cache_scale")
+        if raw:
+            if cache_scale is not None:
+                raise RuntimeError("the raw fp8 gather does not dequantise; pass no cache_scale")
+        else:
+            if cache_scale is None:
+                raise RuntimeError("an fp8 cache needs cache_scale")
+            _check_scales(cache_scale, 1, cache, "cache_scale")
     else:
         _need(cache, (torch.bfloat16,), "cache")
+        if raw:
+            raise RuntimeError("a raw fp8 gather needs an fp8 cache")
         if cache_scale is not None:
             raise RuntimeError("a bf16 cache takes no cache_scale")
     if cache.dim() != 3 or cache.stride(2) != 1:
@@ -399,17 +413,34 @@ def mla_ctx_latent_gather(cache, src_slots, out, cache_scale=None, kv_cache_dtyp
     _same_device(out, cache, "out", "cache")
     st = lib().mla_ctx_latent_gather(
         _ptr(cache), dt, _ptr(cache_scale), cache.shape[1], cache.stride(0), cache.stride(1),
-        _ptr(src_slots), T, out.shape[1], _ptr(out), int(max_blocks), _stream(cache))
+        _ptr(src_slots), T, out.shape[1], MLA_KV_FP8_E4M3 if raw else MLA_KV_BF16, _ptr(out),
+        int(max_blocks), _stream(cache))
     _check(st, "mla_ctx_latent_gather")
+
+
+_SRC_DTYPES = {torch.bfloat16: MLA_KV_BF16, torch.float16: MLA_KV_FP16}
+_FP8_VIEWS = (torch.uint8, torch.float8_e4m3fn)
 
 
 def mla_ctx_kv_pack(k_nope, k_pe, key_out, v=None, v_out=None, mode=MLA_PACK_KEY_BF16,
                     k_scale=None, v_scale=None, max_blocks=0):
-    """Contiguous full key [T, H, nope+rope] (+ fp8 V) from strided k_nope / k_pe / v."""
-    _need(k_nope, (torch.bfloat16,), "k_nope")
-    _need(k_pe, (torch.bfloat16,), "k_pe")
+    """Contiguous full key [T, H, nope+rope] (+ fp8 V) from strided k_nope / k_pe / v.
+
+    k_nope and v are bf16 or fp16.  k_pe has k_nope's dtype, or -- in the fp8
+    modes -- holds fp8 codes (uint8 / float8_e4m3fn, e.g. a view of a raw fp8
+    gather), which are copied into the key as they are.
+    """
+    _need(k_nope, tuple(_SRC_DTYPES), "k_nope")
+    src = _SRC_DTYPES[k_nope.dtype]
     if k_pe.dim() == 3:  # [T, 1, rope]
         k_pe = k_pe.reshape(k_pe.shape[0], k_pe.shape[-1])
+    kpe_raw = k_pe.dtype in _FP8_VIEWS
+    if mode == MLA_PACK_KEY_V_FP8 and kpe_raw:
+        mode = MLA_PACK_KEY_V_FP8_KPE_RAW
+    if mode == MLA_PACK_KEY_V_FP8_KPE_RAW:
+        _need(k_pe, _FP8_VIEWS, "k_pe")
+    else:
+        _need(k_pe, (k_nope.dtype,), "k_pe")
     T, H, nope = k_nope.shape
     rope = k_pe.shape[1]
     if (nope > 1 and k_nope.stride(2) != 1) or (rope > 1 and k_pe.stride(1) != 1):
@@ -422,13 +453,13 @@ def mla_ctx_kv_pack(k_nope, k_pe, key_out, v=None, v_out=None, mode=MLA_PACK_KEY
         raise RuntimeError(f"key_out must be contiguous [{T}, {H}, {nope + rope}]")
     vd = vts = vhs = 0
     if mode == MLA_PACK_KEY_BF16:
-        _need(key_out, (torch.bfloat16,), "key_out")
+        _need(key_out, (k_nope.dtype,), "key_out")
         if v is not None or v_out is not None or k_scale is not None or v_scale is not None:
-            raise RuntimeError("bf16 key mode takes no v, v_out or scales")
-    elif mode == MLA_PACK_KEY_V_FP8:
-        _need(key_out, (torch.uint8, torch.float8_e4m3fn), "key_out")
-        _need(v, (torch.bfloat16,), "v")
-        _need(v_out, (torch.uint8, torch.float8_e4m3fn), "v_out")
+            raise RuntimeError("the 16-bit key mode takes no v, v_out or scales")
+    elif mode in (MLA_PACK_KEY_V_FP8, MLA_PACK_KEY_V_FP8_KPE_RAW):
+        _need(key_out, _FP8_VIEWS, "key_out")
+        _need(v, (k_nope.dtype,), "v")
+        _need(v_out, _FP8_VIEWS, "v_out")
         if tuple(v.shape[:2]) != (T, H) or (v.shape[2] > 1 and v.stride(2) != 1):
             raise RuntimeError("v must be a [T, H, vdim] view with contiguous rows")
         vd, vts, vhs = v.shape[2], v.stride(0), v.stride(1)
@@ -443,6 +474,6 @@ def mla_ctx_kv_pack(k_nope, k_pe, key_out, v=None, v_out=None, mode=MLA_PACK_KEY
         raise RuntimeError(f"unknown pack mode {mode}")
     st = lib().mla_ctx_kv_pack(
         _ptr(k_nope), k_nope.stride(0), k_nope.stride(1), _ptr(k_pe), k_pe.stride(0), _ptr(v),
-        vts, vhs, T, H, nope, rope, vd, int(mode), _ptr(k_scale), _ptr(v_scale), _ptr(key_out),
-        _ptr(v_out), int(max_blocks), _stream(k_nope))
+        vts, vhs, T, H, nope, rope, vd, int(mode), src, _ptr(k_scale), _ptr(v_scale),
+        _ptr(key_out), _ptr(v_out), int(max_blocks), _stream(k_nope))
     _check(st, "mla_ctx_kv_pack")

@@ -26,22 +26,28 @@ struct GatherArgs {
   const uint8_t* cache;  // bytes
   const float* scale;
   const int64_t* slots;
-  uint16_t* out;
+  void* out;
   int64_t block_size, block_stride, entry_stride;  // cache elements
   int64_t width;                                    // output row length
   FastDiv per_row, bsize;
   uint32_t total;
 };
 
+// Gather kinds: a 16-bit row copy (bf16 cache), the dequantising fp8 gather
+// (16 codes in, 16 bf16 out per chunk) and the raw fp8 copy (16 codes).
+enum GatherKind { kGatherCopy16 = 0, kGatherDequant = 1, kGatherRaw8 = 2 };
+
 // Each thread takes U chunks per pass (item, item + stride, ...): the U slot
 // loads go out together, then the U cache-row loads, then the conversions,
 // so the slot -> row dependence is paid once per U chunks.
-template <bool kFp8, int U>
+template <int kKind, int U>
 __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
-  constexpr int E = kFp8 ? 16 : 8;  // elements per chunk
+  constexpr bool kFp8 = kKind != kGatherCopy16;      // cache holds 1-byte codes
+  constexpr int E = kFp8 ? 16 : 8;                   // cache elements per chunk
+  constexpr int kOutBytes = kKind == kGatherRaw8 ? 1 : 2;
   const uint32_t stride = gridDim.x * blockDim.x;
   float sc = 1.0f;
-  if constexpr (kFp8) sc = a.scale[0];
+  if constexpr (kKind == kGatherDequant) sc = a.scale[0];
   for (uint32_t base = blockIdx.x * blockDim.x + threadIdx.x; base < a.total;
        base += U * stride) {
     int64_t s[U];
@@ -74,8 +80,9 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (base + u * stride >= a.total) continue;
-      uint16_t* dst = a.out + int64_t(jj[u]) * a.width + int64_t(cc[u]) * E;
-      if constexpr (kFp8) {
+      uint8_t* dst = static_cast<uint8_t*>(a.out) +
+                     (int64_t(jj[u]) * a.width + int64_t(cc[u]) * E) * kOutBytes;
+      if constexpr (kKind == kGatherDequant) {
         const uint32_t w[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
         uint32_t o[8];
 #pragma unroll
@@ -101,7 +108,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
           o[2 * i + 1] = hi;
         }
         st16<kGatherStream>(dst, make_uint4(o[0], o[1], o[2], o[3]));
-        st16<kGatherStream>(dst + 8, make_uint4(o[4], o[5], o[6], o[7]));
+        st16<kGatherStream>(dst + 16, make_uint4(o[4], o[5], o[6], o[7]));
       } else {
         st16<kGatherStream>(dst, q[u]);
       }
@@ -155,7 +162,10 @@ __global__ __launch_bounds__(256) void pack_bf16_kernel(const PackArgs a) {
     st16<kPackStream>(key + int64_t(item) * E, ld16(key_src<E>(a, item)));
 }
 
-template <bool kScaled>
+// fp8 key and V.  kF16: the 16-bit inputs are IEEE fp16 (else bf16).
+// kKpeRaw: k_pe holds e4m3fn codes (a_pe_ts in bytes), copied into the key's
+// rope chunks unchanged.
+template <bool kScaled, bool kF16, bool kKpeRaw>
 __global__ __launch_bounds__(256) void pack_fp8_kernel(const PackArgs a) {
   constexpr int E = 16;
   float ks = 1.0f, vs = 1.0f;
@@ -169,10 +179,23 @@ __global__ __launch_bounds__(256) void pack_fp8_kernel(const PackArgs a) {
        item += gridDim.x * blockDim.x) {
     const uint16_t* src;
     uint8_t* dst;
+    bool raw = false;
     const bool is_key = item < a.key_total;
     if (is_key) {
-      src = key_src<E>(a, item);
       dst = static_cast<uint8_t*>(a.key_out) + int64_t(item) * E;
+      if constexpr (kKpeRaw) {
+        const uint32_t row = fdiv(item, a.key_per_row);
+        const uint32_t j = item - row * a.key_per_row.d;
+        const uint32_t t = fdiv(row, a.heads);
+        const uint32_t h = row - t * a.heads.d;
+        raw = j >= a.nope_chunks;
+        src = raw ? reinterpret_cast<const uint16_t*>(
+                        reinterpret_cast<const uint8_t*>(a.k_pe) + int64_t(t) * a.pe_ts +
+                        (j - a.nope_chunks) * E)
+                  : a.k_nope + int64_t(t) * a.kn_ts + int64_t(h) * a.kn_hs + j * E;
+      } else {
+        src = key_src<E>(a, item);
+      }
     } else {
       const uint32_t vi = item - a.key_total;
       const uint32_t row = fdiv(vi, a.v_per_row);
@@ -183,9 +206,13 @@ __global__ __launch_bounds__(256) void pack_fp8_kernel(const PackArgs a) {
       dst = a.v_out + int64_t(vi) * E;
     }
     const uint4 x0 = ld16(src);
+    if (kKpeRaw && raw) {
+      st16<kPackStream>(dst, x0);   // 16 codes, as they are
+      continue;
+    }
     const uint4 x1 = ld16(src + 8);
-    st16<kPackStream>(dst, quant16<kScaled>(x0, x1, is_key ? ks : vs, is_key ? kr : vr,
-                                            is_key ? kf : vf));
+    st16<kPackStream>(dst, quant16<kScaled, kF16>(x0, x1, is_key ? ks : vs, is_key ? kr : vr,
+                                                  is_key ? kf : vf));
   }
 }
 
@@ -193,6 +220,18 @@ __global__ __launch_bounds__(256) void pack_fp8_kernel(const PackArgs a) {
 #define MLA_GATHER_UNROLL 1
 #endif
 constexpr int kGatherUnroll = MLA_GATHER_UNROLL;
+
+template <bool kScaled>
+void launch_pack_fp8(bool f16, bool kpe_raw, dim3 g, dim3 b, hipStream_t s, const PackArgs& a) {
+  if (f16 && kpe_raw)
+    launch(pack_fp8_kernel<kScaled, true, true>, g, b, 0, s, a);
+  else if (f16)
+    launch(pack_fp8_kernel<kScaled, true, false>, g, b, 0, s, a);
+  else if (kpe_raw)
+    launch(pack_fp8_kernel<kScaled, false, true>, g, b, 0, s, a);
+  else
+    launch(pack_fp8_kernel<kScaled, false, false>, g, b, 0, s, a);
+}
 
 int64_t grid_for(int64_t total, int64_t max_blocks) {
   const int64_t cap = max_blocks > 0 ? max_blocks : default_grid_cap();
@@ -208,19 +247,28 @@ extern "C" int32_t mla_ctx_latent_gather(const void* cache, int32_t cache_dtype,
                                          const float* cache_scale, int64_t block_size,
                                          int64_t block_stride, int64_t entry_stride,
                                          const int64_t* src_slots, int64_t num_tokens,
-                                         int64_t width, void* out, int64_t max_blocks,
-                                         mla_stream_t stream) {
+                                         int64_t width, int32_t out_dtype, void* out,
+                                         int64_t max_blocks, mla_stream_t stream) {
   static const char* fn = "mla_ctx_latent_gather";
   clear_error();
   int32_t st;
+  const bool raw = out_dtype == MLA_KV_FP8_E4M3;
+  if (out_dtype != MLA_KV_BF16 && !raw)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: out_dtype must be bf16 or fp8_e4m3 (raw codes)",
+                fn);
   switch (cache_dtype) {
     case MLA_KV_AUTO:
     case MLA_KV_BF16:
+      if (raw)
+        return fail(MLA_ERR_INVALID_ARGUMENT, "%s: raw fp8 output needs an fp8 cache", fn);
       if (cache_scale)
         return fail(MLA_ERR_INVALID_ARGUMENT, "%s: a bf16 cache takes no cache_scale", fn);
       break;
     case MLA_KV_FP8_E4M3:
-      if (!cache_scale)
+      if (raw && cache_scale)
+        return fail(MLA_ERR_INVALID_ARGUMENT,
+                    "%s: the raw fp8 gather does not dequantise; pass no cache_scale", fn);
+      if (!raw && !cache_scale)
         return fail(MLA_ERR_INVALID_ARGUMENT, "%s: an fp8 cache needs cache_scale", fn);
       break;
     default:
@@ -254,7 +302,7 @@ extern "C" int32_t mla_ctx_latent_gather(const void* cache, int32_t cache_dtype,
   a.cache = static_cast<const uint8_t*>(cache);
   a.scale = cache_scale;
   a.slots = src_slots;
-  a.out = static_cast<uint16_t*>(out);
+  a.out = out;
   a.block_size = block_size;
   a.block_stride = block_stride;
   a.entry_stride = entry_stride;
@@ -264,10 +312,12 @@ extern "C" int32_t mla_ctx_latent_gather(const void* cache, int32_t cache_dtype,
   a.total = static_cast<uint32_t>(total);
   auto s = static_cast<hipStream_t>(stream);
   const int64_t blocks = grid_for(ceil_div(total, kGatherUnroll), max_blocks);
-  if (fp8)
-    launch((gather_kernel<true, kGatherUnroll>), dim3(blocks), dim3(256), 0, s, a);
+  if (raw)
+    launch((gather_kernel<kGatherRaw8, kGatherUnroll>), dim3(blocks), dim3(256), 0, s, a);
+  else if (fp8)
+    launch((gather_kernel<kGatherDequant, kGatherUnroll>), dim3(blocks), dim3(256), 0, s, a);
   else
-    launch((gather_kernel<false, kGatherUnroll>), dim3(blocks), dim3(256), 0, s, a);
+    launch((gather_kernel<kGatherCopy16, kGatherUnroll>), dim3(blocks), dim3(256), 0, s, a);
   return launch_status(fn);
 }
 
@@ -276,19 +326,25 @@ extern "C" int32_t mla_ctx_kv_pack(const void* k_nope, int64_t kn_tok_stride,
                                    int64_t kpe_tok_stride, const void* v,
                                    int64_t v_tok_stride, int64_t v_head_stride,
                                    int64_t num_tokens, int64_t num_heads, int64_t nope,
-                                   int64_t rope, int64_t vdim, int32_t mode,
+                                   int64_t rope, int64_t vdim, int32_t mode, int32_t src_dtype,
                                    const float* k_scale, const float* v_scale,
                                    void* key_out, void* v_out, int64_t max_blocks,
                                    mla_stream_t stream) {
   static const char* fn = "mla_ctx_kv_pack";
   clear_error();
-  if (mode != MLA_PACK_KEY_BF16 && mode != MLA_PACK_KEY_V_FP8)
+  if (mode != MLA_PACK_KEY_BF16 && mode != MLA_PACK_KEY_V_FP8 &&
+      mode != MLA_PACK_KEY_V_FP8_KPE_RAW)
     return fail(MLA_ERR_INVALID_ARGUMENT, "%s: unknown mode %d", fn, mode);
-  const bool fp8 = mode == MLA_PACK_KEY_V_FP8;
+  if (src_dtype != MLA_KV_BF16 && src_dtype != MLA_KV_FP16)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: src_dtype must be bf16 or fp16", fn);
+  const bool fp8 = mode != MLA_PACK_KEY_BF16;
+  const bool kpe_raw = mode == MLA_PACK_KEY_V_FP8_KPE_RAW;
+  const bool f16 = src_dtype == MLA_KV_FP16;
   if (num_tokens < 0 || num_heads < 0 || nope < 0 || rope < 0 || vdim < 0 || max_blocks < 0)
     return fail(MLA_ERR_INVALID_ARGUMENT, "%s: negative size", fn);
   if (!fp8 && (v || v_out || k_scale || v_scale))
-    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: bf16 key mode takes no v, v_out or scales", fn);
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: the 16-bit key mode takes no v, v_out or scales",
+                fn);
   if (num_tokens == 0 || num_heads == 0) return MLA_OK;
   if (nope + rope == 0)
     return fail(MLA_ERR_INVALID_ARGUMENT, "%s: empty key rows", fn);
@@ -298,7 +354,8 @@ extern "C" int32_t mla_ctx_kv_pack(const void* k_nope, int64_t kn_tok_stride,
     return fail(MLA_ERR_UNSUPPORTED, "%s: nope, rope and vdim must be multiples of 16", fn);
   if (!aligned16(k_nope) || !aligned16(k_pe) || !aligned16(key_out) || !aligned16(v) ||
       !aligned16(v_out) || !bytes16(kn_tok_stride, 2) || !bytes16(kn_head_stride, 2) ||
-      !bytes16(kpe_tok_stride, 2) || !bytes16(v_tok_stride, 2) || !bytes16(v_head_stride, 2))
+      !bytes16(kpe_tok_stride, kpe_raw ? 1 : 2) || !bytes16(v_tok_stride, 2) ||
+      !bytes16(v_head_stride, 2))
     return fail(MLA_ERR_MISALIGNED, "%s: addresses and strides must be multiples of 16 bytes",
                 fn);
   const int64_t E = fp8 ? 16 : 8;
@@ -331,11 +388,13 @@ extern "C" int32_t mla_ctx_kv_pack(const void* k_nope, int64_t kn_tok_stride,
   auto s = static_cast<hipStream_t>(stream);
   const int64_t full = ceil_div(total, 256);
   const int64_t blocks = max_blocks > 0 ? std::min(full, max_blocks) : full;
+  const bool scaled = k_scale || v_scale;
+  const dim3 g(blocks), b(256);
   if (!fp8)
-    launch(pack_bf16_kernel, dim3(blocks), dim3(256), 0, s, a);
-  else if (k_scale || v_scale)
-    launch(pack_fp8_kernel<true>, dim3(blocks), dim3(256), 0, s, a);
+    launch(pack_bf16_kernel, g, b, 0, s, a);
+  else if (scaled)
+    launch_pack_fp8<true>(f16, kpe_raw, g, b, s, a);
   else
-    launch(pack_fp8_kernel<false>, dim3(blocks), dim3(256), 0, s, a);
+    launch_pack_fp8<false>(f16, kpe_raw, g, b, s, a);
   return launch_status(fn);
 }

@@ -129,16 +129,26 @@ __device__ __forceinline__ uint32_t put_nan(uint32_t w, float x, int k) {
   return (w & ~(0xFFu << (8 * k))) | (code << (8 * k));
 }
 
-// 8 bf16 (one uint4: element 2i in the low half of word i) -> 8 codes.
+// IEEE fp16 halves of a word as fp32 (exact).
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w)));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+}
+
+// 8 16-bit values (one uint4: element 2i in the low half of word i) -> 8
+// codes.  kF16 reads them as IEEE fp16, else as bf16; both formats keep the
+// sign in bit 15, so the sign overwrite below serves both.
 // sign_flip is 0x80808080 when s < 0, else 0.
-template <bool kScaled>
+template <bool kScaled, bool kF16 = false>
 __device__ __forceinline__ uint2 quant8(uint4 v, float s, float r, uint32_t sign_flip) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
   float f[8], q[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    f[2 * i] = bf16_lo(w[i]);
-    f[2 * i + 1] = bf16_hi(w[i]);
+    f[2 * i] = kF16 ? f16_lo(w[i]) : bf16_lo(w[i]);
+    f[2 * i + 1] = kF16 ? f16_hi(w[i]) : bf16_hi(w[i]);
   }
   bool nan = false;
 #pragma unroll
@@ -148,7 +158,7 @@ __device__ __forceinline__ uint2 quant8(uint4 v, float s, float r, uint32_t sign
   }
   uint32_t c0 = cvt4_raw(q[0], q[1], q[2], q[3]);
   uint32_t c1 = cvt4_raw(q[4], q[5], q[6], q[7]);
-  // bf16 high bytes (bit 7 = sign) of elements 0-3 and 4-7
+  // high bytes (bit 7 = sign) of elements 0-3 and 4-7
   const uint32_t s0 = __builtin_amdgcn_perm(w[1], w[0], 0x07050301u) ^ sign_flip;
   const uint32_t s1 = __builtin_amdgcn_perm(w[3], w[2], 0x07050301u) ^ sign_flip;
   c0 = (c0 & 0x7F7F7F7Fu) | (s0 & 0x80808080u);
@@ -187,11 +197,11 @@ __device__ __forceinline__ uint32_t quant4(uint2 v, float s, float r, uint32_t s
   return c;
 }
 
-// 16 bf16 (two uint4) -> 16 codes (uint4).
-template <bool kScaled>
+// 16 16-bit values (two uint4) -> 16 codes (uint4).
+template <bool kScaled, bool kF16 = false>
 __device__ __forceinline__ uint4 quant16(uint4 a, uint4 b, float s, float r, uint32_t flip) {
-  const uint2 lo = quant8<kScaled>(a, s, r, flip);
-  const uint2 hi = quant8<kScaled>(b, s, r, flip);
+  const uint2 lo = quant8<kScaled, kF16>(a, s, r, flip);
+  const uint2 hi = quant8<kScaled, kF16>(b, s, r, flip);
   return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 

@@ -45,6 +45,14 @@ def bf16_normal(shape, g, device="cpu", std=1.0) -> torch.Tensor:
     return x.to(torch.bfloat16)
 
 
+def f16_normal(shape, g, device="cpu", std=1.0) -> torch.Tensor:
+    """N(0, std^2) rounded to IEEE fp16 (values beyond 65504 become inf)."""
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        x = x * std
+    return x.to(torch.float16)
+
+
 def f32_uniform(shape, lo, hi, g, device="cpu") -> torch.Tensor:
     u = torch.rand(shape, generator=g, device=device, dtype=torch.float32)
     return lo + (hi - lo) * u

@@ -6,7 +6,7 @@
  *   projection  mla_ctx_kv_proj        Y = X . W  (one KV-only GEMM for all layers)
  *   epilogue    mla_ctx_kv_epilogue    RMSNorm(kv_c) | RoPE(k_pe) -> fp8/bf16 -> paged caches
  *   insert      mla_kv_insert_grouped  [kv_c | k_pe] -> fp8/bf16 -> paged caches, all layers
- *   gather      mla_ctx_latent_gather  paged cache rows -> contiguous bf16 workspace
+ *   gather      mla_ctx_latent_gather  paged cache rows -> contiguous bf16 (or raw fp8) workspace
  *   pack        mla_ctx_kv_pack        [k_nope | k_pe] full key (+ fp8 V), contiguous
  *
  * Pages cited (title and section heading):
@@ -21,9 +21,9 @@
  *   - All work is enqueued on `stream` (a hipStream_t; NULL = the null
  *     stream) and is asynchronous; nothing synchronises inside the library.
  *   - Strides are in ELEMENTS of the array they describe.
- *   - bf16 arrays hold IEEE bfloat16; fp8 arrays hold OCP e4m3fn codes
- *     (bias 7, no infinity, NaN = 0x7F/0xFF, max 448) -- the
- *     torch.float8_e4m3fn format.
+ *   - bf16 arrays hold IEEE bfloat16, fp16 arrays IEEE binary16; fp8 arrays
+ *     hold OCP e4m3fn codes (bias 7, no infinity, NaN = 0x7F/0xFF, max 448)
+ *     -- the torch.float8_e4m3fn format.
  *   - Arguments are validated on the host before anything is enqueued; on
  *     any error nothing is launched, the status is returned and
  *     mla_last_error() describes it.  Values that live in device memory
@@ -58,14 +58,16 @@ typedef enum {
   MLA_KV_AUTO = 0,
   MLA_KV_BF16 = 1,
   MLA_KV_FP8_E4M3 = 2,
-  MLA_KV_FP8_E5M2 = 3
+  MLA_KV_FP8_E5M2 = 3,
+  MLA_KV_FP16 = 4   /* IEEE fp16: a source format of the pack, never a cache */
 } mla_kv_dtype_t;
 
 /* Output layout of the chunked-context pack ([P1] 关键源码片段,
  * fused_mla_kv_concat and fused_mla_kv_concat_quant_fp8). */
 typedef enum {
-  MLA_PACK_KEY_BF16 = 0,  /* bf16 full key only */
-  MLA_PACK_KEY_V_FP8 = 1  /* fp8 full key and fp8 V */
+  MLA_PACK_KEY_BF16 = 0,          /* 16-bit full key only, in the source format */
+  MLA_PACK_KEY_V_FP8 = 1,         /* fp8 full key and fp8 V */
+  MLA_PACK_KEY_V_FP8_KPE_RAW = 2  /* as KEY_V_FP8, k_pe given as fp8 codes, copied as is */
 } mla_pack_mode_t;
 
 /* Description of the last error on the calling thread ("" if none). */
@@ -200,47 +202,59 @@ int32_t mla_ctx_kv_proj(const void* X, int64_t x_row_stride, int64_t T,
 
 /* ------------------------------------------------------------------------
  * mla_ctx_latent_gather -- read one sequence's context rows out of a paged
- * latent cache into a contiguous bf16 workspace ([P1] 实现拆解 item 2:
- * _gather_context_latent before kv_b_proj; the plain-fp8 cache case must feed
- * a bf16 kv_b_proj, as the second commit's fix in 实现拆解 item 5 requires).
+ * latent cache into a contiguous workspace ([P1] 实现拆解 item 2:
+ * _gather_context_latent before kv_b_proj, dispatched on the cache dtype;
+ * 关键源码片段: with a plain fp8 cache the gather does not dequantise, and
+ * 实现拆解 item 5: a bf16 kv_b_proj must then still receive bf16).
  *   s = src_slots[j]; row = cache + (s / block_size) * block_stride
  *                               + (s % block_size) * entry_stride
- *   out[j, i] = bf16(fl32(e4m3fn(row[i])) * cache_scale[0])   (FP8_E4M3)
- *   out[j, i] = row[i]  bit for bit                            (AUTO/BF16)
- * cache       device, element type from cache_dtype.
- * cache_scale device fp32 [1] for FP8 (read at kernel time), NULL otherwise.
+ *   out_dtype BF16, fp8 cache:  out[j, i] = bf16(fl32(e4m3fn(row[i])) * cache_scale[0])
+ *   out_dtype BF16, bf16 cache: out[j, i] = row[i]  bit for bit
+ *   out_dtype FP8_E4M3 (fp8 cache only): out[j, i] = row[i]  code for code,
+ *                               no dequantisation (cache_scale must be NULL)
+ * cache       device, element type from cache_dtype (AUTO/BF16 or FP8_E4M3).
+ * cache_scale device fp32 [1] for the dequantising fp8 gather (read at kernel
+ *             time), NULL otherwise.
  * src_slots   device int64 [num_tokens]; every entry >= 0 and inside the cache
  *             (precondition).
- * out         device bf16 [num_tokens, width] contiguous; width must be a
- *             multiple of 16 and <= entry_stride.
+ * out         device [num_tokens, width] contiguous, bf16 or fp8 codes per
+ *             out_dtype; width must be a multiple of 16 and <= entry_stride.
  * max_blocks  grid cap (0 = library default); the kernel loops grid-stride.
  * ------------------------------------------------------------------------ */
 int32_t mla_ctx_latent_gather(const void* cache, int32_t cache_dtype,
                               const float* cache_scale, int64_t block_size,
                               int64_t block_stride, int64_t entry_stride,
                               const int64_t* src_slots, int64_t num_tokens,
-                              int64_t width, void* out, int64_t max_blocks,
-                              mla_stream_t stream);
+                              int64_t width, int32_t out_dtype, void* out,
+                              int64_t max_blocks, mla_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * mla_ctx_kv_pack -- build the contiguous full key [k_nope | k_pe] (and, in
- * fp8 mode, the contiguous fp8 V) of one context chunk in one launch, reading
- * k_nope / v straight from the strided kv_b_proj output and k_pe straight
- * from the gather workspace ([P1] 实现拆解 item 1, 关键源码片段
- * fused_mla_key_concat_kv_cache.py).
+ * fp8 modes, the contiguous fp8 V) of one context chunk in one launch,
+ * reading k_nope / v straight from the strided kv_b_proj output and k_pe
+ * straight from the gather workspace ([P1] 实现拆解 item 1, 关键源码片段
+ * fused_mla_key_concat_kv_cache.py, 评论区精华 on the tested input types).
  *   key[t, h, 0:nope]         = k_nope[t, h, :]
  *   key[t, h, nope:nope+rope] = k_pe[t, :]           (same for every head)
- *   v_out[t, h, :]            = v[t, h, :]            (KEY_V_FP8 only)
- * KEY_BF16:   key_out bf16 [T, H, nope+rope]; v, v_out, scales must be NULL.
+ *   v_out[t, h, :]            = v[t, h, :]            (fp8 modes only)
+ * src_dtype: MLA_KV_BF16 or MLA_KV_FP16, the format of k_nope, v and (unless
+ *   KPE_RAW) k_pe.
+ * KEY_BF16:   key_out [T, H, nope+rope] in the source format (a 16-bit copy);
+ *   v, v_out and the scales must be NULL.
  * KEY_V_FP8:  key_out and v_out fp8 [T, H, nope+rope] / [T, H, vdim]; each
  *   element x becomes e4m3fn(fl32(x) / scale), RNE, saturating at +-448;
  *   k_scale / v_scale are device fp32 [1] or NULL for 1.0 (a plain cast,
  *   bit-identical to torch's float8_e4m3fn cast -- the page's op has no scale).
- * k_nope  device bf16: [t, h, i] at t*kn_tok_stride + h*kn_head_stride + i
- * k_pe    device bf16: [t, j]    at t*kpe_tok_stride + j
- * v       device bf16: [t, h, i] at t*v_tok_stride + h*v_head_stride + i
- * nope, rope, vdim must be multiples of 16; pointers and strides 16-byte
- * aligned.  max_blocks caps the grid (0 = default); the kernel loops
+ * KEY_V_FP8_KPE_RAW: as KEY_V_FP8, except that k_pe holds e4m3fn codes (one
+ *   byte each; kpe_tok_stride in bytes), which are copied into the key
+ *   unchanged -- the page's KPE_FP8 branch for a plain fp8 cache.  The codes
+ *   keep the cache's scale, so this matches KEY_V_FP8 only when that scale
+ *   equals k_scale (the caller's choice; not checked).
+ * k_nope  device: [t, h, i] at t*kn_tok_stride + h*kn_head_stride + i
+ * k_pe    device: [t, j]    at t*kpe_tok_stride + j
+ * v       device: [t, h, i] at t*v_tok_stride + h*v_head_stride + i
+ * nope, rope, vdim must be multiples of 16; pointers and strides (in bytes)
+ * 16-byte aligned.  max_blocks caps the grid (0 = default); the kernel loops
  * grid-stride over T * H rows, so any T fits.
  * ------------------------------------------------------------------------ */
 int32_t mla_ctx_kv_pack(const void* k_nope, int64_t kn_tok_stride,
@@ -248,7 +262,7 @@ int32_t mla_ctx_kv_pack(const void* k_nope, int64_t kn_tok_stride,
                         int64_t kpe_tok_stride, const void* v,
                         int64_t v_tok_stride, int64_t v_head_stride,
                         int64_t num_tokens, int64_t num_heads, int64_t nope,
-                        int64_t rope, int64_t vdim, int32_t mode,
+                        int64_t rope, int64_t vdim, int32_t mode, int32_t src_dtype,
                         const float* k_scale, const float* v_scale,
                         void* key_out, void* v_out, int64_t max_blocks,
                         mla_stream_t stream);

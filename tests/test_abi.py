@@ -120,11 +120,11 @@ def test_epilogue_rejects_bad_arguments(mk, kw, status, msg):
 def pack_call(mk, **kw):
     a = dict(kn=P16, kn_ts=16384, kn_hs=256, kpe=P16, kpe_ts=576, v=P16, v_ts=16384,
              v_hs=256, T=8192, H=64, nope=128, rope=64, vdim=128, mode=mk.MLA_PACK_KEY_V_FP8,
-             ks=None, vs=None, key=P16, vo=P16, maxb=0)
+             src=mk.MLA_KV_BF16, ks=None, vs=None, key=P16, vo=P16, maxb=0)
     a.update(kw)
     return mk.lib().mla_ctx_kv_pack(
         a["kn"], a["kn_ts"], a["kn_hs"], a["kpe"], a["kpe_ts"], a["v"], a["v_ts"], a["v_hs"],
-        a["T"], a["H"], a["nope"], a["rope"], a["vdim"], a["mode"], a["ks"], a["vs"],
+        a["T"], a["H"], a["nope"], a["rope"], a["vdim"], a["mode"], a["src"], a["ks"], a["vs"],
         a["key"], a["vo"], a["maxb"], None)
 
 
@@ -137,6 +137,10 @@ def pack_call(mk, **kw):
     (dict(nope=120), 2, "multiples of 16"),
     (dict(kn_hs=257), 3, "multiples of 16 bytes"),
     (dict(vo=P_ODD), 3, "multiples of 16 bytes"),
+    (dict(src=2), 1, "src_dtype"),
+    (dict(src=0), 1, "src_dtype"),
+    (dict(mode=2, kpe_ts=577), 3, "multiples of 16 bytes"),
+    (dict(mode=1, kpe_ts=580), 3, "multiples of 16 bytes"),
 ])
 def test_pack_rejects_bad_arguments(mk, kw, status, msg):
     assert pack_call(mk, **kw) == status
@@ -146,15 +150,17 @@ def test_pack_rejects_bad_arguments(mk, kw, status, msg):
 def test_pack_zero_tokens_is_a_noop(mk):
     assert pack_call(mk, T=0) == mk.MLA_OK
     assert pack_call(mk, H=0) == mk.MLA_OK
+    assert pack_call(mk, T=0, mode=mk.MLA_PACK_KEY_V_FP8_KPE_RAW, src=mk.MLA_KV_FP16) == mk.MLA_OK
+
 
 
 def gather_call(mk, **kw):
     a = dict(cache=P16, dt=mk.MLA_KV_FP8_E4M3, scale=P16, bs=64, bstride=64 * 576,
-             estride=576, slots=P16, T=8192, width=576, out=P16, maxb=0)
+             estride=576, slots=P16, T=8192, width=576, odt=mk.MLA_KV_BF16, out=P16, maxb=0)
     a.update(kw)
     return mk.lib().mla_ctx_latent_gather(
         a["cache"], a["dt"], a["scale"], a["bs"], a["bstride"], a["estride"], a["slots"],
-        a["T"], a["width"], a["out"], a["maxb"], None)
+        a["T"], a["width"], a["odt"], a["out"], a["maxb"], None)
 
 
 @pytest.mark.parametrize("kw,status,msg", [
@@ -165,6 +171,9 @@ def gather_call(mk, **kw):
     (dict(width=40), 2, "multiple of 16"),
     (dict(out=None), 1, "NULL"),
     (dict(out=P_ODD), 3, "multiples of 16 bytes"),
+    (dict(odt=0), 1, "out_dtype"),
+    (dict(odt=2), 1, "does not dequantise"),
+    (dict(odt=2, scale=None, dt=1), 1, "needs an fp8 cache"),
 ])
 def test_gather_rejects_bad_arguments(mk, kw, status, msg):
     assert gather_call(mk, **kw) == status
