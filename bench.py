@@ -54,6 +54,17 @@ def pack_fp8_bytes(tokens, heads, nope=128, rope=64, vdim=128):
             + tokens * heads * (nope + rope) + tokens * heads * vdim)
 
 
+def gather_raw_bytes(tokens, width=W):
+    """Read one fp8 cache row and one slot per token; write the same codes."""
+    return tokens * width + tokens * 8 + tokens * width
+
+
+def pack_fp8_kpe_raw_bytes(tokens, heads, nope=128, rope=64, vdim=128):
+    """As the fp8 pack, with k_pe read as one byte per value."""
+    return (tokens * heads * (nope + vdim) * 2 + tokens * rope
+            + tokens * heads * (nope + rope) + tokens * heads * vdim)
+
+
 def pack_bf16_bytes(tokens, heads, nope=128, rope=64):
     return tokens * heads * nope * 2 + tokens * rope * 2 + tokens * heads * (nope + rope) * 2
 
@@ -270,44 +281,69 @@ def small_batch(torch, mk, dev):
             "bytes": insert_bytes(L, 4, valid_rows=15)}
 
 
+def kernel_us(torch, mk, fn, flush, reps=22, warm=3):
+    """Median duration of the one kernel fn launches, bracketed by events the
+    kernel itself records (mla_set_launch_events), after a cache flush."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()            # torch creates the events on first record
+    e1.record()
+    torch.cuda.synchronize()
+    times = []
+    for i in range(reps + warm):
+        flush_llc(torch, flush)
+        mk.set_launch_events(e0, e1)
+        fn()
+        e1.synchronize()
+        if i >= warm:
+            times.append(e0.elapsed_time(e1) * 1e3)
+    return statistics.median(times)
+
+
 def context_pack_component(torch, mk, dev, flush):
     from fp8_paged_insert_amd import synth
 
     d = synth.context_pack(dev)
     ws = torch.empty(8192, W, dtype=torch.bfloat16, device=dev)
+    ws8 = torch.empty(8192, W, dtype=torch.uint8, device=dev)
     sc = torch.tensor([0.5], device=dev)
     kvb = d["kvb"]
+    kvh = synth.f16_normal((8192, 64, 256), synth.gen(44, dev), dev)
     key8 = torch.empty(8192, 64, 192, dtype=torch.uint8, device=dev)
     v8 = torch.empty(8192, 64, 128, dtype=torch.uint8, device=dev)
     keyb = torch.empty(8192, 64, 192, dtype=torch.bfloat16, device=dev)
+    mk.mla_ctx_latent_gather(d["cache"], d["src_slots"], ws, sc, "fp8")
+    mk.mla_ctx_latent_gather(d["cache"], d["src_slots"], ws8, None, "fp8")
 
     def gather():
         mk.mla_ctx_latent_gather(d["cache"], d["src_slots"], ws, sc, "fp8")
 
+    def gather_raw():
+        mk.mla_ctx_latent_gather(d["cache"], d["src_slots"], ws8, None, "fp8")
+
     def pack8():
         mk.mla_ctx_kv_pack(kvb[..., :128], ws[:, 512:], key8, v=kvb[..., 128:], v_out=v8,
                            mode=mk.MLA_PACK_KEY_V_FP8)
+
+    def pack8_raw():
+        mk.mla_ctx_kv_pack(kvb[..., :128], ws8[:, 512:], key8, v=kvb[..., 128:], v_out=v8,
+                           mode=mk.MLA_PACK_KEY_V_FP8)
+
+    def pack8_f16():
+        mk.mla_ctx_kv_pack(kvh[..., :128], kvh[:, 0, 128:192], key8, v=kvh[..., 128:],
+                           v_out=v8, mode=mk.MLA_PACK_KEY_V_FP8)
 
     def packb():
         mk.mla_ctx_kv_pack(kvb[..., :128], ws[:, 512:], keyb)
 
     out = {"workload": "chunked-context pack, 8192 tokens x 64 heads"}
     for name, fn, nbytes in (("gather", gather, gather_bytes(8192)),
+                             ("gather_raw_fp8", gather_raw, gather_raw_bytes(8192)),
                              ("pack_fp8", pack8, pack_fp8_bytes(8192, 64)),
+                             ("pack_fp8_kpe_raw", pack8_raw, pack_fp8_kpe_raw_bytes(8192, 64)),
+                             ("pack_fp8_fp16_inputs", pack8_f16, pack_fp8_bytes(8192, 64)),
                              ("pack_bf16", packb, pack_bf16_bytes(8192, 64))):
-        # time only the kernel: events around fn, after a cache flush
-        times = []
-        for i in range(25):
-            flush_llc(torch, flush)
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            fn()
-            e1.record()
-            e1.synchronize()
-            if i >= 3:
-                times.append(e0.elapsed_time(e1) * 1e3)
-        us = statistics.median(times)
+        us = kernel_us(torch, mk, fn, flush)
         out[name] = {"us": round(us, 2), "bytes": nbytes, "GBps": round(nbytes / us / 1e3, 1),
                      "frac_of_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
     return out
@@ -326,18 +362,7 @@ def epilogue_component(torch, mk, dev, flush):
         mk.mla_ctx_kv_epilogue(d["all_kv"], d["gamma"], d["eps"], d["positions"], cs, ptrs,
                                d["slot_mapping"], 64, 64 * W, W, d["scales"], "fp8")
 
-    times = []
-    for i in range(25):
-        flush_llc(torch, flush)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        epi()
-        e1.record()
-        e1.synchronize()
-        if i >= 3:
-            times.append(e0.elapsed_time(e1) * 1e3)
-    us = statistics.median(times)
+    us = kernel_us(torch, mk, epi, flush)
     nb = epilogue_bytes(L, T)
     res = {"workload": "context-KV epilogue, 5 layers x 4096 tokens (norm+rope+fp8+scatter)",
            "us": round(us, 2), "bytes": nb, "GBps": round(nb / us / 1e3, 1),
@@ -345,7 +370,7 @@ def epilogue_component(torch, mk, dev, flush):
     return res
 
 
-def projection_component(torch, mk, dev):
+def projection_component(torch, mk, dev, flush):
     from fp8_paged_insert_amd import synth
 
     g = synth.gen(3, dev)
@@ -353,13 +378,27 @@ def projection_component(torch, mk, dev):
     w_nk = synth.bf16_normal((7168, L * W), g, dev, std=0.02).t().contiguous()
     y = torch.empty(4096, L * W, dtype=torch.bfloat16, device=dev)
     try:
-        us = time_kernel(torch, lambda: mk.mla_ctx_kv_proj(x, w_nk, y), reps=30)
+        us = kernel_us(torch, mk, lambda: mk.mla_ctx_kv_proj(x, w_nk, y), flush)
     except mk.MlaError as e:
         return {"workload": "context_kv_proj 4096x7168 . 7168x2880", "status": str(e)}
+    # the vendor library GEMM on the same operands, for context (torch.matmul
+    # -> hipBLASLt), timed with stream events around the call after the same flush
+    ref = []
+    for i in range(25):
+        flush_llc(torch, flush)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.matmul(x, w_nk.t())
+        e1.record()
+        e1.synchronize()
+        if i >= 3:
+            ref.append(e0.elapsed_time(e1) * 1e3)
     flops = 2 * 4096 * 7168 * L * W
     return {"workload": "context_kv_proj 4096x7168 . 7168x2880 (bf16 MFMA, fp32 acc)",
             "us": round(us, 2), "TFLOPs": round(flops / us / 1e6, 1),
-            "frac_of_peak": round(flops / us / 1e6 / 2500.0, 4)}
+            "frac_of_peak": round(flops / us / 1e6 / 2500.0, 4),
+            "torch_matmul_us_stream_events": round(statistics.median(ref), 2)}
 
 
 # ----------------------------------------------------------- CPU baseline --
@@ -489,7 +528,7 @@ def main():
         comps = {"small_batch_insert": small_batch(torch, mk, dev),
                  "context_pack": context_pack_component(torch, mk, dev, flush),
                  "context_epilogue": epilogue_component(torch, mk, dev, flush),
-                 "context_kv_proj": projection_component(torch, mk, dev)}
+                 "context_kv_proj": projection_component(torch, mk, dev, flush)}
         result["components"] = comps
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(torch)
