@@ -24,6 +24,7 @@ _LIB = os.path.join(_HERE, "libmla_oracle.so")
 
 CACHE_BF16 = 0
 CACHE_FP8_E4M3 = 1
+CACHE_FP8_E5M2 = 2
 PACK_KEY_BF16 = 0
 PACK_KEY_V_FP8 = 1
 PACK_KEY_V_FP8_KPE_RAW = 2
@@ -100,6 +101,12 @@ def _load():
         "orc_pack": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _i64,
                             _i64, _i64, _i64, _i64, _int, _int, _f32, _f32, _vp, _vp]),
         "orc_f16_to_f32_n": (None, [_vp, _i64, _vp]),
+        "orc_e5m2_decode": (_f64, [ctypes.c_uint8]),
+        "orc_e5m2_encode": (ctypes.c_uint8, [_f64]),
+        "orc_e5m2_encode_f32_n": (None, [_vp, _i64, _vp]),
+        "orc_e5m2_decode_n": (None, [_vp, _i64, _vp]),
+        "orc_quantize_e5m2_n": (None, [_vp, _i64, _f32, _vp]),
+        "orc_dequantize_e5m2_n": (None, [_vp, _i64, _f32, _vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -172,16 +179,53 @@ def dequantize(codes: np.ndarray, scale: float) -> np.ndarray:
     return out
 
 
+def e5m2_encode(x) -> np.ndarray:
+    """Saturating round-to-nearest-even float32 -> e5m2 codes."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, np.uint8)
+    _load().orc_e5m2_encode_f32_n(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def e5m2_decode(codes) -> np.ndarray:
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, np.float64)
+    _load().orc_e5m2_decode_n(_ptr(c), c.size, _ptr(out))
+    return out
+
+
+def quantize_e5m2(x_bf16: np.ndarray, scale: float) -> np.ndarray:
+    x = np.ascontiguousarray(x_bf16)
+    _need(x, np.uint16, "x_bf16")
+    out = np.empty(x.shape, np.uint8)
+    _load().orc_quantize_e5m2_n(_ptr(x), x.size, float(scale), _ptr(out))
+    return out
+
+
+def dequantize_e5m2(codes: np.ndarray, scale: float) -> np.ndarray:
+    c = np.ascontiguousarray(codes)
+    _need(c, np.uint8, "codes")
+    out = np.empty(c.shape, np.uint16)
+    _load().orc_dequantize_e5m2_n(_ptr(c), c.size, float(scale), _ptr(out))
+    return out
+
+
 # ----------------------------------------------------------------- insert --
-def _cache_dtype_code(cache: np.ndarray) -> int:
+def _cache_dtype_code(cache: np.ndarray, fp8_format="e4m3") -> int:
+    """uint16 arrays are bf16 caches; uint8 arrays hold fp8 codes of the
+    given format ("e4m3" = e4m3fn, "e5m2")."""
     if cache.dtype == np.uint16:
         return CACHE_BF16
     if cache.dtype == np.uint8:
-        return CACHE_FP8_E4M3
-    raise TypeError("cache must be uint16 (bf16) or uint8 (fp8 e4m3fn)")
+        if fp8_format == "e4m3":
+            return CACHE_FP8_E4M3
+        if fp8_format == "e5m2":
+            return CACHE_FP8_E5M2
+        raise ValueError(f"unknown fp8 format {fp8_format!r}")
+    raise TypeError("cache must be uint16 (bf16) or uint8 (fp8 codes)")
 
 
-def insert_single(kv_c, k_pe, slots, cache, scale=1.0):
+def insert_single(kv_c, k_pe, slots, cache, scale=1.0, fp8_format="e4m3"):
     """In-place single-layer concat-and-cache.
 
     kv_c [T, R] uint16, k_pe [T, P] uint16 (row strides taken from the arrays),
@@ -197,11 +241,11 @@ def insert_single(kv_c, k_pe, slots, cache, scale=1.0):
         _ptr(kv_c), kv_c.strides[0] // it_c, _ptr(k_pe), k_pe.strides[0] // it_c,
         _ptr(slots), slots.shape[0], kv_c.shape[1], k_pe.shape[1],
         _ptr(cache), cache.shape[1], cache.strides[0] // it, cache.strides[1] // it,
-        _cache_dtype_code(cache), float(scale))
+        _cache_dtype_code(cache, fp8_format), float(scale))
     _check(rc, "insert_single")
 
 
-def insert_grouped(kv_c, k_pe, slot_mapping, caches, scales=None):
+def insert_grouped(kv_c, k_pe, slot_mapping, caches, scales=None, fp8_format="e4m3"):
     """In-place grouped insert.
 
     kv_c [L, T, R] and k_pe [L, T, P] uint16 views with any strides;
@@ -219,10 +263,10 @@ def insert_grouped(kv_c, k_pe, slot_mapping, caches, scales=None):
     for c in caches:
         if c.dtype != c0.dtype or c.strides != c0.strides or c.shape[1] != c0.shape[1]:
             raise ValueError("caches must share dtype and layout")
-    dt = _cache_dtype_code(c0)
+    dt = _cache_dtype_code(c0, fp8_format)
     ptr_arr = (ctypes.c_void_p * max(L, 1))(*[c.ctypes.data for c in caches])
     sc = None
-    if dt == CACHE_FP8_E4M3:
+    if dt != CACHE_BF16:
         sc = np.ascontiguousarray(scales, dtype=np.float32)
     rc = _load().orc_insert_grouped(
         _ptr(kv_c), kv_c.strides[0] // 2, kv_c.strides[1] // 2,
@@ -271,7 +315,7 @@ def rope_row(x, pos, base=10000.0) -> np.ndarray:
 
 
 def ctx_kv_epilogue(all_kv, gamma, eps, positions, slot_mapping, caches,
-                    scales=None, rope_base=10000.0, kv_lora_rank=512):
+                    scales=None, rope_base=10000.0, kv_lora_rank=512, fp8_format="e4m3"):
     """Norm + RoPE of every (layer, token) row, then the grouped insert.
 
     all_kv: [T, L, R+P] uint16 view (any strides); gamma [L, R] uint16;
@@ -294,13 +338,13 @@ def ctx_kv_epilogue(all_kv, gamma, eps, positions, slot_mapping, caches,
     if caches is not None:
         c0 = caches[0]
         it = c0.itemsize
-        dt = _cache_dtype_code(c0)
+        dt = _cache_dtype_code(c0, fp8_format)
         ptr_arr = (ctypes.c_void_p * max(L, 1))(*[c.ctypes.data for c in caches])
         ptrs = ctypes.cast(ptr_arr, ctypes.c_void_p)
         bs, bstride, estride = c0.shape[1], c0.strides[0] // it, c0.strides[1] // it
         _need(slot_mapping, np.int64, "slot_mapping")
         sls = slot_mapping.strides[0] // 8
-        if dt == CACHE_FP8_E4M3:
+        if dt != CACHE_BF16:
             sc = np.ascontiguousarray(scales, dtype=np.float32)
     rc = _load().orc_ctx_kv_epilogue(
         _ptr(all_kv), all_kv.strides[1] // 2, all_kv.strides[0] // 2, _ptr(gamma),
@@ -312,10 +356,10 @@ def ctx_kv_epilogue(all_kv, gamma, eps, positions, slot_mapping, caches,
 
 
 # --------------------------------------------------------- gather / pack --
-def gather(cache, src_slots, scale=1.0, width=None, raw=False) -> np.ndarray:
+def gather(cache, src_slots, scale=1.0, width=None, raw=False, fp8_format="e4m3") -> np.ndarray:
     """Contiguous [T, width] rows read through src_slots: bf16 (dequantised for
-    an fp8 cache) or, with raw=True (fp8 caches only), the e4m3fn codes."""
-    dt = _cache_dtype_code(cache)
+    an fp8 cache) or, with raw=True (fp8 caches only), the codes as they are."""
+    dt = _cache_dtype_code(cache, fp8_format)
     it = cache.itemsize
     src_slots = np.ascontiguousarray(src_slots, np.int64)
     width = cache.shape[2] if width is None else width

@@ -187,6 +187,100 @@ uint16_t orc_dequantize(uint8_t code, float scale) {
   return orc_f64_to_bf16((double)p);
 }
 
+/*
+ * OCP FP8 e5m2 decode: 1 sign bit, 5 exponent bits with bias 15, 2 mantissa
+ * bits; exponent field 0 is subnormal (m * 2^-16); exponent field 31 is
+ * infinity (m = 0) or NaN (m != 0); the largest finite magnitude is code
+ * 0x7B = 57344.  The format behind torch.float8_e5m2 and the "fp8_e5m2"
+ * cache dtype of [P3] 实现拆解 item 3 (the kFp8E5M2 template instance).
+ */
+double orc_e5m2_decode(uint8_t code) {
+  const int s = code >> 7;
+  const int e = (code >> 2) & 0x1F;
+  const int m = code & 0x3;
+  double v;
+  if (e == 0x1F) {
+    if (m != 0) return s ? -NAN : NAN;
+    v = INFINITY;
+  } else if (e == 0) {
+    v = ldexp((double)m, -16);
+  } else {
+    v = ldexp((double)(4 + m), e - 17);
+  }
+  return s ? -v : v;
+}
+
+/*
+ * e5m2 encode, round to nearest with ties to even, saturating:
+ *   NaN -> 0x7F | sign;  |x| >= 57344 (Inf included) -> 0x7B | sign;
+ *   otherwise the finite code nearest |x|, ties to the even code.
+ * Reading: the pages only name scaled_convert for this dtype; the same
+ * saturating rule as for e4m3fn is taken (torch's own e5m2 cast rounds to
+ * infinity from 61440 up and agrees everywhere below).
+ */
+static double g_e5m2_values[0x7C];
+static int g_e5m2_values_ready = 0;
+
+uint8_t orc_e5m2_encode(double x) {
+  const uint8_t sign = signbit(x) ? 0x80u : 0u;
+  if (isnan(x)) return (uint8_t)(sign | 0x7Fu);
+  const double a = fabs(x);
+  if (a >= 57344.0) return (uint8_t)(sign | 0x7Bu);
+  if (!g_e5m2_values_ready) {
+    for (int c = 0; c <= 0x7B; ++c) g_e5m2_values[c] = orc_e5m2_decode((uint8_t)c);
+    g_e5m2_values_ready = 1;
+  }
+  int best = 0;
+  double best_d = fabs(a - g_e5m2_values[0]);
+  for (int c = 1; c <= 0x7B; ++c) {
+    const double d = fabs(a - g_e5m2_values[c]);
+    if (d < best_d || (d == best_d && (c & 1) == 0)) {
+      best = c;
+      best_d = d;
+    }
+  }
+  return (uint8_t)(sign | (uint8_t)best);
+}
+
+/* The e5m2 cache's quantisation and dequantisation: the same steps as the
+ * e4m3fn ones, with the e5m2 codec. */
+uint8_t orc_quantize_e5m2(uint16_t x_bf16, float scale) {
+  const float q = orc_bf16_to_f32(x_bf16) / scale;
+  return orc_e5m2_encode((double)q);
+}
+
+uint16_t orc_dequantize_e5m2(uint8_t code, float scale) {
+  const float d = (float)orc_e5m2_decode(code); /* exact */
+  const float p = d * scale;
+  return orc_f64_to_bf16((double)p);
+}
+
+void orc_e5m2_encode_f32_n(const float* x, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e5m2_encode((double)x[i]);
+}
+void orc_e5m2_decode_n(const uint8_t* c, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e5m2_decode(c[i]);
+}
+void orc_quantize_e5m2_n(const uint16_t* x, int64_t n, float scale, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_quantize_e5m2(x[i], scale);
+}
+void orc_dequantize_e5m2_n(const uint8_t* c, int64_t n, float scale, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_dequantize_e5m2(c[i], scale);
+}
+
+/* Quantise / dequantise for an fp8 cache dtype. */
+static uint8_t quantize_as(uint16_t x_bf16, float scale, int cache_dtype) {
+  return cache_dtype == ORC_CACHE_FP8_E5M2 ? orc_quantize_e5m2(x_bf16, scale)
+                                           : orc_quantize(x_bf16, scale);
+}
+static uint16_t dequantize_as(uint8_t code, float scale, int cache_dtype) {
+  return cache_dtype == ORC_CACHE_FP8_E5M2 ? orc_dequantize_e5m2(code, scale)
+                                           : orc_dequantize(code, scale);
+}
+static int is_fp8_cache(int cache_dtype) {
+  return cache_dtype == ORC_CACHE_FP8_E4M3 || cache_dtype == ORC_CACHE_FP8_E5M2;
+}
+
 void orc_f64_to_bf16_n(const double* x, int64_t n, uint16_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = orc_f64_to_bf16(x[i]);
 }
@@ -238,7 +332,8 @@ static int has_duplicate_slots(const int64_t* slots, int64_t n) {
  *   entry = block * block_stride + offset * entry_stride;
  *   cache[entry + i]                = conv(kv_c[t, i])  for i < kv_lora_rank
  *   cache[entry + kv_lora_rank + j] = conv(k_pe[t, j])  for j < pe_dim
- * conv is a raw 16-bit copy for the bf16/auto cache and orc_quantize for fp8.
+ * conv is a raw 16-bit copy for the bf16/auto cache, orc_quantize for the
+ * e4m3fn cache and orc_quantize_e5m2 for the e5m2 cache.
  * No other cache element is touched.
  */
 int orc_insert_single(const uint16_t* kv_c, int64_t kv_c_tok_stride,
@@ -249,8 +344,7 @@ int orc_insert_single(const uint16_t* kv_c, int64_t kv_c_tok_stride,
                       int64_t entry_stride, int cache_dtype, float scale) {
   if (num_tokens < 0 || kv_lora_rank < 0 || pe_dim < 0 || block_size <= 0)
     return ORC_EINVAL;
-  if (cache_dtype != ORC_CACHE_BF16 && cache_dtype != ORC_CACHE_FP8_E4M3)
-    return ORC_EINVAL;
+  if (cache_dtype != ORC_CACHE_BF16 && !is_fp8_cache(cache_dtype)) return ORC_EINVAL;
   if (has_duplicate_slots(slots, num_tokens)) return ORC_EDUPSLOT;
   for (int64_t t = 0; t < num_tokens; ++t) {
     const int64_t s = slots[t];
@@ -267,9 +361,9 @@ int orc_insert_single(const uint16_t* kv_c, int64_t kv_c_tok_stride,
     } else {
       uint8_t* dst = (uint8_t*)cache + entry;
       for (int64_t i = 0; i < kv_lora_rank; ++i)
-        dst[i] = orc_quantize(src_c[i], scale);
+        dst[i] = quantize_as(src_c[i], scale, cache_dtype);
       for (int64_t j = 0; j < pe_dim; ++j)
-        dst[kv_lora_rank + j] = orc_quantize(src_p[j], scale);
+        dst[kv_lora_rank + j] = quantize_as(src_p[j], scale, cache_dtype);
     }
   }
   return ORC_OK;
@@ -295,10 +389,9 @@ int orc_insert_grouped(const uint16_t* kv_c, int64_t kv_c_layer_stride,
                        int64_t block_size, int64_t block_stride,
                        int64_t entry_stride, int cache_dtype) {
   if (num_layers < 0) return ORC_EINVAL;
-  if (cache_dtype == ORC_CACHE_FP8_E4M3 && num_layers > 0 && !scales)
-    return ORC_EINVAL;
+  if (is_fp8_cache(cache_dtype) && num_layers > 0 && !scales) return ORC_EINVAL;
   for (int64_t l = 0; l < num_layers; ++l) {
-    const float sc = cache_dtype == ORC_CACHE_FP8_E4M3 ? scales[l] : 1.0f;
+    const float sc = is_fp8_cache(cache_dtype) ? scales[l] : 1.0f;
     const int rc = orc_insert_single(
         kv_c + l * kv_c_layer_stride, kv_c_tok_stride,
         k_pe + l * k_pe_layer_stride, k_pe_tok_stride,
@@ -454,10 +547,10 @@ int orc_gather(const void* cache, int cache_dtype, float cache_scale,
                const int64_t* src_slots, int64_t num_tokens, int64_t width,
                int out_kind, void* out) {
   if (num_tokens < 0 || width < 0 || block_size <= 0) return ORC_EINVAL;
-  if (cache_dtype != ORC_CACHE_FP8_E4M3 && cache_dtype != ORC_CACHE_BF16) return ORC_EINVAL;
+  if (!is_fp8_cache(cache_dtype) && cache_dtype != ORC_CACHE_BF16) return ORC_EINVAL;
   if (out_kind != ORC_GATHER_BF16 && out_kind != ORC_GATHER_FP8_RAW) return ORC_EINVAL;
   /* the raw output exists only for an fp8 cache: its codes, not dequantised */
-  if (out_kind == ORC_GATHER_FP8_RAW && cache_dtype != ORC_CACHE_FP8_E4M3) return ORC_EINVAL;
+  if (out_kind == ORC_GATHER_FP8_RAW && !is_fp8_cache(cache_dtype)) return ORC_EINVAL;
   for (int64_t j = 0; j < num_tokens; ++j) {
     const int64_t s = src_slots[j];
     if (s < 0) return ORC_EINVAL;
@@ -465,9 +558,9 @@ int orc_gather(const void* cache, int cache_dtype, float cache_scale,
     for (int64_t i = 0; i < width; ++i) {
       if (out_kind == ORC_GATHER_FP8_RAW)
         ((uint8_t*)out)[j * width + i] = ((const uint8_t*)cache)[entry + i];
-      else if (cache_dtype == ORC_CACHE_FP8_E4M3)
+      else if (is_fp8_cache(cache_dtype))
         ((uint16_t*)out)[j * width + i] =
-            orc_dequantize(((const uint8_t*)cache)[entry + i], cache_scale);
+            dequantize_as(((const uint8_t*)cache)[entry + i], cache_scale, cache_dtype);
       else
         ((uint16_t*)out)[j * width + i] = ((const uint16_t*)cache)[entry + i];
     }

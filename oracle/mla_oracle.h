@@ -26,7 +26,7 @@ extern "C" {
 #endif
 
 enum { ORC_OK = 0, ORC_EINVAL = -1, ORC_EDUPSLOT = -2 };
-enum { ORC_CACHE_BF16 = 0, ORC_CACHE_FP8_E4M3 = 1 };
+enum { ORC_CACHE_BF16 = 0, ORC_CACHE_FP8_E4M3 = 1, ORC_CACHE_FP8_E5M2 = 2 };
 enum { ORC_PACK_KEY_BF16 = 0, ORC_PACK_KEY_V_FP8 = 1, ORC_PACK_KEY_V_FP8_KPE_RAW = 2 };
 enum { ORC_SRC_BF16 = 0, ORC_SRC_FP16 = 1 };          /* 16-bit source format of the pack */
 enum { ORC_GATHER_BF16 = 0, ORC_GATHER_FP8_RAW = 1 };  /* gather output */
@@ -40,6 +40,10 @@ uint8_t  orc_quantize(uint16_t x_bf16, float scale);
 float    orc_f16_to_f32(uint16_t h);
 uint8_t  orc_quantize_f32(float x, float scale);
 uint16_t orc_dequantize(uint8_t code, float scale);
+double   orc_e5m2_decode(uint8_t code);
+uint8_t  orc_e5m2_encode(double x);
+uint8_t  orc_quantize_e5m2(uint16_t x_bf16, float scale);
+uint16_t orc_dequantize_e5m2(uint8_t code, float scale);
 
 void orc_f64_to_bf16_n(const double* x, int64_t n, uint16_t* out);
 void orc_e4m3_encode_f32_n(const float* x, int64_t n, uint8_t* out);
@@ -47,6 +51,10 @@ void orc_e4m3_decode_n(const uint8_t* c, int64_t n, double* out);
 void orc_quantize_n(const uint16_t* x, int64_t n, float scale, uint8_t* out);
 void orc_dequantize_n(const uint8_t* c, int64_t n, float scale, uint16_t* out);
 void orc_f16_to_f32_n(const uint16_t* h, int64_t n, float* out);
+void orc_e5m2_encode_f32_n(const float* x, int64_t n, uint8_t* out);
+void orc_e5m2_decode_n(const uint8_t* c, int64_t n, double* out);
+void orc_quantize_e5m2_n(const uint16_t* x, int64_t n, float scale, uint8_t* out);
+void orc_dequantize_e5m2_n(const uint8_t* c, int64_t n, float scale, uint16_t* out);
 
 /* ---- insert ------------------------------------------------------------ */
 int orc_insert_single(const uint16_t* kv_c, int64_t kv_c_tok_stride,
