@@ -177,7 +177,13 @@ def cache_ptr_table(caches, device=None) -> torch.Tensor:
     return torch.tensor([c.data_ptr() for c in caches], dtype=torch.int64).to(device)
 
 
-_FP8_CACHE_DTYPES = (torch.uint8, torch.float8_e4m3fn)
+# tensor dtypes that may hold each fp8 cache format's codes
+_FP8_TENSOR_DTYPES = {MLA_KV_FP8_E4M3: (torch.uint8, torch.float8_e4m3fn),
+                      MLA_KV_FP8_E5M2: (torch.uint8, torch.float8_e5m2)}
+
+
+def _is_fp8(dt) -> bool:
+    return dt in _FP8_TENSOR_DTYPES
 
 
 def _resolve_caches(kv_caches, L, dt, width, block_size, block_stride, entry_stride, ref):
@@ -194,7 +200,7 @@ def _resolve_caches(kv_caches, L, dt, width, block_size, block_stride, entry_str
     caches = list(kv_caches)
     if len(caches) != L:
         raise RuntimeError(f"expected {L} caches, got {len(caches)}")
-    want = _FP8_CACHE_DTYPES if dt == MLA_KV_FP8_E4M3 else (torch.bfloat16,)
+    want = _FP8_TENSOR_DTYPES.get(dt, (torch.bfloat16,))
     c0 = caches[0]
     for i, c in enumerate(caches):
         _need(c, want, f"cache {i} (for kv_cache_dtype code {dt})")
@@ -248,7 +254,7 @@ def _insert_args(kv_c, k_pe, kv_cache_ptrs, slot_mapping, block_size, block_stri
     dt = _cache_dtype_code(kv_cache_dtype)
     kv_cache_ptrs = _resolve_caches(kv_cache_ptrs, L, dt, R + P, block_size, block_stride,
                                     entry_stride, kv_c)
-    if dt == MLA_KV_FP8_E4M3:
+    if _is_fp8(dt):
         if kv_scales is None:
             raise RuntimeError("an fp8 cache needs kv_scales (one fp32 scale per layer)")
         _check_scales(kv_scales, L, kv_c)
@@ -341,7 +347,7 @@ def mla_ctx_kv_epilogue(all_kv, gamma, eps, positions, cos_sin, kv_cache_ptrs, s
     dt = _cache_dtype_code(kv_cache_dtype)
     kv_cache_ptrs = _resolve_caches(kv_cache_ptrs, L, dt, W, block_size, block_stride,
                                     entry_stride, all_kv)
-    if dt == MLA_KV_FP8_E4M3:
+    if _is_fp8(dt):
         if kv_scales is None:
             raise RuntimeError("an fp8 cache needs kv_scales (one fp32 scale per layer)")
         _check_scales(kv_scales, L, all_kv)
@@ -380,15 +386,15 @@ def mla_ctx_latent_gather(cache, src_slots, out, cache_scale=None, kv_cache_dtyp
     """out[j, :] = cache row of src_slots[j]; cache [num_blocks, block_size, E].
 
     A bf16 `out` receives bf16 rows (dequantised with cache_scale for an fp8
-    cache); a uint8 / float8_e4m3fn `out` receives an fp8 cache's codes as
-    they are (no cache_scale).
+    cache); a uint8 (or same-format float8) `out` receives an fp8 cache's
+    codes as they are (no cache_scale).
     """
     _need(src_slots, (torch.int64,), "src_slots")
-    _need(out, (torch.bfloat16, torch.uint8, torch.float8_e4m3fn), "out")
     raw = out.dtype != torch.bfloat16
     dt = _cache_dtype_code(kv_cache_dtype)
-    if dt == MLA_KV_FP8_E4M3:
-        _need(cache, (torch.uint8, torch.float8_e4m3fn), "cache")
+    if _is_fp8(dt):
+        _need(cache, _FP8_TENSOR_DTYPES[dt], "cache")
+        _need(out, (torch.bfloat16,) + _FP8_TENSOR_DTYPES[dt], "out")
         if raw:
             if cache_scale is not None:
                 raise RuntimeError("the raw fp8 gather does not dequantise; pass no cache_scale")
@@ -398,6 +404,7 @@ def mla_ctx_latent_gather(cache, src_slots, out, cache_scale=None, kv_cache_dtyp
             _check_scales(cache_scale, 1, cache, "cache_scale")
     else:
         _need(cache, (torch.bfloat16,), "cache")
+        _need(out, (torch.bfloat16, torch.uint8), "out")
         if raw:
             raise RuntimeError("a raw fp8 gather needs an fp8 cache")
         if cache_scale is not None:
@@ -413,7 +420,7 @@ def mla_ctx_latent_gather(cache, src_slots, out, cache_scale=None, kv_cache_dtyp
     _same_device(out, cache, "out", "cache")
     st = lib().mla_ctx_latent_gather(
         _ptr(cache), dt, _ptr(cache_scale), cache.shape[1], cache.stride(0), cache.stride(1),
-        _ptr(src_slots), T, out.shape[1], MLA_KV_FP8_E4M3 if raw else MLA_KV_BF16, _ptr(out),
+        _ptr(src_slots), T, out.shape[1], dt if raw else MLA_KV_BF16, _ptr(out),
         int(max_blocks), _stream(cache))
     _check(st, "mla_ctx_latent_gather")
 

@@ -111,8 +111,9 @@ __device__ __forceinline__ int64_t entry_offset(int64_t s, const EpiArgs& a) {
 
 // Rows are numbered token-major (row = t * L + l), the order of the
 // projection output, so the 4 rows of a wavefront are adjacent in memory.
-template <bool kFp8>
+template <int kFmt>
 __global__ __launch_bounds__(256) void epilogue_kernel(const EpiArgs a) {
+  constexpr bool kFp8 = kFmt != kFmtBf16, kE5M2 = kFmt == kFmtE5M2;
   const int lane = threadIdx.x & 63;
   const int j = lane & (kRowLanes - 1);       // lane within the row
   const int grp = lane / kRowLanes;           // row within the wavefront
@@ -214,8 +215,8 @@ __global__ __launch_bounds__(256) void epilogue_kernel(const EpiArgs a) {
       uint8_t* dst = reinterpret_cast<uint8_t*>(cbase) + entry;
 #pragma unroll
       for (int q = 0; q < kChunks; ++q)
-        st8<kEpiStream>(dst + 8 * (j + kRowLanes * q), quant8<true>(y[q], sc, rc, flip));
-      *reinterpret_cast<uint32_t*>(dst + kR + kPe * j) = quant4<true>(ype, sc, rc, flip);
+        st8<kEpiStream>(dst + 8 * (j + kRowLanes * q), quant8<true, false, kE5M2>(y[q], sc, rc, flip));
+      *reinterpret_cast<uint32_t*>(dst + kR + kPe * j) = quant4<true, kE5M2>(ype, sc, rc, flip);
     } else {
       uint16_t* dst = reinterpret_cast<uint16_t*>(cbase) + entry;
 #pragma unroll
@@ -298,9 +299,12 @@ extern "C" int32_t mla_ctx_kv_epilogue(
   a.rows = static_cast<uint32_t>(rows);
   const int64_t blocks = std::min<int64_t>(ceil_div(rows, kRowsPerBlock), default_grid_cap());
   auto s = static_cast<hipStream_t>(stream);
-  if (is_fp8(kv_cache_dtype))
-    launch(epilogue_kernel<true>, dim3(blocks), dim3(256), 0, s, a);
+  const int fmt = cache_fmt(kv_cache_dtype);
+  if (fmt == kFmtE5M2)
+    launch(epilogue_kernel<kFmtE5M2>, dim3(blocks), dim3(256), 0, s, a);
+  else if (fmt == kFmtE4M3)
+    launch(epilogue_kernel<kFmtE4M3>, dim3(blocks), dim3(256), 0, s, a);
   else
-    launch(epilogue_kernel<false>, dim3(blocks), dim3(256), 0, s, a);
+    launch(epilogue_kernel<kFmtBf16>, dim3(blocks), dim3(256), 0, s, a);
   return launch_status(fn);
 }

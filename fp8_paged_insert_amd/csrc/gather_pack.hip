@@ -34,8 +34,9 @@ struct GatherArgs {
 };
 
 // Gather kinds: a 16-bit row copy (bf16 cache), the dequantising fp8 gather
-// (16 codes in, 16 bf16 out per chunk) and the raw fp8 copy (16 codes).
-enum GatherKind { kGatherCopy16 = 0, kGatherDequant = 1, kGatherRaw8 = 2 };
+// from an e4m3fn or an e5m2 cache (16 codes in, 16 bf16 out per chunk) and
+// the raw fp8 copy (16 codes of either format).
+enum GatherKind { kGatherCopy16 = 0, kGatherDequant = 1, kGatherRaw8 = 2, kGatherDequantE5M2 = 3 };
 
 // Each thread takes U chunks per pass (item, item + stride, ...): the U slot
 // loads go out together, then the U cache-row loads, then the conversions,
@@ -45,9 +46,11 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
   constexpr bool kFp8 = kKind != kGatherCopy16;      // cache holds 1-byte codes
   constexpr int E = kFp8 ? 16 : 8;                   // cache elements per chunk
   constexpr int kOutBytes = kKind == kGatherRaw8 ? 1 : 2;
+  constexpr bool kDequant = kKind == kGatherDequant || kKind == kGatherDequantE5M2;
+  constexpr bool kE5M2 = kKind == kGatherDequantE5M2;
   const uint32_t stride = gridDim.x * blockDim.x;
   float sc = 1.0f;
-  if constexpr (kKind == kGatherDequant) sc = a.scale[0];
+  if constexpr (kDequant) sc = a.scale[0];
   for (uint32_t base = blockIdx.x * blockDim.x + threadIdx.x; base < a.total;
        base += U * stride) {
     int64_t s[U];
@@ -82,24 +85,26 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
       if (base + u * stride >= a.total) continue;
       uint8_t* dst = static_cast<uint8_t*>(a.out) +
                      (int64_t(jj[u]) * a.width + int64_t(cc[u]) * E) * kOutBytes;
-      if constexpr (kKind == kGatherDequant) {
+      if constexpr (kDequant) {
         const uint32_t w[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
         uint32_t o[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float f[4];
-          dec4_e4m3(w[i], f);
+          dec4_fp8<kE5M2>(w[i], f);
           // fl32(value * scale) rounded to bf16; the converter's NaN does not
           // keep the code's sign, so NaN codes are rebuilt (a rare branch).
           uint32_t lo = cvt_bf16x2(f[0] * sc, f[1] * sc);
           uint32_t hi = cvt_bf16x2(f[2] * sc, f[3] * sc);
-          const bool nan4 = (((w[i] & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u) != 0;
+          // NaN codes: magnitude byte 0x7F (e4m3fn) or 0x7D-0x7F (e5m2)
+          constexpr uint32_t kNanBias = kE5M2 ? 0x03030303u : 0x01010101u;
+          const bool nan4 = (((w[i] & 0x7F7F7F7Fu) + kNanBias) & 0x80808080u) != 0;
           if (__builtin_expect(__builtin_amdgcn_ballot_w64(nan4) != 0, 0)) {
             uint32_t b[4] = {lo & 0xFFFFu, lo >> 16, hi & 0xFFFFu, hi >> 16};
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
               const uint32_t code = (w[i] >> (8 * k)) & 0xFFu;
-              if ((code & 0x7Fu) == 0x7Fu) b[k] = 0x7FC0u | ((code & 0x80u) << 8);
+              if ((code & 0x7Fu) >= (kE5M2 ? 0x7Du : 0x7Fu)) b[k] = 0x7FC0u | ((code & 0x80u) << 8);
             }
             lo = b[0] | (b[1] << 16);
             hi = b[2] | (b[3] << 16);
@@ -252,10 +257,10 @@ extern "C" int32_t mla_ctx_latent_gather(const void* cache, int32_t cache_dtype,
   static const char* fn = "mla_ctx_latent_gather";
   clear_error();
   int32_t st;
-  const bool raw = out_dtype == MLA_KV_FP8_E4M3;
+  const bool raw = out_dtype == MLA_KV_FP8_E4M3 || out_dtype == MLA_KV_FP8_E5M2;
   if (out_dtype != MLA_KV_BF16 && !raw)
-    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: out_dtype must be bf16 or fp8_e4m3 (raw codes)",
-                fn);
+    return fail(MLA_ERR_INVALID_ARGUMENT,
+                "%s: out_dtype must be bf16, or the fp8 cache's own dtype (raw codes)", fn);
   switch (cache_dtype) {
     case MLA_KV_AUTO:
     case MLA_KV_BF16:
@@ -265,6 +270,10 @@ extern "C" int32_t mla_ctx_latent_gather(const void* cache, int32_t cache_dtype,
         return fail(MLA_ERR_INVALID_ARGUMENT, "%s: a bf16 cache takes no cache_scale", fn);
       break;
     case MLA_KV_FP8_E4M3:
+    case MLA_KV_FP8_E5M2:
+      if (raw && out_dtype != cache_dtype)
+        return fail(MLA_ERR_INVALID_ARGUMENT,
+                    "%s: raw codes keep the cache's format; out_dtype must equal cache_dtype", fn);
       if (raw && cache_scale)
         return fail(MLA_ERR_INVALID_ARGUMENT,
                     "%s: the raw fp8 gather does not dequantise; pass no cache_scale", fn);
@@ -314,6 +323,8 @@ extern "C" int32_t mla_ctx_latent_gather(const void* cache, int32_t cache_dtype,
   const int64_t blocks = grid_for(ceil_div(total, kGatherUnroll), max_blocks);
   if (raw)
     launch((gather_kernel<kGatherRaw8, kGatherUnroll>), dim3(blocks), dim3(256), 0, s, a);
+  else if (cache_dtype == MLA_KV_FP8_E5M2)
+    launch((gather_kernel<kGatherDequantE5M2, kGatherUnroll>), dim3(blocks), dim3(256), 0, s, a);
   else if (fp8)
     launch((gather_kernel<kGatherDequant, kGatherUnroll>), dim3(blocks), dim3(256), 0, s, a);
   else

@@ -37,10 +37,12 @@ struct InsertArgs {
 };
 
 // Any other row shape (kv_lora_rank and pe_dim multiples of 16): one thread
-// per 16-byte output chunk.  kFp8: 16 bf16 in -> 16 e4m3fn codes out per
+// per 16-byte output chunk.  kFmt (CacheFmt): fp8 caches take 16 bf16 in ->
+// 16 e4m3fn or e5m2 codes out per
 // chunk; else 8 bf16 copied.
-template <bool kFp8>
+template <int kFmt>
 __global__ __launch_bounds__(256) void grouped_insert_kernel(const InsertArgs a) {
+  constexpr bool kFp8 = kFmt != kFmtBf16, kE5M2 = kFmt == kFmtE5M2;
   constexpr int E = kFp8 ? 16 : 8;
   const uint32_t stride = gridDim.x * blockDim.x;
   for (uint32_t item = blockIdx.x * blockDim.x + threadIdx.x; item < a.total; item += stride) {
@@ -79,7 +81,7 @@ __global__ __launch_bounds__(256) void grouped_insert_kernel(const InsertArgs a)
     if constexpr (kFp8) {
       const float rc = 1.0f / sc;  // IEEE division: RN(1 / scale)
       st16<kInsertStream>(reinterpret_cast<uint8_t*>(cbase) + dst_off,
-                          quant16<true>(v0, v1, sc, rc, sign_flip_of(sc)));
+                          quant16<true, false, kE5M2>(v0, v1, sc, rc, sign_flip_of(sc)));
     } else {
       st16<kInsertStream>(reinterpret_cast<uint16_t*>(cbase) + dst_off, v0);
     }
@@ -108,8 +110,9 @@ struct RowInsertArgs {
   uint32_t rows;
 };
 
-template <bool kFp8, int kLanes>
+template <int kFmt, int kLanes>
 __global__ __launch_bounds__(256) void row_insert_kernel(const RowInsertArgs a) {
+  constexpr bool kFp8 = kFmt != kFmtBf16, kE5M2 = kFmt == kFmtE5M2;
   constexpr int kChunks = kRowR / 8 / kLanes;  // 16-byte kv_c chunks per lane
   constexpr int kPe = kRowP / kLanes;          // k_pe values per lane (4 or 2)
   constexpr int kRowsPerWave = 64 / kLanes;
@@ -158,8 +161,8 @@ __global__ __launch_bounds__(256) void row_insert_kernel(const RowInsertArgs a) 
       uint8_t* dst = reinterpret_cast<uint8_t*>(cb) + entry;
 #pragma unroll
       for (int q = 0; q < kChunks; ++q)
-        st8<kInsertStream>(dst + 8 * (j + kLanes * q), quant8<true>(v[q], sc, rc, flip));
-      const uint32_t c = quant4<true>(pe, sc, rc, flip);
+        st8<kInsertStream>(dst + 8 * (j + kLanes * q), quant8<true, false, kE5M2>(v[q], sc, rc, flip));
+      const uint32_t c = quant4<true, kE5M2>(pe, sc, rc, flip);
       if constexpr (kPe == 4)
         *reinterpret_cast<uint32_t*>(dst + kRowR + 4 * j) = c;
       else
@@ -230,6 +233,7 @@ extern "C" int32_t mla_kv_insert_grouped(
   if (st != MLA_OK) return st;
   if (num_layers == 0 || num_tokens == 0) return MLA_OK;
   const bool fp8 = is_fp8(kv_cache_dtype);
+  const int fmt = cache_fmt(kv_cache_dtype);
   const int64_t E = fp8 ? 16 : 8;
   if (kv_lora_rank % 16 != 0 || pe_dim % 16 != 0)
     return fail(MLA_ERR_UNSUPPORTED, "%s: kv_lora_rank and pe_dim must be multiples of 16", fn);
@@ -290,16 +294,20 @@ extern "C" int32_t mla_kv_insert_grouped(
     b.bsize = a.bsize;
     b.rows = static_cast<uint32_t>(num_layers * num_tokens);
     const int64_t blocks = ceil_div(num_layers * num_tokens, 4 * (64 / kLanes));
-    if (fp8)
-      launch((row_insert_kernel<true, kLanes>), dim3(blocks), dim3(256), 0, s, b);
+    if (fmt == kFmtE5M2)
+      launch((row_insert_kernel<kFmtE5M2, kLanes>), dim3(blocks), dim3(256), 0, s, b);
+    else if (fmt == kFmtE4M3)
+      launch((row_insert_kernel<kFmtE4M3, kLanes>), dim3(blocks), dim3(256), 0, s, b);
     else
-      launch((row_insert_kernel<false, kLanes>), dim3(blocks), dim3(256), 0, s, b);
+      launch((row_insert_kernel<kFmtBf16, kLanes>), dim3(blocks), dim3(256), 0, s, b);
     return launch_status(fn);
   }
   const int64_t blocks = ceil_div(total, 256);
-  if (fp8)
-    launch(grouped_insert_kernel<true>, dim3(blocks), dim3(256), 0, s, a);
+  if (fmt == kFmtE5M2)
+    launch(grouped_insert_kernel<kFmtE5M2>, dim3(blocks), dim3(256), 0, s, a);
+  else if (fmt == kFmtE4M3)
+    launch(grouped_insert_kernel<kFmtE4M3>, dim3(blocks), dim3(256), 0, s, a);
   else
-    launch(grouped_insert_kernel<false>, dim3(blocks), dim3(256), 0, s, a);
+    launch(grouped_insert_kernel<kFmtBf16>, dim3(blocks), dim3(256), 0, s, a);
   return launch_status(fn);
 }

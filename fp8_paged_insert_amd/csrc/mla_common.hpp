@@ -53,7 +53,14 @@ inline int64_t default_grid_cap() { return int64_t(cu_count()) * 16; }
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-inline bool is_fp8(int32_t dt) { return dt == MLA_KV_FP8_E4M3; }
+inline bool is_fp8(int32_t dt) { return dt == MLA_KV_FP8_E4M3 || dt == MLA_KV_FP8_E5M2; }
+
+// Element formats of a cache (and template parameter of the kernels that
+// write or read one).
+enum CacheFmt { kFmtBf16 = 0, kFmtE4M3 = 1, kFmtE5M2 = 2 };
+inline int cache_fmt(int32_t dt) {
+  return dt == MLA_KV_FP8_E4M3 ? kFmtE4M3 : dt == MLA_KV_FP8_E5M2 ? kFmtE5M2 : kFmtBf16;
+}
 
 // Checks the cache-dtype / scale pairing shared by the insert and epilogue
 // ([P3] "PR #55356 完整报告", 关键源码片段, cache_kernels.cu host checks).
@@ -88,22 +95,25 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 -> e4m3fn with a per-tensor dequantisation scale s:
-//   code = e4m3fn_RNE(fl32(x) / s), saturating at +-448, NaN -> 0x7F | sign.
+// bf16 (or fp16) -> fp8 with a per-tensor dequantisation scale s:
+//   code = fp8_RNE(fl32(x) / s), saturating at the format's largest finite
+//   value (e4m3fn: +-448; e5m2: +-57344), NaN -> 0x7F | sign (a NaN code in
+//   both formats).
 // Exactness argument, step by step:
 //  * quotient: r = RN(1/s) once; q0 = RN(x*r) is within one ulp of x/s, the
 //    remainder x - q0*s is exact under FMA, and q = RN(q0 + rem*r) is the
 //    correctly rounded x/s (Markstein; checked exhaustively on the CPU for
-//    every bf16 significand against every fp32 significand of s).  Where
-//    the step degenerates -- x = +-0 (the sum of signed zeros gives +0),
-//    x = +-Inf or an overflowing quotient (Inf - Inf gives NaN) -- only the
-//    sign of the final code can be wrong, and it is rewritten below.
-//  * saturation: v_med3 clamps to [-448, 448]; it also maps NaN onto a
-//    bound, which is what turns the degenerate Inf cases into +-448.
-//  * the packed converter rounds to nearest even in OCP e4m3fn.
+//    every bf16 and every fp16 significand against every fp32 significand of
+//    s).  Where the step degenerates -- x = +-0 (the sum of signed zeros
+//    gives +0), x = +-Inf or an overflowing quotient (Inf - Inf gives NaN) --
+//    only the sign of the final code can be wrong, and it is rewritten below.
+//  * saturation: v_med3 clamps to [-max, max]; it also maps NaN onto a
+//    bound, which is what turns the degenerate Inf cases into +-max.
+//  * the packed converters round to nearest even in OCP e4m3fn
+//    (v_cvt_pk_fp8_f32) and OCP e5m2 (v_cvt_pk_bf8_f32).
 //  * sign: every code's sign bit is set to sign(x) xor sign(s) (v_perm
-//    gathers the bf16 high bytes, v_bfi merges them) -- exact for all
-//    non-NaN inputs, including zeros, subnormal quotients and saturation.
+//    gathers the 16-bit values' high bytes, v_bfi merges them) -- exact for
+//    all non-NaN inputs, including zeros, subnormal quotients and saturation.
 //  * NaN inputs (rare; a branch no lane takes otherwise) get 0x7F | sign(x).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float div_by_scale(float x, float s, float r) {
@@ -112,14 +122,23 @@ __device__ __forceinline__ float div_by_scale(float x, float s, float r) {
   return __builtin_fmaf(e, r, q0);
 }
 
-__device__ __forceinline__ float sat448(float q) {
-  return __builtin_amdgcn_fmed3f(q, -448.0f, 448.0f);
+template <bool kE5M2>
+__device__ __forceinline__ float sat_fp8(float q) {
+  constexpr float kMax = kE5M2 ? 57344.0f : 448.0f;
+  return __builtin_amdgcn_fmed3f(q, -kMax, kMax);
 }
 
 // Codes of 4 clamped values (byte k = value k).
+template <bool kE5M2>
 __device__ __forceinline__ uint32_t cvt4_raw(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  int w;
+  if constexpr (kE5M2) {
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, w, true);
+  } else {
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  }
   return static_cast<uint32_t>(w);
 }
 
@@ -139,9 +158,10 @@ __device__ __forceinline__ float f16_hi(uint32_t w) {
 
 // 8 16-bit values (one uint4: element 2i in the low half of word i) -> 8
 // codes.  kF16 reads them as IEEE fp16, else as bf16; both formats keep the
-// sign in bit 15, so the sign overwrite below serves both.
+// sign in bit 15, so the sign overwrite below serves both.  kE5M2 selects
+// the e5m2 code format, else e4m3fn.
 // sign_flip is 0x80808080 when s < 0, else 0.
-template <bool kScaled, bool kF16 = false>
+template <bool kScaled, bool kF16 = false, bool kE5M2 = false>
 __device__ __forceinline__ uint2 quant8(uint4 v, float s, float r, uint32_t sign_flip) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
   float f[8], q[8];
@@ -154,10 +174,10 @@ __device__ __forceinline__ uint2 quant8(uint4 v, float s, float r, uint32_t sign
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     nan |= f[i] != f[i];
-    q[i] = sat448(kScaled ? div_by_scale(f[i], s, r) : f[i]);
+    q[i] = sat_fp8<kE5M2>(kScaled ? div_by_scale(f[i], s, r) : f[i]);
   }
-  uint32_t c0 = cvt4_raw(q[0], q[1], q[2], q[3]);
-  uint32_t c1 = cvt4_raw(q[4], q[5], q[6], q[7]);
+  uint32_t c0 = cvt4_raw<kE5M2>(q[0], q[1], q[2], q[3]);
+  uint32_t c1 = cvt4_raw<kE5M2>(q[4], q[5], q[6], q[7]);
   // high bytes (bit 7 = sign) of elements 0-3 and 4-7
   const uint32_t s0 = __builtin_amdgcn_perm(w[1], w[0], 0x07050301u) ^ sign_flip;
   const uint32_t s1 = __builtin_amdgcn_perm(w[3], w[2], 0x07050301u) ^ sign_flip;
@@ -176,7 +196,7 @@ __device__ __forceinline__ uint2 quant8(uint4 v, float s, float r, uint32_t sign
 }
 
 // 4 bf16 (one uint2: element 2i in the low half of word i) -> 4 codes.
-template <bool kScaled>
+template <bool kScaled, bool kE5M2 = false>
 __device__ __forceinline__ uint32_t quant4(uint2 v, float s, float r, uint32_t sign_flip) {
   const float f[4] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y)};
   bool nan = false;
@@ -184,9 +204,9 @@ __device__ __forceinline__ uint32_t quant4(uint2 v, float s, float r, uint32_t s
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     nan |= f[i] != f[i];
-    q[i] = sat448(kScaled ? div_by_scale(f[i], s, r) : f[i]);
+    q[i] = sat_fp8<kE5M2>(kScaled ? div_by_scale(f[i], s, r) : f[i]);
   }
-  uint32_t c = cvt4_raw(q[0], q[1], q[2], q[3]);
+  uint32_t c = cvt4_raw<kE5M2>(q[0], q[1], q[2], q[3]);
   const uint32_t sg = __builtin_amdgcn_perm(v.y, v.x, 0x07050301u) ^ sign_flip;
   c = (c & 0x7F7F7F7Fu) | (sg & 0x80808080u);
   if (__builtin_expect(__builtin_amdgcn_ballot_w64(nan) != 0, 0)) {
@@ -198,33 +218,35 @@ __device__ __forceinline__ uint32_t quant4(uint2 v, float s, float r, uint32_t s
 }
 
 // 16 16-bit values (two uint4) -> 16 codes (uint4).
-template <bool kScaled, bool kF16 = false>
+template <bool kScaled, bool kF16 = false, bool kE5M2 = false>
 __device__ __forceinline__ uint4 quant16(uint4 a, uint4 b, float s, float r, uint32_t flip) {
-  const uint2 lo = quant8<kScaled, kF16>(a, s, r, flip);
-  const uint2 hi = quant8<kScaled, kF16>(b, s, r, flip);
+  const uint2 lo = quant8<kScaled, kF16, kE5M2>(a, s, r, flip);
+  const uint2 hi = quant8<kScaled, kF16, kE5M2>(b, s, r, flip);
   return make_uint4(lo.x, lo.y, hi.x, hi.y);
-}
-
-// One bf16 value (as fp32) -> its code in the low byte.
-__device__ __forceinline__ uint32_t quant1(float x, float s, float r, uint32_t sign_flip) {
-  const float q = sat448(div_by_scale(x, s, r));
-  uint32_t c = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(q, q, 0, false)) & 0x7Fu;
-  c |= ((__float_as_uint(x) >> 24) ^ sign_flip) & 0x80u;
-  if (__builtin_expect(__builtin_amdgcn_ballot_w64(x != x) != 0, 0))
-    c = x != x ? 0x7Fu | ((__float_as_uint(x) >> 24) & 0x80u) : c;
-  return c;
 }
 
 __device__ __forceinline__ uint32_t sign_flip_of(float s) { return s < 0.0f ? 0x80808080u : 0u; }
 
-// Four e4m3fn codes (one word) -> four fp32 values (exact).
-__device__ __forceinline__ void dec4_e4m3(uint32_t w, float* out) {
-  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
-  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
-  out[0] = lo[0];
-  out[1] = lo[1];
-  out[2] = hi[0];
-  out[3] = hi[1];
+// Four fp8 codes (one word; e4m3fn, or e5m2 with kE5M2) -> four fp32 values
+// (exact; the NaN codes' sign is not kept -- callers rebuild those).
+template <bool kE5M2>
+__device__ __forceinline__ void dec4_fp8(uint32_t w, float* out) {
+  float2 lo, hi;
+  if constexpr (kE5M2) {
+    const auto a = __builtin_amdgcn_cvt_pk_f32_bf8(static_cast<int>(w), false);
+    const auto b = __builtin_amdgcn_cvt_pk_f32_bf8(static_cast<int>(w), true);
+    lo = make_float2(a[0], a[1]);
+    hi = make_float2(b[0], b[1]);
+  } else {
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
+    lo = make_float2(a[0], a[1]);
+    hi = make_float2(b[0], b[1]);
+  }
+  out[0] = lo.x;
+  out[1] = lo.y;
+  out[2] = hi.x;
+  out[3] = hi.y;
 }
 
 // Division of n < 2^31 by a fixed divisor d >= 1 with one high multiply:

@@ -62,16 +62,15 @@ int32_t check_cache_dtype(const char* fn, int32_t dt, const float* scales) {
                     "%s: a bf16 cache takes no kv_scales (pass NULL)", fn);
       return MLA_OK;
     case MLA_KV_FP8_E4M3:
+    case MLA_KV_FP8_E5M2:
       if (!scales)
         return fail(MLA_ERR_INVALID_ARGUMENT,
                     "%s: an fp8 cache needs kv_scales (one fp32 scale per layer)", fn);
       return MLA_OK;
-    case MLA_KV_FP8_E5M2:
-      return fail(MLA_ERR_UNSUPPORTED, "%s: fp8_e5m2 caches are not supported on gfx950", fn);
     default:
       return fail(MLA_ERR_INVALID_ARGUMENT,
-                  "%s: unknown KV cache dtype code %d (expected auto, bfloat16 or fp8_e4m3)",
-                  fn, dt);
+                  "%s: unknown KV cache dtype code %d (expected auto, bfloat16, fp8_e4m3 or "
+                  "fp8_e5m2)", fn, dt);
   }
 }
 
@@ -87,12 +86,10 @@ extern "C" int32_t mla_parse_kv_cache_dtype(const char* s, int32_t* out) {
   if (!strcmp(s, "auto")) { *out = MLA_KV_AUTO; return MLA_OK; }
   if (!strcmp(s, "bfloat16")) { *out = MLA_KV_BF16; return MLA_OK; }
   if (!strcmp(s, "fp8") || !strcmp(s, "fp8_e4m3")) { *out = MLA_KV_FP8_E4M3; return MLA_OK; }
-  if (!strcmp(s, "fp8_e5m2")) {
-    *out = MLA_KV_FP8_E5M2;
-    return mla::fail(MLA_ERR_UNSUPPORTED, "KV cache dtype fp8_e5m2 is not supported on gfx950");
-  }
+  if (!strcmp(s, "fp8_e5m2")) { *out = MLA_KV_FP8_E5M2; return MLA_OK; }
   return mla::fail(MLA_ERR_INVALID_ARGUMENT,
-                   "unknown KV cache dtype '%s' (expected auto, bfloat16, fp8 or fp8_e4m3)", s);
+                   "unknown KV cache dtype '%s' (expected auto, bfloat16, fp8, fp8_e4m3 or "
+                   "fp8_e5m2)", s);
 }
 
 extern "C" int32_t mla_set_launch_events(void* start_event, void* stop_event) {

@@ -52,8 +52,9 @@ typedef enum {
 
 /* KV cache element type.  [P3] 实现拆解 item 3 and 关键源码片段
  * (cache_kernels.cu host checks): "auto" and "bfloat16" store raw bf16,
- * "fp8" and "fp8_e4m3" store e4m3fn scaled per layer; "fp8_e5m2" is rejected
- * on ROCm by the page's host code, and is UNSUPPORTED here as well. */
+ * "fp8" and "fp8_e4m3" store e4m3fn scaled per layer, "fp8_e5m2" stores OCP
+ * e5m2 scaled per layer (the page's ROCm build refuses it; gfx950 converts
+ * e5m2 natively, so it is implemented here). */
 typedef enum {
   MLA_KV_AUTO = 0,
   MLA_KV_BF16 = 1,
@@ -86,8 +87,8 @@ const char* mla_version(void);
 int32_t mla_set_launch_events(void* start_event, void* stop_event);
 
 /* Parse a KV-cache dtype string into *out.  Accepts "auto", "bfloat16",
- * "fp8", "fp8_e4m3" (MLA_OK); "fp8_e5m2" gives MLA_ERR_UNSUPPORTED; anything
- * else MLA_ERR_INVALID_ARGUMENT.  Same whitelist as [P3] 关键源码片段
+ * "fp8", "fp8_e4m3", "fp8_e5m2" (MLA_OK); anything else
+ * MLA_ERR_INVALID_ARGUMENT.  Same whitelist as [P3] 关键源码片段
  * (_GROUPED_KV_CACHE_DTYPES and the host checks of cache_kernels.cu). */
 int32_t mla_parse_kv_cache_dtype(const char* s, int32_t* out);
 
@@ -104,7 +105,9 @@ int32_t mla_parse_kv_cache_dtype(const char* s, int32_t* out);
  *   conv(k_pe[l, t, 0:pe_dim]) at element kv_lora_rank.
  * conv is a raw 16-bit copy for AUTO/BF16 and, for FP8_E4M3,
  *   e4m3fn(fl32(x) / kv_scales[l]) rounded to nearest-even, saturating at
- *   +-448 (the quotient is the IEEE fp32 quotient).
+ *   +-448 (the quotient is the IEEE fp32 quotient); for FP8_E5M2 the same
+ *   with the e5m2 format, saturating at +-57344.  NaN gives code 0x7F | sign
+ *   in both formats.
  * Result: bit-identical to num_layers independent single-layer inserts
  * ([P3] 关键源码片段 test_cache.py).
  *
@@ -208,11 +211,14 @@ int32_t mla_ctx_kv_proj(const void* X, int64_t x_row_stride, int64_t T,
  * 实现拆解 item 5: a bf16 kv_b_proj must then still receive bf16).
  *   s = src_slots[j]; row = cache + (s / block_size) * block_stride
  *                               + (s % block_size) * entry_stride
- *   out_dtype BF16, fp8 cache:  out[j, i] = bf16(fl32(e4m3fn(row[i])) * cache_scale[0])
+ *   out_dtype BF16, fp8 cache:  out[j, i] = bf16(fl32(decode(row[i])) * cache_scale[0])
+ *                               (decode: e4m3fn or e5m2 per cache_dtype; NaN
+ *                               codes give the quiet NaN with their sign)
  *   out_dtype BF16, bf16 cache: out[j, i] = row[i]  bit for bit
- *   out_dtype FP8_E4M3 (fp8 cache only): out[j, i] = row[i]  code for code,
- *                               no dequantisation (cache_scale must be NULL)
- * cache       device, element type from cache_dtype (AUTO/BF16 or FP8_E4M3).
+ *   out_dtype = cache_dtype (FP8_E4M3 or FP8_E5M2): out[j, i] = row[i] code
+ *                               for code, no dequantisation (cache_scale NULL)
+ * cache       device, element type from cache_dtype (AUTO/BF16, FP8_E4M3 or
+ *             FP8_E5M2).
  * cache_scale device fp32 [1] for the dequantising fp8 gather (read at kernel
  *             time), NULL otherwise.
  * src_slots   device int64 [num_tokens]; every entry >= 0 and inside the cache

@@ -31,15 +31,13 @@ def test_version(mk):
     assert "gfx950" in mk.version()
 
 
-@pytest.mark.parametrize("s,code", [("auto", 0), ("bfloat16", 1), ("fp8", 2), ("fp8_e4m3", 2)])
+@pytest.mark.parametrize("s,code", [("auto", 0), ("bfloat16", 1), ("fp8", 2), ("fp8_e4m3", 2),
+                                    ("fp8_e5m2", 3)])
 def test_parse_dtype_accepts_whitelist(mk, s, code):
     assert mk.parse_kv_cache_dtype(s) == code
 
 
 def test_parse_dtype_rejects(mk):
-    with pytest.raises(mk.MlaError) as e:
-        mk.parse_kv_cache_dtype("fp8_e5m2")
-    assert e.value.status == mk.MLA_ERR_UNSUPPORTED
     with pytest.raises(mk.MlaError) as e:
         mk.parse_kv_cache_dtype("int8")
     assert e.value.status == mk.MLA_ERR_INVALID_ARGUMENT
@@ -63,7 +61,7 @@ def insert_call(mk, **kw):
 
 
 @pytest.mark.parametrize("kw,status,msg", [
-    (dict(dt=3), 2, "fp8_e5m2"),
+    (dict(dt=3, scales=None), 1, "needs kv_scales"),
     (dict(dt=9), 1, "unknown KV cache dtype"),
     (dict(scales=None), 1, "needs kv_scales"),
     (dict(dt=0), 1, "takes no kv_scales"),
@@ -103,7 +101,7 @@ def epilogue_call(mk, **kw):
 
 
 @pytest.mark.parametrize("kw,status,msg", [
-    (dict(dt=3), 2, "fp8_e5m2"),
+    (dict(dt=3, scales=None), 1, "needs kv_scales"),
     (dict(scales=None), 1, "needs kv_scales"),
     (dict(R=256, estride=320, bstride=64 * 320), 2, "kv_lora_rank 512"),
     (dict(gamma=None), 1, "NULL"),
@@ -166,7 +164,9 @@ def gather_call(mk, **kw):
 @pytest.mark.parametrize("kw,status,msg", [
     (dict(scale=None), 1, "needs cache_scale"),
     (dict(dt=1), 1, "takes no cache_scale"),
-    (dict(dt=3), 2, "fp8_e5m2"),
+    (dict(dt=3, scale=None), 1, "needs cache_scale"),
+    (dict(dt=3, odt=2, scale=None), 1, "must equal cache_dtype"),
+    (dict(dt=2, odt=3, scale=None), 1, "must equal cache_dtype"),
     (dict(width=600), 1, "exceeds entry_stride"),
     (dict(width=40), 2, "multiple of 16"),
     (dict(out=None), 1, "NULL"),

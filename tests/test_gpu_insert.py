@@ -129,8 +129,6 @@ def test_invalid_scales_raise(mk):
             run(bad)
     with pytest.raises(RuntimeError, match="takes no kv_scales"):
         run(d["scales"], "auto")
-    with pytest.raises(RuntimeError, match="fp8_e5m2"):
-        run(d["scales"], "fp8_e5m2")
     torch.cuda.synchronize()
     for a, b in zip(caches, before):
         assert torch.equal(a, b)
