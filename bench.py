@@ -370,6 +370,36 @@ def epilogue_component(torch, mk, dev, flush):
     return res
 
 
+def cache_dtype_component(torch, mk, dev, flush):
+    """The long-context insert (5 x 16384 rows) and the 8192-row gather with
+    e4m3fn and with e5m2 caches, each launch timed on its own."""
+    from fp8_paged_insert_amd import synth
+
+    d = synth.long_context_insert(dev)
+    L, T = d["num_layers"], d["num_tokens"]
+    ptrs = mk.cache_ptr_table(d["caches"])
+    pc = synth.context_pack(dev)
+    ws = torch.empty(8192, W, dtype=torch.bfloat16, device=dev)
+    sc = torch.tensor([0.5], device=dev)
+    out = {"workload": "long-context insert 5 x 16384 rows into [4096,64,576] caches; "
+                       "gather 8192 rows from a [512,64,576] cache"}
+    for name in ("fp8_e4m3", "fp8_e5m2"):
+        def ins():
+            mk.mla_kv_insert_grouped(d["kv_c"], d["k_pe"], ptrs, d["slot_mapping"], 64, 64 * W, W,
+                                     d["scales"], name)
+
+        def gat():
+            mk.mla_ctx_latent_gather(pc["cache"], pc["src_slots"], ws, sc, name)
+
+        for kind, fn, nbytes in (("insert", ins, insert_bytes(L, T)),
+                                 ("gather", gat, gather_bytes(8192))):
+            us = kernel_us(torch, mk, fn, flush)
+            out[f"{kind}_{name}"] = {"us": round(us, 2), "bytes": nbytes,
+                                     "GBps": round(nbytes / us / 1e3, 1),
+                                     "frac_of_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+    return out
+
+
 def projection_component(torch, mk, dev, flush):
     from fp8_paged_insert_amd import synth
 
@@ -528,6 +558,7 @@ def main():
         comps = {"small_batch_insert": small_batch(torch, mk, dev),
                  "context_pack": context_pack_component(torch, mk, dev, flush),
                  "context_epilogue": epilogue_component(torch, mk, dev, flush),
+                 "cache_dtypes": cache_dtype_component(torch, mk, dev, flush),
                  "context_kv_proj": projection_component(torch, mk, dev, flush)}
         result["components"] = comps
     if not args.no_cpu_baseline:
