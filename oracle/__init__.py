@@ -32,6 +32,9 @@ SRC_BF16 = 0
 SRC_FP16 = 1
 GATHER_BF16 = 0
 GATHER_FP8_RAW = 1
+MERGE_INIT_COPY = 0
+MERGE_INIT_WRITTEN = 1
+MERGE_ACCUMULATE = 2
 
 OK = 0
 EINVAL = -1
@@ -101,6 +104,10 @@ def _load():
         "orc_pack": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _i64,
                             _i64, _i64, _i64, _i64, _int, _int, _f32, _f32, _vp, _vp]),
         "orc_f16_to_f32_n": (None, [_vp, _i64, _vp]),
+        "orc_merge_chunk": (_int, [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp,
+                                   _i64, _i64, _i64, _i64, _i64, _int]),
+        "orc_neutralize_partials": (_int, [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64,
+                                           _i64]),
         "orc_e5m2_decode": (_f64, [ctypes.c_uint8]),
         "orc_e5m2_encode": (ctypes.c_uint8, [_f64]),
         "orc_e5m2_encode_f32_n": (None, [_vp, _i64, _vp]),
@@ -416,3 +423,39 @@ def pack(k_nope, k_pe, v=None, mode=PACK_KEY_BF16, k_scale=1.0, v_scale=1.0, fp1
                           float(v_scale), _ptr(key), _ptr(vout))
     _check(rc, "pack")
     return key, vout
+
+
+# ------------------------------------------------------------ chunk merge --
+def merge_chunk(out, lse, part, part_lse, mode=MERGE_ACCUMULATE):
+    """In-place merge of one chunk's partial into the accumulator.
+
+    out / part: [T, H, D] uint16 (bf16 bits) views with contiguous rows;
+    lse / part_lse: [H, T] float32 views (any strides).  Returns out, lse.
+    """
+    _need(out, np.uint16, "out")
+    _need(part, np.uint16, "part")
+    _need(lse, np.float32, "lse")
+    _need(part_lse, np.float32, "part_lse")
+    T, H, D = out.shape
+    if part.shape != out.shape or lse.shape != (H, T) or part_lse.shape != (H, T):
+        raise ValueError("shape mismatch")
+    rc = _load().orc_merge_chunk(
+        _ptr(out), out.strides[0] // 2, out.strides[1] // 2,
+        _ptr(lse), lse.strides[0] // 4, lse.strides[1] // 4,
+        _ptr(part), part.strides[0] // 2, part.strides[1] // 2,
+        _ptr(part_lse), part_lse.strides[0] // 4, part_lse.strides[1] // 4, T, H, D, mode)
+    _check(rc, "merge_chunk")
+    return out, lse
+
+
+def neutralize_partials(out, lse, no_context):
+    """out[t] = 0 and lse[:, t] = -inf wherever no_context[t] is nonzero (in place)."""
+    _need(out, np.uint16, "out")
+    _need(lse, np.float32, "lse")
+    T, H, D = out.shape
+    m = np.ascontiguousarray(no_context, dtype=np.uint8)
+    rc = _load().orc_neutralize_partials(
+        _ptr(out), out.strides[0] // 2, out.strides[1] // 2,
+        _ptr(lse), lse.strides[0] // 4, lse.strides[1] // 4, _ptr(m), T, H, D)
+    _check(rc, "neutralize_partials")
+    return out, lse

@@ -638,3 +638,89 @@ int orc_pack(const uint16_t* k_nope, int64_t kn_tok_stride, int64_t kn_head_stri
   }
   return ORC_OK;
 }
+
+/* ======================================================================== */
+/* Chunk-partial merge                                                       */
+/* ======================================================================== */
+
+/*
+ * Merge of chunked-context attention partials ([P1] 实现拆解 item 3:
+ * accumulate_mla_context_chunk with output_written, and
+ * neutralize_empty_context_partials; the pages give the behaviour, not the
+ * arithmetic).  Reading: a partial over one chunk of keys is the normalised
+ * output O_c[t, h, :] (bf16, the backend's output) and the natural-log
+ * log-sum-exp lse_c[h, t] (fp32) of that chunk's scores; two partials over
+ * disjoint key sets combine into the partial over their union by
+ *   m = max(lse_a, lse_b), w_x = exp(lse_x - m),
+ *   O = (w_a O_a + w_b O_b) / (w_a + w_b),  lse = m + log(w_a + w_b),
+ * computed here in float64 and rounded once (O to bf16, lse to fp32).  A
+ * partial whose lse is -inf covers no keys: it contributes nothing, whatever
+ * its O holds, and two such partials give (0, -inf), the neutral partial.
+ * Modes: INIT_COPY (the first chunk: the accumulator takes the partial),
+ * INIT_WRITTEN (the first chunk's output is already in the accumulator, so
+ * only its lse is taken -- the page's output_written), ACCUMULATE (a
+ * continuation chunk, merged as above).
+ */
+int orc_merge_chunk(uint16_t* out, int64_t out_tok_stride, int64_t out_head_stride,
+                    float* lse, int64_t lse_head_stride, int64_t lse_tok_stride,
+                    const uint16_t* part, int64_t part_tok_stride, int64_t part_head_stride,
+                    const float* part_lse, int64_t plse_head_stride, int64_t plse_tok_stride,
+                    int64_t num_tokens, int64_t num_heads, int64_t head_dim, int mode) {
+  if (num_tokens < 0 || num_heads < 0 || head_dim < 0) return ORC_EINVAL;
+  if (mode != ORC_MERGE_INIT_COPY && mode != ORC_MERGE_INIT_WRITTEN &&
+      mode != ORC_MERGE_ACCUMULATE)
+    return ORC_EINVAL;
+  for (int64_t t = 0; t < num_tokens; ++t) {
+    for (int64_t h = 0; h < num_heads; ++h) {
+      uint16_t* o = out + t * out_tok_stride + h * out_head_stride;
+      const uint16_t* p = part + t * part_tok_stride + h * part_head_stride;
+      float* l = lse + h * lse_head_stride + t * lse_tok_stride;
+      const float lp = part_lse[h * plse_head_stride + t * plse_tok_stride];
+      if (mode == ORC_MERGE_INIT_COPY) {
+        for (int64_t i = 0; i < head_dim; ++i) o[i] = p[i];
+        *l = lp;
+        continue;
+      }
+      if (mode == ORC_MERGE_INIT_WRITTEN) {
+        *l = lp;
+        continue;
+      }
+      const double la = (double)*l, lb = (double)lp;
+      const double m = la > lb ? la : lb;
+      if (m == -INFINITY) {                 /* neither partial covers a key */
+        for (int64_t i = 0; i < head_dim; ++i) o[i] = 0;
+        *l = -INFINITY;
+        continue;
+      }
+      const double wa = exp(la - m), wb = exp(lb - m);
+      const double sum = wa + wb;
+      for (int64_t i = 0; i < head_dim; ++i) {
+        double acc = 0.0;
+        if (wa != 0.0) acc += wa * (double)orc_bf16_to_f32(o[i]);
+        if (wb != 0.0) acc += wb * (double)orc_bf16_to_f32(p[i]);
+        o[i] = orc_f64_to_bf16(acc / sum);
+      }
+      *l = (float)(m + log(sum));
+    }
+  }
+  return ORC_OK;
+}
+
+/* The neutral partial (O = 0, lse = -inf) for every token whose flag is set:
+ * a prefill token with no context ([P1] 实现拆解 item 3,
+ * neutralize_empty_context_partials). */
+int orc_neutralize_partials(uint16_t* out, int64_t out_tok_stride, int64_t out_head_stride,
+                            float* lse, int64_t lse_head_stride, int64_t lse_tok_stride,
+                            const uint8_t* no_context, int64_t num_tokens,
+                            int64_t num_heads, int64_t head_dim) {
+  if (num_tokens < 0 || num_heads < 0 || head_dim < 0) return ORC_EINVAL;
+  for (int64_t t = 0; t < num_tokens; ++t) {
+    if (!no_context[t]) continue;
+    for (int64_t h = 0; h < num_heads; ++h) {
+      uint16_t* o = out + t * out_tok_stride + h * out_head_stride;
+      for (int64_t i = 0; i < head_dim; ++i) o[i] = 0;
+      lse[h * lse_head_stride + t * lse_tok_stride] = -INFINITY;
+    }
+  }
+  return ORC_OK;
+}

@@ -30,6 +30,7 @@ enum { ORC_CACHE_BF16 = 0, ORC_CACHE_FP8_E4M3 = 1, ORC_CACHE_FP8_E5M2 = 2 };
 enum { ORC_PACK_KEY_BF16 = 0, ORC_PACK_KEY_V_FP8 = 1, ORC_PACK_KEY_V_FP8_KPE_RAW = 2 };
 enum { ORC_SRC_BF16 = 0, ORC_SRC_FP16 = 1 };          /* 16-bit source format of the pack */
 enum { ORC_GATHER_BF16 = 0, ORC_GATHER_FP8_RAW = 1 };  /* gather output */
+enum { ORC_MERGE_INIT_COPY = 0, ORC_MERGE_INIT_WRITTEN = 1, ORC_MERGE_ACCUMULATE = 2 };
 
 /* ---- number formats --------------------------------------------------- */
 float    orc_bf16_to_f32(uint16_t b);
@@ -110,6 +111,18 @@ int orc_pack(const uint16_t* k_nope, int64_t kn_tok_stride, int64_t kn_head_stri
              int64_t num_tokens, int64_t num_heads, int64_t nope_dim,
              int64_t rope_dim, int64_t v_dim, int mode, int src_format,
              float k_scale, float v_scale, void* key_out, uint8_t* v_out);
+
+/* ---- chunk-partial merge ------------------------------------------------ */
+int orc_merge_chunk(uint16_t* out, int64_t out_tok_stride, int64_t out_head_stride,
+                    float* lse, int64_t lse_head_stride, int64_t lse_tok_stride,
+                    const uint16_t* part, int64_t part_tok_stride, int64_t part_head_stride,
+                    const float* part_lse, int64_t plse_head_stride, int64_t plse_tok_stride,
+                    int64_t num_tokens, int64_t num_heads, int64_t head_dim, int mode);
+
+int orc_neutralize_partials(uint16_t* out, int64_t out_tok_stride, int64_t out_head_stride,
+                            float* lse, int64_t lse_head_stride, int64_t lse_tok_stride,
+                            const uint8_t* no_context, int64_t num_tokens,
+                            int64_t num_heads, int64_t head_dim);
 
 #ifdef __cplusplus
 }
