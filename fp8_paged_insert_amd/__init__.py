@@ -1,5 +1,5 @@
-"""MI355X (gfx950) grouped MLA latent-KV insert, context-KV epilogue and
-chunked-context gather / pack.
+"""MI355X (gfx950) grouped MLA latent-KV insert, context-KV epilogue,
+chunked-context gather / pack and the merge of chunk attention partials.
 
 The computation lives in ``libmla_kv.so`` (hand-written HIP, built by
 ``python -m fp8_paged_insert_amd.build``); this package only marshals torch
@@ -21,6 +21,9 @@ from ._binding import (  # noqa: F401
     MLA_PACK_KEY_BF16,
     MLA_PACK_KEY_V_FP8,
     MLA_PACK_KEY_V_FP8_KPE_RAW,
+    MLA_MERGE_INIT_COPY,
+    MLA_MERGE_INIT_WRITTEN,
+    MLA_MERGE_ACCUMULATE,
     LIB_PATH,
     MlaError,
     cache_ptr_table,
@@ -30,6 +33,8 @@ from ._binding import (  # noqa: F401
     mla_ctx_kv_pack,
     mla_ctx_kv_proj,
     mla_ctx_latent_gather,
+    mla_ctx_merge_chunk,
+    mla_ctx_neutralize_partials,
     mla_kv_insert_grouped,
     mla_rope_cos_sin_cache,
     parse_kv_cache_dtype,

@@ -33,11 +33,16 @@ MLA_PACK_KEY_BF16 = 0
 MLA_PACK_KEY_V_FP8 = 1
 MLA_PACK_KEY_V_FP8_KPE_RAW = 2
 
+MLA_MERGE_INIT_COPY = 0
+MLA_MERGE_INIT_WRITTEN = 1
+MLA_MERGE_ACCUMULATE = 2
+
 # Every symbol include/mla_kv.h declares.
 EXPORTS = (
     "mla_last_error", "mla_version", "mla_parse_kv_cache_dtype", "mla_set_launch_events",
     "mla_kv_insert_grouped", "mla_rope_cos_sin_cache", "mla_ctx_kv_epilogue",
     "mla_ctx_kv_proj", "mla_ctx_latent_gather", "mla_ctx_kv_pack",
+    "mla_ctx_merge_chunk", "mla_ctx_neutralize_partials",
 )
 
 
@@ -66,6 +71,10 @@ _SIGS = {
                                      _vp, _i64, _vp]),
     "mla_ctx_kv_pack": (_i32, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _i64,
                                _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _vp]),
+    "mla_ctx_merge_chunk": (_i32, [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp,
+                                   _i64, _i64, _i64, _i64, _i64, _i32, _vp]),
+    "mla_ctx_neutralize_partials": (_i32, [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64,
+                                           _i64, _vp]),
 }
 
 _lib = None
@@ -484,3 +493,49 @@ def mla_ctx_kv_pack(k_nope, k_pe, key_out, v=None, v_out=None, mode=MLA_PACK_KEY
         vts, vhs, T, H, nope, rope, vd, int(mode), src, _ptr(k_scale), _ptr(v_scale),
         _ptr(key_out), _ptr(v_out), int(max_blocks), _stream(k_nope))
     _check(st, "mla_ctx_kv_pack")
+
+
+# ------------------------------------------------------------ chunk merge --
+def _check_partial(o, lse, T, H, D, name, lname, ref):
+    _need(o, (torch.bfloat16,), name)
+    _need(lse, (torch.float32,), lname)
+    if o.dim() != 3 or tuple(o.shape) != (T, H, D) or (D > 1 and o.stride(2) != 1):
+        raise RuntimeError(f"{name} must be a [{T}, {H}, {D}] view with contiguous rows")
+    if lse.dim() != 2 or tuple(lse.shape) != (H, T):
+        raise RuntimeError(f"{lname} must be a [{H}, {T}] view (heads, tokens)")
+    _same_device(o, ref, name, "out")
+    _same_device(lse, ref, lname, "out")
+
+
+def mla_ctx_merge_chunk(out, lse, part, part_lse, mode=MLA_MERGE_ACCUMULATE):
+    """Fold one chunk's partial (part [T, H, D] bf16, part_lse [H, T] fp32) into
+    the accumulator (out, lse), in place.  In MLA_MERGE_INIT_WRITTEN mode the
+    chunk's output is already in `out`; pass part=None (or out)."""
+    if out.dim() != 3:
+        raise RuntimeError("out must be [num_tokens, num_heads, head_dim]")
+    T, H, D = out.shape
+    _check_partial(out, lse, T, H, D, "out", "lse", out)
+    if mode == MLA_MERGE_INIT_WRITTEN and part is None:
+        part = out
+    _check_partial(part, part_lse, T, H, D, "part", "part_lse", out)
+    st = lib().mla_ctx_merge_chunk(
+        _ptr(out), out.stride(0), out.stride(1), _ptr(lse), lse.stride(0), lse.stride(1),
+        None if mode == MLA_MERGE_INIT_WRITTEN else _ptr(part), part.stride(0), part.stride(1),
+        _ptr(part_lse), part_lse.stride(0), part_lse.stride(1), T, H, D, int(mode), _stream(out))
+    _check(st, "mla_ctx_merge_chunk")
+
+
+def mla_ctx_neutralize_partials(out, lse, no_context):
+    """out[t] = 0 and lse[:, t] = -inf wherever no_context[t] (bool/uint8 [T]) is set."""
+    if out.dim() != 3:
+        raise RuntimeError("out must be [num_tokens, num_heads, head_dim]")
+    T, H, D = out.shape
+    _check_partial(out, lse, T, H, D, "out", "lse", out)
+    _need(no_context, (torch.uint8, torch.bool), "no_context")
+    if no_context.numel() != T or not no_context.is_contiguous():
+        raise RuntimeError(f"no_context must be a contiguous [{T}] mask")
+    _same_device(no_context, out, "no_context", "out")
+    st = lib().mla_ctx_neutralize_partials(
+        _ptr(out), out.stride(0), out.stride(1), _ptr(lse), lse.stride(0), lse.stride(1),
+        _ptr(no_context), T, H, D, _stream(out))
+    _check(st, "mla_ctx_neutralize_partials")

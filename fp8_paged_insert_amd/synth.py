@@ -192,6 +192,24 @@ def context_pack(device="cpu", seed=4, num_ctx=8192, heads=64):
     return d
 
 
+def attention_partials(device="cpu", seed=7, num_tokens=16384, heads=64, head_dim=128,
+                       chunks=16, empty_frac=0.0):
+    """Per-chunk attention partials of the chunked-context loop: outputs
+    [chunks][T, H, D] ~ N(0, 1) in bf16 and natural-log lse [chunks][H, T]
+    ~ N(8, 3^2) in fp32; a fraction empty_frac of the lse entries is -inf
+    (chunks that hold no key for that query)."""
+    g = gen(seed, device)
+    outs = [bf16_normal((num_tokens, heads, head_dim), g, device) for _ in range(chunks)]
+    lses = []
+    for _ in range(chunks):
+        l = 8.0 + 3.0 * torch.randn((heads, num_tokens), generator=g, device=device)
+        if empty_frac > 0:
+            u = torch.rand((heads, num_tokens), generator=g, device=device)
+            l = torch.where(u < empty_frac, torch.full_like(l, float("-inf")), l)
+        lses.append(l)
+    return dict(outs=outs, lses=lses, num_tokens=num_tokens, heads=heads, head_dim=head_dim)
+
+
 def long_context_insert(device="cpu", seed=5, num_tokens=16384, num_blocks=4096):
     g = gen(seed, device)
     L, T = NUM_LAYERS, num_tokens

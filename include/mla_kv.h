@@ -8,6 +8,7 @@
  *   insert      mla_kv_insert_grouped  [kv_c | k_pe] -> fp8/bf16 -> paged caches, all layers
  *   gather      mla_ctx_latent_gather  paged cache rows -> contiguous bf16 (or raw fp8) workspace
  *   pack        mla_ctx_kv_pack        [k_nope | k_pe] full key (+ fp8 V), contiguous
+ *   merge       mla_ctx_merge_chunk    chunk attention partials -> accumulator (log-sum-exp)
  *
  * Pages cited (title and section heading):
  *   [P1] "PR #51772 完整报告" -- [Attention][MLA] Fuse Kimi-K3 chunked-context K/V packing
@@ -70,6 +71,15 @@ typedef enum {
   MLA_PACK_KEY_V_FP8 = 1,         /* fp8 full key and fp8 V */
   MLA_PACK_KEY_V_FP8_KPE_RAW = 2  /* as KEY_V_FP8, k_pe given as fp8 codes, copied as is */
 } mla_pack_mode_t;
+
+/* How a chunk's attention partial enters the accumulator ([P1] 实现拆解
+ * item 3, accumulate_mla_context_chunk and its output_written flag). */
+typedef enum {
+  MLA_MERGE_INIT_COPY = 0,     /* first chunk: the accumulator takes the partial */
+  MLA_MERGE_INIT_WRITTEN = 1,  /* first chunk already written into the accumulator:
+                                  only its lse is taken */
+  MLA_MERGE_ACCUMULATE = 2     /* continuation chunk: log-sum-exp merge */
+} mla_merge_mode_t;
 
 /* Description of the last error on the calling thread ("" if none). */
 const char* mla_last_error(void);
@@ -272,6 +282,48 @@ int32_t mla_ctx_kv_pack(const void* k_nope, int64_t kn_tok_stride,
                         const float* k_scale, const float* v_scale,
                         void* key_out, void* v_out, int64_t max_blocks,
                         mla_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * mla_ctx_merge_chunk -- fold one context chunk's attention partial into the
+ * accumulator of the chunked-context loop ([P1] 实现拆解 item 3: the
+ * accumulator is allocated before any chunk; a non-continuation chunk may
+ * write its output straight into it, after which only its log-sum-exp is
+ * folded in; continuation chunks are merged).  For every token t and head h:
+ *   INIT_COPY:    out[t, h, :] = part[t, h, :];  lse[h, t] = part_lse[h, t]
+ *   INIT_WRITTEN: lse[h, t] = part_lse[h, t]   (out already holds the
+ *                 chunk's output; part is not read and may be NULL)
+ *   ACCUMULATE:   m = max(lse, part_lse), w_x = exp(lse_x - m),
+ *                 out = bf16((w_a out + w_b part) / (w_a + w_b)),
+ *                 lse = m + log(w_a + w_b)  (natural log; fp32 arithmetic)
+ *                 A partial whose lse is -inf covers no key and contributes
+ *                 nothing (its output is not used); if both are -inf the
+ *                 result is the neutral partial (0, -inf).
+ * out, part  device bf16 [t, h, i] at t*tok_stride + h*head_stride + i; rows
+ *            16-byte aligned; head_dim a multiple of 8.  out is updated in
+ *            place; ACCUMULATE refuses part == out (a continuation chunk's
+ *            output cannot already sit in the accumulator -- the page's
+ *            assertion on output_written).
+ * lse, part_lse  device fp32 [h, t] at h*head_stride + t*tok_stride.
+ * ------------------------------------------------------------------------ */
+int32_t mla_ctx_merge_chunk(void* out, int64_t out_tok_stride, int64_t out_head_stride,
+                            float* lse, int64_t lse_head_stride, int64_t lse_tok_stride,
+                            const void* part, int64_t part_tok_stride,
+                            int64_t part_head_stride, const float* part_lse,
+                            int64_t part_lse_head_stride, int64_t part_lse_tok_stride,
+                            int64_t num_tokens, int64_t num_heads, int64_t head_dim,
+                            int32_t mode, mla_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * mla_ctx_neutralize_partials -- set the neutral partial (out = 0,
+ * lse = -inf) for every token t with no_context[t] != 0: prefill tokens
+ * whose request has no context start the merge from it ([P1] 实现拆解
+ * item 3, neutralize_empty_context_partials).  Layouts as for
+ * mla_ctx_merge_chunk; no_context is a device uint8 [num_tokens].
+ * ------------------------------------------------------------------------ */
+int32_t mla_ctx_neutralize_partials(void* out, int64_t out_tok_stride, int64_t out_head_stride,
+                                    float* lse, int64_t lse_head_stride, int64_t lse_tok_stride,
+                                    const uint8_t* no_context, int64_t num_tokens,
+                                    int64_t num_heads, int64_t head_dim, mla_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -184,3 +184,39 @@ def test_rope_table_rejects(mk):
     assert mk.lib().mla_rope_cos_sin_cache(P16, 10, 63, 10000.0, None) == mk.MLA_ERR_INVALID_ARGUMENT
     assert mk.lib().mla_rope_cos_sin_cache(P16, 10, 64, -1.0, None) == mk.MLA_ERR_INVALID_ARGUMENT
     assert mk.lib().mla_rope_cos_sin_cache(None, 0, 64, 10000.0, None) == mk.MLA_OK
+
+
+def merge_call(mk, **kw):
+    a = dict(out=P16, ots=8192, ohs=128, lse=P16, lhs=16384, lts=1, part=P16 + 0x100000,
+             pts=8192, phs=128, plse=P16, plhs=16384, plts=1, T=16384, H=64, D=128,
+             mode=mk.MLA_MERGE_ACCUMULATE)
+    a.update(kw)
+    return mk.lib().mla_ctx_merge_chunk(
+        a["out"], a["ots"], a["ohs"], a["lse"], a["lhs"], a["lts"], a["part"], a["pts"], a["phs"],
+        a["plse"], a["plhs"], a["plts"], a["T"], a["H"], a["D"], a["mode"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(mode=5), 1, "unknown mode"),
+    (dict(T=-1), 1, "negative"),
+    (dict(lse=None), 1, "NULL"),
+    (dict(plse=None), 1, "NULL part_lse"),
+    (dict(part=None), 1, "NULL part"),
+    (dict(D=100), 2, "multiple of 8"),
+    (dict(ohs=127), 3, "16-byte aligned"),
+    (dict(part=P_ODD), 3, "16-byte aligned"),
+    (dict(part=P16), 1, "continuation chunk"),
+    (dict(plse=P16 + 2), 3, "4-byte aligned"),
+])
+def test_merge_rejects_bad_arguments(mk, kw, status, msg):
+    assert merge_call(mk, **kw) == status
+    assert msg in mk.last_error()
+
+
+def test_merge_and_neutralize_zero_sizes_are_noops(mk):
+    assert merge_call(mk, T=0) == mk.MLA_OK
+    assert merge_call(mk, H=0, part=None) == mk.MLA_OK
+    assert mk.lib().mla_ctx_neutralize_partials(P16, 8192, 128, P16, 16384, 1, None, 0, 64, 128,
+                                                None) == mk.MLA_OK
+    assert mk.lib().mla_ctx_neutralize_partials(P16, 8192, 128, P16, 16384, 1, None, 5, 64, 128,
+                                                None) == mk.MLA_ERR_INVALID_ARGUMENT
