@@ -65,6 +65,12 @@ def pack_fp8_kpe_raw_bytes(tokens, heads, nope=128, rope=64, vdim=128):
             + tokens * heads * (nope + rope) + tokens * heads * vdim)
 
 
+def merge_bytes(tokens, heads, head_dim=128):
+    """Read the accumulator and the chunk's partial (bf16 rows and fp32 lse);
+    write the accumulator back."""
+    return 3 * tokens * heads * head_dim * 2 + 3 * tokens * heads * 4
+
+
 def pack_bf16_bytes(tokens, heads, nope=128, rope=64):
     return tokens * heads * nope * 2 + tokens * rope * 2 + tokens * heads * (nope + rope) * 2
 
@@ -400,6 +406,28 @@ def cache_dtype_component(torch, mk, dev, flush):
     return out
 
 
+def merge_component(torch, mk, dev, flush):
+    """One log-sum-exp merge of a chunk partial into the accumulator of the
+    chunked-context loop: 16384 query tokens x 64 heads x 128 (bf16 rows,
+    fp32 lse [heads, tokens])."""
+    from fp8_paged_insert_amd import synth
+
+    T, H, D = 16384, 64, 128
+    d = synth.attention_partials(dev, num_tokens=T, heads=H, head_dim=D, chunks=2)
+    acc, lacc = d["outs"][0].clone(), d["lses"][0].clone()
+    part, plse = d["outs"][1], d["lses"][1]
+
+    def merge():
+        mk.mla_ctx_merge_chunk(acc, lacc, part, plse, mk.MLA_MERGE_ACCUMULATE)
+
+    us = kernel_us(torch, mk, merge, flush)
+    nb = merge_bytes(T, H, D)
+    return {"workload": "merge of one chunk partial into the accumulator, 16384 tokens x 64 "
+                        "heads x 128 (bf16 outputs, fp32 lse)",
+            "us": round(us, 2), "bytes": nb, "GBps": round(nb / us / 1e3, 1),
+            "frac_of_peak": round(nb / us / 1e3 / HBM_PEAK_GBS, 4)}
+
+
 def projection_component(torch, mk, dev, flush):
     from fp8_paged_insert_amd import synth
 
@@ -559,6 +587,7 @@ def main():
                  "context_pack": context_pack_component(torch, mk, dev, flush),
                  "context_epilogue": epilogue_component(torch, mk, dev, flush),
                  "cache_dtypes": cache_dtype_component(torch, mk, dev, flush),
+                 "chunk_merge": merge_component(torch, mk, dev, flush),
                  "context_kv_proj": projection_component(torch, mk, dev, flush)}
         result["components"] = comps
     if not args.no_cpu_baseline:
