@@ -192,6 +192,38 @@ def context_pack(device="cpu", seed=4, num_ctx=8192, heads=64):
     return d
 
 
+def new_tokens(device="cpu", seed=8, num_tokens=8192, heads=64, num_blocks=512, requests=8,
+               fp8_cache=True):
+    """Inputs of the new-token epilogue for one layer: the query projection
+    output q [T, H, 192] (q_nope | q_pe), the kv_b_proj output [T, H, 256]
+    (k_nope | v), the normed latent and un-rotated k_pe [T, 576], positions of
+    `requests` prefills of T / requests tokens each that continue a context
+    of U[0, 4096) tokens, a seeded cache of num_blocks x 64 entries, distinct
+    slots with one padded token (-1), and scales U(0.5, 2)."""
+    g = gen(seed, device)
+    T, H = num_tokens, heads
+    q = bf16_normal((T, H, 192), g, device)
+    kvb = kv_b_proj_output(T, g, device, heads=H)
+    kv = bf16_normal((T, KV_WIDTH), g, device)
+    per = max(1, T // requests)
+    starts = torch.randint(0, 4096, (requests,), generator=g, device=device)
+    idx = torch.arange(T, device=device)
+    req = torch.clamp(idx // per, max=requests - 1)
+    positions = starts[req] + (idx - req * per)
+    if fp8_cache:
+        cache = random_bytes((num_blocks, 64, KV_WIDTH), g, device)
+    else:
+        cache = random_bf16_bits((num_blocks, 64, KV_WIDTH), g, device)
+    slots = randperm(num_blocks * 64, g, device)[:T].clone()
+    if T > 5:
+        slots[5] = -1
+    sc = f32_uniform((4,), 0.5, 2.0, g, device)
+    return dict(q=q, kvb=kvb, kv=kv, positions=positions.to(torch.int64), cache=cache,
+                slots=slots, q_scale=sc[0:1], k_scale=sc[1:2], v_scale=sc[2:3],
+                cache_scale=sc[3:4], num_tokens=T, num_heads=H, max_pos=8192 + T,
+                block_size=64)
+
+
 def attention_partials(device="cpu", seed=7, num_tokens=16384, heads=64, head_dim=128,
                        chunks=16, empty_frac=0.0):
     """Per-chunk attention partials of the chunked-context loop: outputs

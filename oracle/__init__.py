@@ -48,7 +48,9 @@ class OracleError(RuntimeError):
 def build(force: bool = True) -> str:
     """Compile the oracle shared library with gcc; returns its path."""
     if not force and os.path.exists(_LIB):
-        return _LIB
+        srcs = (_SRC, os.path.splitext(_SRC)[0] + ".h")
+        if all(os.path.getmtime(x) <= os.path.getmtime(_LIB) for x in srcs):
+            return _LIB
     tmp = _LIB + ".tmp"
     cmd = [
         "gcc", "-std=c11", "-O2", "-fno-fast-math", "-ffp-contract=off",
@@ -104,6 +106,11 @@ def _load():
         "orc_pack": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _i64,
                             _i64, _i64, _i64, _i64, _int, _int, _f32, _f32, _vp, _vp]),
         "orc_f16_to_f32_n": (None, [_vp, _i64, _vp]),
+        "orc_new_token_epilogue": (_int, [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64,
+                                          _vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _f64,
+                                          _i64, _i64, _i64, _i64, _i64, _i64, _int,
+                                          _f32, _f32, _f32, _vp, _vp, _vp,
+                                          _vp, _vp, _i64, _i64, _i64, _int, _f32]),
         "orc_merge_chunk": (_int, [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp,
                                    _i64, _i64, _i64, _i64, _i64, _int]),
         "orc_neutralize_partials": (_int, [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64,
@@ -423,6 +430,55 @@ def pack(k_nope, k_pe, v=None, mode=PACK_KEY_BF16, k_scale=1.0, v_scale=1.0, fp1
                           float(v_scale), _ptr(key), _ptr(vout))
     _check(rc, "pack")
     return key, vout
+
+
+# ------------------------------------------------------ new-token epilogue --
+def new_token_epilogue(q_nope, q_pe, k_nope, kv_c, k_pe, positions, v=None, mode=PACK_KEY_BF16,
+                       q_scale=1.0, k_scale=1.0, v_scale=1.0, cache=None, slots=None,
+                       cache_scale=1.0, fp8_format="e4m3", rope_base=10000.0):
+    """RoPE of q_pe and k_pe, the query row, the chunked-context pack of the
+    key (and V), and the insert of [kv_c | rotated k_pe] into `cache` (in place).
+
+    q_nope [T, H, nope], q_pe [T, H, rope], k_nope [T, H, nope], v [T, H, vdim]
+    uint16 views with contiguous last dims; kv_c [T, R], k_pe [T, rope] uint16
+    views; positions [T] int64; cache [num_blocks, block_size, E] or None,
+    slots [T] int64.  Returns (q_out, key, v_out) as the pack does.
+    """
+    for a, n in ((q_nope, "q_nope"), (q_pe, "q_pe"), (k_nope, "k_nope"), (kv_c, "kv_c"),
+                 (k_pe, "k_pe")):
+        _need(a, np.uint16, n)
+        if a.size and a.strides[-1] != 2:
+            raise ValueError(f"{n}: innermost dimension must be contiguous")
+    T, H, nope = q_nope.shape
+    rope = q_pe.shape[2]
+    R = kv_c.shape[1]
+    positions = np.ascontiguousarray(positions, np.int64)
+    fp8 = mode != PACK_KEY_BF16
+    q_out = np.empty((T, H, nope + rope), np.uint8 if fp8 else np.uint16)
+    key = np.empty((T, H, nope + rope), np.uint8 if fp8 else np.uint16)
+    vout, vd, vts, vhs = None, 0, 0, 0
+    if fp8:
+        _need(v, np.uint16, "v")
+        vd = v.shape[2]
+        vts, vhs = v.strides[0] // 2, v.strides[1] // 2
+        vout = np.empty((T, H, vd), np.uint8)
+    bs = bst = est = 0
+    cdt = CACHE_BF16
+    if cache is not None:
+        slots = np.ascontiguousarray(slots, np.int64)
+        it = cache.itemsize
+        bs, bst, est = cache.shape[1], cache.strides[0] // it, cache.strides[1] // it
+        cdt = _cache_dtype_code(cache, fp8_format)
+    rc = _load().orc_new_token_epilogue(
+        _ptr(q_nope), q_nope.strides[0] // 2, q_nope.strides[1] // 2,
+        _ptr(q_pe), q_pe.strides[0] // 2, q_pe.strides[1] // 2,
+        _ptr(k_nope), k_nope.strides[0] // 2, k_nope.strides[1] // 2,
+        _ptr(v), vts, vhs, _ptr(kv_c), kv_c.strides[0] // 2, _ptr(k_pe), k_pe.strides[0] // 2,
+        _ptr(positions), float(rope_base), T, H, nope, rope, vd, R, mode,
+        float(q_scale), float(k_scale), float(v_scale), _ptr(q_out), _ptr(key), _ptr(vout),
+        _ptr(cache), _ptr(slots), bs, bst, est, cdt, float(cache_scale))
+    _check(rc, "new_token_epilogue")
+    return q_out, key, vout
 
 
 # ------------------------------------------------------------ chunk merge --

@@ -639,6 +639,95 @@ int orc_pack(const uint16_t* k_nope, int64_t kn_tok_stride, int64_t kn_head_stri
   return ORC_OK;
 }
 
+/*
+ * New-token epilogue ([P1] 功能与动机: the new-token epilogue already
+ * quantises the query; [P1] 关键源码片段, fused_mla_key_concat_kv_cache.py:
+ * the chunked-context pack is the new-token op without the query, without
+ * the cache insert and without RoPE, because gathered context k_pe is already
+ * rotated).  The pages name the op (fused_mla_key_concat_kv_cache_insert) and
+ * nothing more; the reading is that op = the chunked-context pack plus the
+ * three parts it lacks, each done as elsewhere on the path:
+ *   1. RoPE at the token's position, of k_pe[t, :] once and of q_pe[t, h, :]
+ *      for every head (orc_rope_row; bf16 results);
+ *   2. query:  q_out[t, h, :] = [q_nope[t, h, :] | rope(q_pe[t, h, :])],
+ *      a bf16 copy in mode KEY_BF16, e4m3fn codes of fl32(x) / q_scale in
+ *      mode KEY_V_FP8;
+ *   3. key (and V in fp8 mode): the chunked-context pack (orc_pack) of
+ *      k_nope and v with the rotated k_pe;
+ *   4. cache insert of [kv_c[t, :] | rope(k_pe[t, :])] at slots[t]
+ *      (orc_insert_single; a negative slot skips the token); cache may be
+ *      NULL to skip the insert.
+ * Outputs q_out and key_out are contiguous [T, H, nope + rope] (uint16 bf16
+ * bits or uint8 codes), v_out contiguous [T, H, v_dim] codes (fp8 mode).
+ */
+int orc_new_token_epilogue(
+    const uint16_t* q_nope, int64_t qn_tok_stride, int64_t qn_head_stride,
+    const uint16_t* q_pe, int64_t qp_tok_stride, int64_t qp_head_stride,
+    const uint16_t* k_nope, int64_t kn_tok_stride, int64_t kn_head_stride,
+    const uint16_t* v, int64_t v_tok_stride, int64_t v_head_stride,
+    const uint16_t* kv_c, int64_t kv_c_tok_stride,
+    const uint16_t* k_pe, int64_t k_pe_tok_stride,
+    const int64_t* positions, double rope_base,
+    int64_t num_tokens, int64_t num_heads, int64_t nope_dim, int64_t rope_dim,
+    int64_t v_dim, int64_t kv_lora_rank, int mode,
+    float q_scale, float k_scale, float v_scale,
+    void* q_out, void* key_out, uint8_t* v_out,
+    void* cache, const int64_t* slots, int64_t block_size, int64_t block_stride,
+    int64_t entry_stride, int cache_dtype, float cache_scale) {
+  if (num_tokens < 0 || num_heads < 0 || nope_dim < 0 || rope_dim <= 0 || (rope_dim & 1) ||
+      v_dim < 0 || kv_lora_rank < 0)
+    return ORC_EINVAL;
+  if (mode != ORC_PACK_KEY_BF16 && mode != ORC_PACK_KEY_V_FP8) return ORC_EINVAL;
+  for (int64_t t = 0; t < num_tokens; ++t)
+    if (positions[t] < 0) return ORC_EINVAL;
+  const int64_t qw = nope_dim + rope_dim;
+  uint16_t* kpe_rot = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(num_tokens * rope_dim + 1));
+  uint16_t* qpe_rot = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)rope_dim);
+  if (!kpe_rot || !qpe_rot) {
+    free(kpe_rot);
+    free(qpe_rot);
+    return ORC_EINVAL;
+  }
+  int rc = ORC_OK;
+  /* 1. RoPE of k_pe, once per token */
+  for (int64_t t = 0; t < num_tokens && rc == ORC_OK; ++t)
+    rc = orc_rope_row(k_pe + t * k_pe_tok_stride, rope_dim, positions[t], rope_base,
+                      kpe_rot + t * rope_dim);
+  /* 1 + 2. RoPE of q_pe per head, and the query row */
+  for (int64_t t = 0; t < num_tokens && rc == ORC_OK; ++t) {
+    for (int64_t h = 0; h < num_heads && rc == ORC_OK; ++h) {
+      const uint16_t* qn = q_nope + t * qn_tok_stride + h * qn_head_stride;
+      rc = orc_rope_row(q_pe + t * qp_tok_stride + h * qp_head_stride, rope_dim, positions[t],
+                        rope_base, qpe_rot);
+      const int64_t o = (t * num_heads + h) * qw;
+      if (mode == ORC_PACK_KEY_BF16) {
+        uint16_t* q = (uint16_t*)q_out + o;
+        for (int64_t i = 0; i < nope_dim; ++i) q[i] = qn[i];
+        for (int64_t j = 0; j < rope_dim; ++j) q[nope_dim + j] = qpe_rot[j];
+      } else {
+        uint8_t* q = (uint8_t*)q_out + o;
+        for (int64_t i = 0; i < nope_dim; ++i)
+          q[i] = orc_quantize_f32(orc_bf16_to_f32(qn[i]), q_scale);
+        for (int64_t j = 0; j < rope_dim; ++j)
+          q[nope_dim + j] = orc_quantize_f32(orc_bf16_to_f32(qpe_rot[j]), q_scale);
+      }
+    }
+  }
+  /* 3. key (and V): the chunked-context pack with the rotated k_pe */
+  if (rc == ORC_OK)
+    rc = orc_pack(k_nope, kn_tok_stride, kn_head_stride, kpe_rot, rope_dim, v, v_tok_stride,
+                  v_head_stride, num_tokens, num_heads, nope_dim, rope_dim, v_dim, mode,
+                  ORC_SRC_BF16, k_scale, v_scale, key_out, v_out);
+  /* 4. the cache row [kv_c | rotated k_pe] */
+  if (rc == ORC_OK && cache)
+    rc = orc_insert_single(kv_c, kv_c_tok_stride, kpe_rot, rope_dim, slots, num_tokens,
+                           kv_lora_rank, rope_dim, cache, block_size, block_stride,
+                           entry_stride, cache_dtype, cache_scale);
+  free(kpe_rot);
+  free(qpe_rot);
+  return rc;
+}
+
 /* ======================================================================== */
 /* Chunk-partial merge                                                       */
 /* ======================================================================== */

@@ -112,6 +112,22 @@ int orc_pack(const uint16_t* k_nope, int64_t kn_tok_stride, int64_t kn_head_stri
              int64_t rope_dim, int64_t v_dim, int mode, int src_format,
              float k_scale, float v_scale, void* key_out, uint8_t* v_out);
 
+/* ---- new-token epilogue ------------------------------------------------- */
+int orc_new_token_epilogue(
+    const uint16_t* q_nope, int64_t qn_tok_stride, int64_t qn_head_stride,
+    const uint16_t* q_pe, int64_t qp_tok_stride, int64_t qp_head_stride,
+    const uint16_t* k_nope, int64_t kn_tok_stride, int64_t kn_head_stride,
+    const uint16_t* v, int64_t v_tok_stride, int64_t v_head_stride,
+    const uint16_t* kv_c, int64_t kv_c_tok_stride,
+    const uint16_t* k_pe, int64_t k_pe_tok_stride,
+    const int64_t* positions, double rope_base,
+    int64_t num_tokens, int64_t num_heads, int64_t nope_dim, int64_t rope_dim,
+    int64_t v_dim, int64_t kv_lora_rank, int mode,
+    float q_scale, float k_scale, float v_scale,
+    void* q_out, void* key_out, uint8_t* v_out,
+    void* cache, const int64_t* slots, int64_t block_size, int64_t block_stride,
+    int64_t entry_stride, int cache_dtype, float cache_scale);
+
 /* ---- chunk-partial merge ------------------------------------------------ */
 int orc_merge_chunk(uint16_t* out, int64_t out_tok_stride, int64_t out_head_stride,
                     float* lse, int64_t lse_head_stride, int64_t lse_tok_stride,
