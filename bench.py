@@ -71,6 +71,18 @@ def merge_bytes(tokens, heads, head_dim=128):
     return 3 * tokens * heads * head_dim * 2 + 3 * tokens * heads * 4
 
 
+def new_token_bytes(tokens, heads, fp8, valid_rows, cache_elem=1, nope=128, rope=64, vdim=128):
+    """Read the query [T, H, nope+rope], k_nope (and v in fp8 mode) from their
+    strided views, the latent row [kv_c | k_pe], the position, the slot and
+    the cos/sin row of each token; write the query and key rows (and fp8 V)
+    and one cache entry per valid token."""
+    ob = 1 if fp8 else 2
+    per_row = (nope + rope) * 2 + nope * 2 + (vdim * 2 if fp8 else 0)
+    per_row += 2 * (nope + rope) * ob + (vdim if fp8 else 0)
+    per_tok = (R + P) * 2 + 8 + 8 + P * 4
+    return tokens * heads * per_row + tokens * per_tok + valid_rows * W * cache_elem
+
+
 def pack_bf16_bytes(tokens, heads, nope=128, rope=64):
     return tokens * heads * nope * 2 + tokens * rope * 2 + tokens * heads * (nope + rope) * 2
 
@@ -428,6 +440,47 @@ def merge_component(torch, mk, dev, flush):
             "frac_of_peak": round(nb / us / 1e3 / HBM_PEAK_GBS, 4)}
 
 
+def new_token_component(torch, mk, dev, flush):
+    """The new-token epilogue of one layer for an 8192-token prefill batch
+    (8 requests continuing contexts of up to 4096 tokens) with 64 heads:
+    RoPE of q_pe / k_pe, query and key rows (+ fp8 V), insert into a
+    [512, 64, 576] e4m3fn cache; fp8 (e4m3fn) and bf16 attention inputs."""
+    from fp8_paged_insert_amd import synth
+
+    d = synth.new_tokens(dev)
+    T, H = d["num_tokens"], d["num_heads"]
+    cs = torch.empty(d["max_pos"], P, dtype=torch.float32, device=dev)
+    mk.mla_rope_cos_sin_cache(cs, d["max_pos"], P, 10000.0)
+    q, kvb, kv = d["q"], d["kvb"], d["kv"]
+    valid = int((d["slots"] >= 0).sum())
+    out = {"workload": "new-token epilogue, 8192 tokens x 64 heads, one layer, "
+                       "e4m3fn cache [512, 64, 576]"}
+    # fp8: a plain cast of the query / key / V (no scales, as the chunked
+    # pack's op); fp8_scaled: with per-tensor q / k / v scales (exact x / scale)
+    for name, fp8, scaled in (("fp8", True, False), ("fp8_scaled", True, True),
+                              ("bf16", False, False)):
+        odt = torch.uint8 if fp8 else torch.bfloat16
+        qo = torch.empty(T, H, 192, dtype=odt, device=dev)
+        ko = torch.empty(T, H, 192, dtype=odt, device=dev)
+        kw = dict(v=kvb[:, :, 128:], v_out=torch.empty(T, H, 128, dtype=torch.uint8, device=dev),
+                  mode=mk.MLA_PACK_KEY_V_FP8) if fp8 else {}
+        if scaled:
+            kw.update(q_scale=d["q_scale"], k_scale=d["k_scale"], v_scale=d["v_scale"])
+        cache = d["cache"]
+
+        def run():
+            mk.mla_new_token_epilogue(q[:, :, :128], q[:, :, 128:], kvb[:, :, :128], kv[:, :R],
+                                      kv[:, R:], d["positions"], cs, qo, ko, cache=cache,
+                                      slot_mapping=d["slots"], kv_cache_dtype="fp8",
+                                      cache_scale=d["cache_scale"], **kw)
+
+        us = kernel_us(torch, mk, run, flush)
+        nb = new_token_bytes(T, H, fp8, valid)
+        out[name] = {"us": round(us, 2), "bytes": nb, "GBps": round(nb / us / 1e3, 1),
+                     "frac_of_peak": round(nb / us / 1e3 / HBM_PEAK_GBS, 4)}
+    return out
+
+
 def projection_component(torch, mk, dev, flush):
     from fp8_paged_insert_amd import synth
 
@@ -588,6 +641,7 @@ def main():
                  "context_epilogue": epilogue_component(torch, mk, dev, flush),
                  "cache_dtypes": cache_dtype_component(torch, mk, dev, flush),
                  "chunk_merge": merge_component(torch, mk, dev, flush),
+                 "new_token_epilogue": new_token_component(torch, mk, dev, flush),
                  "context_kv_proj": projection_component(torch, mk, dev, flush)}
         result["components"] = comps
     if not args.no_cpu_baseline:

@@ -35,6 +35,7 @@ from ._binding import (  # noqa: F401
     mla_ctx_latent_gather,
     mla_ctx_merge_chunk,
     mla_ctx_neutralize_partials,
+    mla_new_token_epilogue,
     mla_kv_insert_grouped,
     mla_rope_cos_sin_cache,
     parse_kv_cache_dtype,

@@ -42,7 +42,7 @@ EXPORTS = (
     "mla_last_error", "mla_version", "mla_parse_kv_cache_dtype", "mla_set_launch_events",
     "mla_kv_insert_grouped", "mla_rope_cos_sin_cache", "mla_ctx_kv_epilogue",
     "mla_ctx_kv_proj", "mla_ctx_latent_gather", "mla_ctx_kv_pack",
-    "mla_ctx_merge_chunk", "mla_ctx_neutralize_partials",
+    "mla_ctx_merge_chunk", "mla_ctx_neutralize_partials", "mla_new_token_epilogue",
 )
 
 
@@ -75,6 +75,11 @@ _SIGS = {
                                    _i64, _i64, _i64, _i64, _i64, _i32, _vp]),
     "mla_ctx_neutralize_partials": (_i32, [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64,
                                            _i64, _vp]),
+    "mla_new_token_epilogue": (_i32, [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp,
+                                      _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _i64,
+                                      _i64, _i64, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp,
+                                      _vp, _vp, _vp, _i32, _vp, _vp, _i64, _i64, _i64, _i64,
+                                      _vp]),
 }
 
 _lib = None
@@ -493,6 +498,102 @@ def mla_ctx_kv_pack(k_nope, k_pe, key_out, v=None, v_out=None, mode=MLA_PACK_KEY
         vts, vhs, T, H, nope, rope, vd, int(mode), src, _ptr(k_scale), _ptr(v_scale),
         _ptr(key_out), _ptr(v_out), int(max_blocks), _stream(k_nope))
     _check(st, "mla_ctx_kv_pack")
+
+
+# ------------------------------------------------------ new-token epilogue --
+def mla_new_token_epilogue(q_nope, q_pe, k_nope, kv_c, k_pe, positions, cos_sin, q_out, key_out,
+                           v=None, v_out=None, mode=MLA_PACK_KEY_BF16, q_scale=None,
+                           k_scale=None, v_scale=None, cache=None, slot_mapping=None,
+                           kv_cache_dtype="auto", cache_scale=None, max_blocks=0):
+    """RoPE of q_pe / k_pe, the query row [q_nope | RoPE(q_pe)], the full key
+    [k_nope | RoPE(k_pe)] (+ fp8 V), and the insert of [kv_c | RoPE(k_pe)]
+    into one layer's paged cache [num_blocks, block_size, >= R + rope].
+
+    q_nope / q_pe / k_nope / v: bf16 [T, H, d] views with contiguous rows;
+    kv_c / k_pe: bf16 [T, d] views; positions int64 [T]; cos_sin fp32
+    [max_pos, rope] (mla_rope_cos_sin_cache).  q_out / key_out [T, H, nope+rope]
+    and v_out [T, H, vdim] contiguous: bf16 in KEY_BF16 mode, fp8 e4m3fn
+    (uint8 or float8_e4m3fn) in KEY_V_FP8 mode.  cache=None skips the insert.
+    """
+    for t_, n in ((q_nope, "q_nope"), (q_pe, "q_pe"), (k_nope, "k_nope"), (kv_c, "kv_c"),
+                  (k_pe, "k_pe")):
+        _need(t_, (torch.bfloat16,), n)
+        if t_.shape[-1] > 1 and t_.stride(-1) != 1:
+            raise RuntimeError(f"{n} innermost dimension must be contiguous")
+        _same_device(t_, q_nope, n, "q_nope")
+    if k_pe.dim() == 3:  # [T, 1, rope]
+        k_pe = k_pe.reshape(k_pe.shape[0], k_pe.shape[-1])
+    T, H, nope = q_nope.shape
+    rope = q_pe.shape[2]
+    if tuple(q_pe.shape[:2]) != (T, H) or tuple(k_nope.shape) != (T, H, nope):
+        raise RuntimeError("q_pe / k_nope must be [T, H, d] like q_nope")
+    if kv_c.dim() != 2 or kv_c.shape[0] != T or tuple(k_pe.shape) != (T, rope):
+        raise RuntimeError("kv_c must be [T, R] and k_pe [T, rope]")
+    R = kv_c.shape[1]
+    _need(positions, (torch.int64,), "positions")
+    if positions.numel() != T or not positions.is_contiguous():
+        raise RuntimeError("positions must be a contiguous int64 [T] tensor")
+    _need(cos_sin, (torch.float32,), "cos_sin")
+    if cos_sin.dim() != 2 or cos_sin.shape[1] != rope or not cos_sin.is_contiguous():
+        raise RuntimeError(f"cos_sin must be a contiguous fp32 [max_pos, {rope}] table")
+    for t_, n in ((positions, "positions"), (cos_sin, "cos_sin"), (q_out, "q_out"),
+                  (key_out, "key_out")):
+        _same_device(t_, q_nope, n, "q_nope")
+    for t_, n in ((q_out, "q_out"), (key_out, "key_out")):
+        if not t_.is_contiguous() or tuple(t_.shape) != (T, H, nope + rope):
+            raise RuntimeError(f"{n} must be contiguous [{T}, {H}, {nope + rope}]")
+    vd = vts = vhs = 0
+    if mode == MLA_PACK_KEY_BF16:
+        _need(q_out, (torch.bfloat16,), "q_out")
+        _need(key_out, (torch.bfloat16,), "key_out")
+        if any(x is not None for x in (v, v_out, q_scale, k_scale, v_scale)):
+            raise RuntimeError("the bf16 mode takes no v, v_out or query/key/V scales")
+    elif mode == MLA_PACK_KEY_V_FP8:
+        _need(q_out, _FP8_VIEWS, "q_out")
+        _need(key_out, _FP8_VIEWS, "key_out")
+        _need(v, (torch.bfloat16,), "v")
+        _need(v_out, _FP8_VIEWS, "v_out")
+        if tuple(v.shape[:2]) != (T, H) or (v.shape[2] > 1 and v.stride(2) != 1):
+            raise RuntimeError("v must be a [T, H, vdim] view with contiguous rows")
+        vd, vts, vhs = v.shape[2], v.stride(0), v.stride(1)
+        if not v_out.is_contiguous() or tuple(v_out.shape) != (T, H, vd):
+            raise RuntimeError(f"v_out must be contiguous [{T}, {H}, {vd}]")
+        _same_device(v, q_nope, "v", "q_nope")
+        _same_device(v_out, q_nope, "v_out", "q_nope")
+        for sc, n in ((q_scale, "q_scale"), (k_scale, "k_scale"), (v_scale, "v_scale")):
+            if sc is not None:
+                _check_scales(sc, 1, q_nope, n)
+    else:
+        raise RuntimeError(f"unknown new-token mode {mode}")
+    dt = _cache_dtype_code(kv_cache_dtype)
+    bs = bst = est = 0
+    if cache is not None:
+        _need(cache, _FP8_TENSOR_DTYPES.get(dt, (torch.bfloat16,)), "cache")
+        if cache.dim() != 3 or cache.shape[2] < R + rope or cache.stride(2) != 1:
+            raise RuntimeError(f"cache must be [num_blocks, block_size, >= {R + rope}] with "
+                               "contiguous entries")
+        _same_device(cache, q_nope, "cache", "q_nope")
+        _need(slot_mapping, (torch.int64,), "slot_mapping")
+        if slot_mapping.numel() != T or not slot_mapping.is_contiguous():
+            raise RuntimeError("slot_mapping must be a contiguous int64 [T] tensor")
+        _same_device(slot_mapping, q_nope, "slot_mapping", "q_nope")
+        if _is_fp8(dt):
+            if cache_scale is None:
+                raise RuntimeError("an fp8 cache requires cache_scale")
+            _check_scales(cache_scale, 1, q_nope, "cache_scale")
+        elif cache_scale is not None:
+            raise RuntimeError("a bf16 cache does not use cache_scale")
+        bs, bst, est = cache.shape[1], cache.stride(0), cache.stride(1)
+    elif slot_mapping is not None or cache_scale is not None:
+        raise RuntimeError("slot_mapping / cache_scale given without a cache")
+    st = lib().mla_new_token_epilogue(
+        _ptr(q_nope), q_nope.stride(0), q_nope.stride(1), _ptr(q_pe), q_pe.stride(0),
+        q_pe.stride(1), _ptr(k_nope), k_nope.stride(0), k_nope.stride(1), _ptr(v), vts, vhs,
+        _ptr(kv_c), kv_c.stride(0), _ptr(k_pe), k_pe.stride(0), _ptr(positions), _ptr(cos_sin),
+        cos_sin.shape[0], T, H, nope, rope, vd, R, int(mode), _ptr(q_scale), _ptr(k_scale),
+        _ptr(v_scale), _ptr(q_out), _ptr(key_out), _ptr(v_out), _ptr(cache), dt,
+        _ptr(cache_scale), _ptr(slot_mapping), bs, bst, est, int(max_blocks), _stream(q_nope))
+    _check(st, "mla_new_token_epilogue")
 
 
 # ------------------------------------------------------------ chunk merge --

@@ -9,6 +9,8 @@
  *   gather      mla_ctx_latent_gather  paged cache rows -> contiguous bf16 (or raw fp8) workspace
  *   pack        mla_ctx_kv_pack        [k_nope | k_pe] full key (+ fp8 V), contiguous
  *   merge       mla_ctx_merge_chunk    chunk attention partials -> accumulator (log-sum-exp)
+ *   new tokens  mla_new_token_epilogue RoPE(q_pe, k_pe) -> query row, full key (+ fp8 V),
+ *                                      and the cache insert of [kv_c | RoPE(k_pe)]
  *
  * Pages cited (title and section heading):
  *   [P1] "PR #51772 完整报告" -- [Attention][MLA] Fuse Kimi-K3 chunked-context K/V packing
@@ -324,6 +326,56 @@ int32_t mla_ctx_neutralize_partials(void* out, int64_t out_tok_stride, int64_t o
                                     float* lse, int64_t lse_head_stride, int64_t lse_tok_stride,
                                     const uint8_t* no_context, int64_t num_tokens,
                                     int64_t num_heads, int64_t head_dim, mla_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * mla_new_token_epilogue -- the new-token counterpart of the chunked-context
+ * pack, for one layer's prefill tokens ([P1] 功能与动机: the new-token epilogue
+ * already quantises the query; 关键源码片段, fused_mla_key_concat_kv_cache.py:
+ * the chunked-context pack is fused_mla_key_concat_kv_cache_insert without
+ * the query, without the cache insert and without RoPE).  The pages name the
+ * op only; this entry point is that reading, with every step done as
+ * elsewhere in this library:
+ *   pe_q = RoPE(q_pe[t, h, :], pos[t]),  pe_k = RoPE(k_pe[t, :], pos[t])
+ *            (half-split rotation, angles from cos_sin as in
+ *            mla_ctx_kv_epilogue; fp32 math, each result rounded to bf16)
+ *   q_out[t, h, :]   = [q_nope[t, h, :] | pe_q]
+ *   key_out[t, h, :] = [k_nope[t, h, :] | pe_k]     (same pe_k for every head)
+ *   v_out[t, h, :]   = v[t, h, :]                    (KEY_V_FP8 only)
+ *   cache entry slot_mapping[t] = [kv_c[t, :] | pe_k] (as mla_kv_insert_grouped
+ *            with one layer; slot < 0 skips the token; cache NULL skips the insert)
+ * mode KEY_BF16:  q_out / key_out bf16 [T, H, nope+rope] contiguous; v, v_out
+ *   and q/k/v scales must be NULL.
+ * mode KEY_V_FP8: q_out / key_out / v_out e4m3fn codes, each bf16 value x
+ *   (for the rope parts, the rounded rotation) becomes e4m3fn(fl32(x) / scale),
+ *   RNE, saturating at +-448; q_scale / k_scale / v_scale are device fp32 [1],
+ *   or NULL for 1.0.
+ * Inputs are bf16 device views: [t, h, i] at t*tok_stride + h*head_stride + i
+ *   (q_nope, q_pe, k_nope, v), [t, i] at t*tok_stride + i (kv_c, k_pe).
+ * positions   device int64 [T], each in [0, max_pos) (precondition; values
+ *             outside are clamped to that range).
+ * cos_sin     device fp32 [max_pos, rope] = cos of the rope/2 angles | their
+ *             sin (mla_rope_cos_sin_cache fills it).
+ * cache       device; element type from cache_dtype (AUTO/BF16, FP8_E4M3,
+ *             FP8_E5M2); cache_scale device fp32 [1] for an fp8 cache, NULL
+ *             for bf16; slot_mapping device int64 [T] with distinct
+ *             non-negative slots inside the cache, or -1 (precondition).
+ * rope must be 64; nope, vdim and kv_lora_rank multiples
+ * of 16; addresses and strides (in bytes) 16-byte aligned.  num_heads may be
+ * 0 (cache insert only).  max_blocks caps the grid (0 = one item per thread);
+ * the kernel loops grid-stride.  Host-side validation happens before any
+ * launch, so a rejected call writes nothing.
+ * ------------------------------------------------------------------------ */
+int32_t mla_new_token_epilogue(
+    const void* q_nope, int64_t qn_tok_stride, int64_t qn_head_stride, const void* q_pe,
+    int64_t qp_tok_stride, int64_t qp_head_stride, const void* k_nope, int64_t kn_tok_stride,
+    int64_t kn_head_stride, const void* v, int64_t v_tok_stride, int64_t v_head_stride,
+    const void* kv_c, int64_t kv_c_tok_stride, const void* k_pe, int64_t k_pe_tok_stride,
+    const int64_t* positions, const float* cos_sin, int64_t max_pos, int64_t num_tokens,
+    int64_t num_heads, int64_t nope, int64_t rope, int64_t vdim, int64_t kv_lora_rank,
+    int32_t mode, const float* q_scale, const float* k_scale, const float* v_scale,
+    void* q_out, void* key_out, void* v_out, void* cache, int32_t cache_dtype,
+    const float* cache_scale, const int64_t* slot_mapping, int64_t block_size,
+    int64_t block_stride, int64_t entry_stride, int64_t max_blocks, mla_stream_t stream);
 
 #ifdef __cplusplus
 }

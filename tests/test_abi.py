@@ -220,3 +220,54 @@ def test_merge_and_neutralize_zero_sizes_are_noops(mk):
                                                 None) == mk.MLA_OK
     assert mk.lib().mla_ctx_neutralize_partials(P16, 8192, 128, P16, 16384, 1, None, 5, 64, 128,
                                                 None) == mk.MLA_ERR_INVALID_ARGUMENT
+
+
+def new_token_call(mk, **kw):
+    a = dict(qn=P16, qn_ts=64 * 192, qn_hs=192, qp=P16, qp_ts=64 * 192, qp_hs=192, kn=P16,
+             kn_ts=16384, kn_hs=256, v=P16, v_ts=16384, v_hs=256, kvc=P16, kvc_ts=576, kpe=P16,
+             kpe_ts=576, pos=P16, cs=P16, maxpos=16384, T=8192, H=64, nope=128, rope=64,
+             vdim=128, R=512, mode=mk.MLA_PACK_KEY_V_FP8, qs=None, ks=None, vs=None, qo=P16,
+             ko=P16, vo=P16, cache=P16, dt=mk.MLA_KV_FP8_E4M3, cscale=P16, slots=P16, bs=64,
+             bstride=64 * 576, estride=576, maxb=0)
+    a.update(kw)
+    return mk.lib().mla_new_token_epilogue(
+        a["qn"], a["qn_ts"], a["qn_hs"], a["qp"], a["qp_ts"], a["qp_hs"], a["kn"], a["kn_ts"],
+        a["kn_hs"], a["v"], a["v_ts"], a["v_hs"], a["kvc"], a["kvc_ts"], a["kpe"], a["kpe_ts"],
+        a["pos"], a["cs"], a["maxpos"], a["T"], a["H"], a["nope"], a["rope"], a["vdim"], a["R"],
+        a["mode"], a["qs"], a["ks"], a["vs"], a["qo"], a["ko"], a["vo"], a["cache"], a["dt"],
+        a["cscale"], a["slots"], a["bs"], a["bstride"], a["estride"], a["maxb"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(mode=2), 1, "KEY_BF16 or KEY_V_FP8"),
+    (dict(mode=0), 1, "takes no v"),
+    (dict(T=-1), 1, "negative"),
+    (dict(maxb=-1), 1, "negative"),
+    (dict(cscale=None), 1, "needs kv_scales"),
+    (dict(dt=1), 1, "takes no kv_scales"),
+    (dict(dt=9), 1, "unknown KV cache dtype"),
+    (dict(slots=None), 1, "needs slot_mapping"),
+    (dict(bs=0), 1, "positive"),
+    (dict(estride=560), 1, "wider than entry_stride"),
+    (dict(cache=None), 1, "without a cache"),
+    (dict(rope=48), 2, "rope must be 64"),
+    (dict(rope=32), 2, "rope must be 64"),
+    (dict(nope=120), 2, "multiples of 16"),
+    (dict(pos=None), 1, "positions"),
+    (dict(maxpos=0), 1, "max_pos"),
+    (dict(qo=None), 1, "NULL input or output"),
+    (dict(vo=None), 1, "NULL input or output"),
+    (dict(kvc=None), 1, "NULL kv_c"),
+    (dict(qp_hs=193), 3, "multiples of 16 bytes"),
+    (dict(kpe=P_ODD), 3, "multiples of 16 bytes"),
+    (dict(dt=1, cscale=None, estride=580), 3, "multiples of 16 bytes"),
+])
+def test_new_token_rejects_bad_arguments(mk, kw, status, msg):
+    assert new_token_call(mk, **kw) == status
+    assert msg in mk.last_error()
+
+
+def test_new_token_zero_tokens_is_a_noop(mk):
+    assert new_token_call(mk, T=0) == mk.MLA_OK
+    assert new_token_call(mk, T=0, mode=mk.MLA_PACK_KEY_BF16, v=None, vo=None) == mk.MLA_OK
+    assert new_token_call(mk, T=0, cache=None, cscale=None, slots=None) == mk.MLA_OK
