@@ -299,9 +299,10 @@ def small_batch(torch, mk, dev):
             "bytes": insert_bytes(L, 4, valid_rows=15)}
 
 
-def kernel_us(torch, mk, fn, flush, reps=22, warm=3):
-    """Median duration of the one kernel fn launches, bracketed by events the
-    kernel itself records (mla_set_launch_events), after a cache flush."""
+def kernel_us(torch, mk, fn, flush, reps=100, warm=10):
+    """Median and 90th-percentile duration of the one kernel fn launches,
+    bracketed by events the kernel itself records (mla_set_launch_events),
+    each launch after a cache flush (10 untimed launches first)."""
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()            # torch creates the events on first record
@@ -315,7 +316,16 @@ def kernel_us(torch, mk, fn, flush, reps=22, warm=3):
         e1.synchronize()
         if i >= warm:
             times.append(e0.elapsed_time(e1) * 1e3)
-    return statistics.median(times)
+    times.sort()
+    return statistics.median(times), times[min(len(times) - 1, int(0.9 * len(times)))]
+
+
+def rate(us, p90, nbytes):
+    """Component line: median and p90 microseconds, bytes, median GB/s and
+    fraction of the HBM peak."""
+    return {"us": round(us, 2), "p90_us": round(p90, 2), "bytes": nbytes,
+            "GBps": round(nbytes / us / 1e3, 1),
+            "frac_of_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
 
 
 def context_pack_component(torch, mk, dev, flush):
@@ -361,9 +371,8 @@ def context_pack_component(torch, mk, dev, flush):
                              ("pack_fp8_kpe_raw", pack8_raw, pack_fp8_kpe_raw_bytes(8192, 64)),
                              ("pack_fp8_fp16_inputs", pack8_f16, pack_fp8_bytes(8192, 64)),
                              ("pack_bf16", packb, pack_bf16_bytes(8192, 64))):
-        us = kernel_us(torch, mk, fn, flush)
-        out[name] = {"us": round(us, 2), "bytes": nbytes, "GBps": round(nbytes / us / 1e3, 1),
-                     "frac_of_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+        us, p90 = kernel_us(torch, mk, fn, flush)
+        out[name] = rate(us, p90, nbytes)
     return out
 
 
@@ -380,11 +389,9 @@ def epilogue_component(torch, mk, dev, flush):
         mk.mla_ctx_kv_epilogue(d["all_kv"], d["gamma"], d["eps"], d["positions"], cs, ptrs,
                                d["slot_mapping"], 64, 64 * W, W, d["scales"], "fp8")
 
-    us = kernel_us(torch, mk, epi, flush)
-    nb = epilogue_bytes(L, T)
+    us, p90 = kernel_us(torch, mk, epi, flush)
     res = {"workload": "context-KV epilogue, 5 layers x 4096 tokens (norm+rope+fp8+scatter)",
-           "us": round(us, 2), "bytes": nb, "GBps": round(nb / us / 1e3, 1),
-           "frac_of_peak": round(nb / us / 1e3 / HBM_PEAK_GBS, 4)}
+           **rate(us, p90, epilogue_bytes(L, T))}
     return res
 
 
@@ -411,10 +418,8 @@ def cache_dtype_component(torch, mk, dev, flush):
 
         for kind, fn, nbytes in (("insert", ins, insert_bytes(L, T)),
                                  ("gather", gat, gather_bytes(8192))):
-            us = kernel_us(torch, mk, fn, flush)
-            out[f"{kind}_{name}"] = {"us": round(us, 2), "bytes": nbytes,
-                                     "GBps": round(nbytes / us / 1e3, 1),
-                                     "frac_of_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+            us, p90 = kernel_us(torch, mk, fn, flush)
+            out[f"{kind}_{name}"] = rate(us, p90, nbytes)
     return out
 
 
@@ -432,12 +437,10 @@ def merge_component(torch, mk, dev, flush):
     def merge():
         mk.mla_ctx_merge_chunk(acc, lacc, part, plse, mk.MLA_MERGE_ACCUMULATE)
 
-    us = kernel_us(torch, mk, merge, flush)
-    nb = merge_bytes(T, H, D)
+    us, p90 = kernel_us(torch, mk, merge, flush)
     return {"workload": "merge of one chunk partial into the accumulator, 16384 tokens x 64 "
                         "heads x 128 (bf16 outputs, fp32 lse)",
-            "us": round(us, 2), "bytes": nb, "GBps": round(nb / us / 1e3, 1),
-            "frac_of_peak": round(nb / us / 1e3 / HBM_PEAK_GBS, 4)}
+            **rate(us, p90, merge_bytes(T, H, D))}
 
 
 def new_token_component(torch, mk, dev, flush):
@@ -474,10 +477,8 @@ def new_token_component(torch, mk, dev, flush):
                                       slot_mapping=d["slots"], kv_cache_dtype="fp8",
                                       cache_scale=d["cache_scale"], **kw)
 
-        us = kernel_us(torch, mk, run, flush)
-        nb = new_token_bytes(T, H, fp8, valid)
-        out[name] = {"us": round(us, 2), "bytes": nb, "GBps": round(nb / us / 1e3, 1),
-                     "frac_of_peak": round(nb / us / 1e3 / HBM_PEAK_GBS, 4)}
+        us, p90 = kernel_us(torch, mk, run, flush)
+        out[name] = rate(us, p90, new_token_bytes(T, H, fp8, valid))
     return out
 
 
@@ -489,7 +490,7 @@ def projection_component(torch, mk, dev, flush):
     w_nk = synth.bf16_normal((7168, L * W), g, dev, std=0.02).t().contiguous()
     y = torch.empty(4096, L * W, dtype=torch.bfloat16, device=dev)
     try:
-        us = kernel_us(torch, mk, lambda: mk.mla_ctx_kv_proj(x, w_nk, y), flush)
+        us, p90 = kernel_us(torch, mk, lambda: mk.mla_ctx_kv_proj(x, w_nk, y), flush)
     except mk.MlaError as e:
         return {"workload": "context_kv_proj 4096x7168 . 7168x2880", "status": str(e)}
     # the vendor library GEMM on the same operands, for context (torch.matmul
@@ -507,7 +508,7 @@ def projection_component(torch, mk, dev, flush):
             ref.append(e0.elapsed_time(e1) * 1e3)
     flops = 2 * 4096 * 7168 * L * W
     return {"workload": "context_kv_proj 4096x7168 . 7168x2880 (bf16 MFMA, fp32 acc)",
-            "us": round(us, 2), "TFLOPs": round(flops / us / 1e6, 1),
+            "us": round(us, 2), "p90_us": round(p90, 2), "TFLOPs": round(flops / us / 1e6, 1),
             "frac_of_peak": round(flops / us / 1e6 / 2500.0, 4),
             "torch_matmul_us_stream_events": round(statistics.median(ref), 2)}
 

@@ -1,0 +1,48 @@
+"""CPU checks of bench.py's contract: the algorithmic byte counts it divides
+by are the figures derived from the workloads' shapes, and a request for more
+than one GPU is refused before anything touches a device."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+@pytest.mark.parametrize("fn,args,want", [
+    # fp8 pack of 8192 tokens x 64 heads: k_nope + v read (2 x 128 bf16), k_pe read once per
+    # token (64 bf16); key (192 codes) and V (128 codes) written
+    (bench.pack_fp8_bytes, (8192, 64), 8192 * 64 * (512 + 192 + 128) + 8192 * 128),
+    (bench.pack_bf16_bytes, (8192, 64), 8192 * 64 * (256 + 384) + 8192 * 128),
+    # gather: 576 codes read, 576 bf16 written, one int64 slot per token, the fp32 scale
+    (bench.gather_bytes, (8192,), 8192 * (576 + 1152 + 8) + 4),
+    # merge: accumulator read + write and the partial read (bf16 rows), three fp32 lse
+    (bench.merge_bytes, (16384, 64), 16384 * 64 * (3 * 256 + 3 * 4)),
+])
+def test_byte_formulas(fn, args, want):
+    assert fn(*args) == want
+
+
+def test_long_context_insert_bytes_match_the_workload():
+    # 5 layers x 16384 rows: bf16 kv_c + k_pe read (1152 B), one slot each, 576 codes
+    # written per row, plus the per-layer pointer and scale
+    assert bench.insert_bytes(5, 16384) == 5 * 16384 * (1152 + 8 + 576) + 5 * 12
+
+
+def test_new_token_bytes_are_mode_specific_sums():
+    T, H = 8192, 64
+    fp8 = T * H * (384 + 256 + 256 + 192 + 192 + 128) + T * (1152 + 8 + 8 + 256) + (T - 1) * 576
+    bf16 = T * H * (384 + 256 + 384 + 384) + T * (1152 + 8 + 8 + 256) + (T - 1) * 576
+    assert bench.new_token_bytes(T, H, True, T - 1) == fp8
+    assert bench.new_token_bytes(T, H, False, T - 1) == bf16
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
