@@ -271,3 +271,24 @@ def test_new_token_zero_tokens_is_a_noop(mk):
     assert new_token_call(mk, T=0) == mk.MLA_OK
     assert new_token_call(mk, T=0, mode=mk.MLA_PACK_KEY_BF16, v=None, vo=None) == mk.MLA_OK
     assert new_token_call(mk, T=0, cache=None, cscale=None, slots=None) == mk.MLA_OK
+
+
+def test_sizes_beyond_one_launch_are_refused_before_launching(mk):
+    """Every entry point indexes with 32-bit work-item counters; sizes past
+    that are rejected on the host with UNSUPPORTED (nothing is launched)."""
+    big = 1 << 31
+    assert insert_call(mk, T=big) == mk.MLA_ERR_UNSUPPORTED
+    assert "exceed one launch" in mk.last_error()
+    assert pack_call(mk, T=1 << 27) == mk.MLA_ERR_UNSUPPORTED
+    assert "split the chunk" in mk.last_error()
+    assert gather_call(mk, T=big // 36 + 1) == mk.MLA_ERR_UNSUPPORTED
+    assert "too many tokens" in mk.last_error()
+    assert merge_call(mk, T=1 << 25) == mk.MLA_ERR_UNSUPPORTED
+    assert "too many rows" in mk.last_error()
+    assert new_token_call(mk, T=1 << 21) == mk.MLA_ERR_UNSUPPORTED
+    assert "split the batch" in mk.last_error()
+    assert mk.lib().mla_ctx_kv_proj(P16, 7168, big, 7168, P16, 2880, P16, 2880,
+                                    None) == mk.MLA_ERR_UNSUPPORTED
+    assert "beyond 2^31" in mk.last_error()
+    # just inside the limits the same calls pass validation (T = 0 variants are no-ops)
+    assert pack_call(mk, T=0) == mk.MLA_OK
