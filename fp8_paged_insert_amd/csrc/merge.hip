@@ -46,6 +46,14 @@ struct MergeArgs {
   uint32_t chunks;  // 16-byte chunks per row (head_dim / 8)
 };
 
+// 16-byte load that does not keep its line in the caches: a chunk's partial
+// is read once (126 -> 124.5 us at 16384 x 64 x 128); the accumulator, read
+// and written back, keeps ordinary loads.
+__device__ __forceinline__ uint4 ld16_once(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // bf16 pair -> weighted fp32 sum -> bf16 pair, skipping a term whose weight
 // is exactly zero (that partial covers no key; its values may be anything).
 __device__ __forceinline__ uint32_t merge2(uint32_t a, uint32_t b, float ca, float cb,
@@ -94,7 +102,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
     const bool use_a = wa != 0.0f, use_b = wb != 0.0f;
     for (uint32_t c = j; c < a.chunks; c += kRowLanes) {
       const uint4 x = ld16(o + 8 * c);
-      const uint4 y = ld16(p + 8 * c);
+      const uint4 y = ld16_once(p + 8 * c);
       st16(o + 8 * c, make_uint4(merge2(x.x, y.x, ca, cb, use_a, use_b),
                                  merge2(x.y, y.y, ca, cb, use_a, use_b),
                                  merge2(x.z, y.z, ca, cb, use_a, use_b),
