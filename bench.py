@@ -506,11 +506,31 @@ def projection_component(torch, mk, dev, flush):
         e1.synchronize()
         if i >= 3:
             ref.append(e0.elapsed_time(e1) * 1e3)
+    # end to end: the projection, then the epilogue reading its output as
+    # [T, L, 576] and inserting into 5 fp8 caches (stream events around both)
+    e = synth.context_epilogue(dev, with_gemm=False)
+    cs = torch.empty(4096, P, dtype=torch.float32, device=dev)
+    mk.mla_rope_cos_sin_cache(cs, 4096, P, 10000.0)
+    ptrs = mk.cache_ptr_table(e["caches"])
+    e2e = []
+    for i in range(25):
+        flush_llc(torch, flush)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        mk.mla_ctx_kv_proj(x, w_nk, y)
+        mk.mla_ctx_kv_epilogue(y.view(4096, L, W), e["gamma"], e["eps"], e["positions"], cs,
+                               ptrs, e["slot_mapping"], 64, 64 * W, W, e["scales"], "fp8")
+        e1.record()
+        e1.synchronize()
+        if i >= 3:
+            e2e.append(e0.elapsed_time(e1) * 1e3)
     flops = 2 * 4096 * 7168 * L * W
     return {"workload": "context_kv_proj 4096x7168 . 7168x2880 (bf16 MFMA, fp32 acc)",
             "us": round(us, 2), "p90_us": round(p90, 2), "TFLOPs": round(flops / us / 1e6, 1),
             "frac_of_peak": round(flops / us / 1e6 / 2500.0, 4),
-            "torch_matmul_us_stream_events": round(statistics.median(ref), 2)}
+            "torch_matmul_us_stream_events": round(statistics.median(ref), 2),
+            "with_epilogue_us_stream_events": round(statistics.median(e2e), 2)}
 
 
 # ----------------------------------------------------------- CPU baseline --
