@@ -333,13 +333,20 @@ extern "C" int32_t mla_new_token_epilogue(
   a.kv_lora_rank = static_cast<uint32_t>(kv_lora_rank);
   a.rows = static_cast<uint32_t>(rows);
   a.tasks = static_cast<uint32_t>(tasks);
+  // Default grid: one 16-lane row per task, except for scaled fp8 outputs,
+  // where every wavefront first computes three reciprocals of the scales by
+  // IEEE division; 4 workgroups per CU looping over the tasks pay that once
+  // per ~30 tasks (8192 x 64: 158.7 -> 141.4 us; unscaled, the full grid is
+  // faster: 131 vs 135 us).
+  const bool scaled = fp8 && (q_scale || k_scale || v_scale);
   const int64_t full = ceil_div(tasks * kLanes, 256);
-  const dim3 g(max_blocks > 0 ? std::min(full, max_blocks) : full), b(256);
+  const int64_t dflt = scaled ? std::min(full, int64_t(4) * cu_count()) : full;
+  const dim3 g(max_blocks > 0 ? std::min(full, max_blocks) : dflt), b(256);
   const int fmt = cache ? cache_fmt(cache_dtype) : kFmtBf16;
   auto s = static_cast<hipStream_t>(stream);
   if (!fp8)
     launch_new_token<false, false>(fmt, g, b, s, a);
-  else if (q_scale || k_scale || v_scale)
+  else if (scaled)
     launch_new_token<true, true>(fmt, g, b, s, a);
   else
     launch_new_token<true, false>(fmt, g, b, s, a);
