@@ -1,0 +1,104 @@
+"""Largest launches each entry point accepts: the work-item counters are 32-bit,
+so the pack, the gather and the merge are run with just under 2^31 items
+(85-105 GB of device memory each) and sampled outputs -- the first rows, the
+last rows and rows past 2^30 items -- are compared with the CPU oracle.  An
+index overflow anywhere in the item -> (token, head, chunk) -> address chain
+would put some of these rows in the wrong place.  Skipped when the device has
+not enough free memory.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import DEV, announce, requires_gpu, u16, u8
+from test_gpu_merge import merge_close
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+GB = 1 << 30
+
+
+def need(nbytes):
+    free, _ = torch.cuda.mem_get_info(DEV)
+    if free < nbytes + 8 * GB:
+        pytest.skip(f"needs {nbytes / GB:.0f} GiB free on the device, {free / GB:.0f} GiB free")
+
+
+def random_bits(shape, dtype):
+    """Random 16-bit patterns (bf16 view) or bytes, generated on the device."""
+    if dtype == torch.bfloat16:
+        return torch.randint(-32768, 32768, shape, dtype=torch.int16, device=DEV).view(dtype)
+    return torch.randint(0, 256, shape, dtype=torch.uint8, device=DEV)
+
+
+def sample(n, count, seed):
+    r = np.random.default_rng(seed)
+    idx = np.concatenate([np.arange(4), n - 1 - np.arange(4), r.integers(n // 2, n, count)])
+    return np.unique(idx)
+
+
+def test_pack_just_below_2_31_chunks(mk):
+    T, H = 1677721, 64                         # T * H * (12 + 8) = 2^31 - 768 chunks
+    assert T * H * 20 < (1 << 31)
+    need(T * H * (512 + 320) + T * 128)
+    announce("pack at the 2^31-chunk limit", T, H)
+    torch.manual_seed(11)
+    kvb = random_bits((T, H, 256), torch.bfloat16)
+    kpe = random_bits((T, 64), torch.bfloat16)
+    key = torch.empty(T, H, 192, dtype=torch.uint8, device=DEV)
+    v8 = torch.empty(T, H, 128, dtype=torch.uint8, device=DEV)
+    mk.mla_ctx_kv_pack(kvb[..., :128], kpe, key, v=kvb[..., 128:], v_out=v8,
+                       mode=mk.MLA_PACK_KEY_V_FP8)
+    torch.cuda.synchronize()
+    rows = torch.from_numpy(sample(T, 60, 1)).to(DEV)
+    kn = u16(kvb[rows])
+    rk, rv = oracle.pack(kn[..., :128], u16(kpe[rows]), kn[..., 128:], mode=oracle.PACK_KEY_V_FP8)
+    assert np.array_equal(u8(key[rows]), rk)
+    assert np.array_equal(u8(v8[rows]), rv)
+    del kvb, kpe, key, v8
+    torch.cuda.empty_cache()
+
+
+def test_gather_just_below_2_31_chunks(mk):
+    T = (1 << 31) // 36 - 1                    # 36 chunks of 16 codes per 576-byte row
+    nb = (T + 63) // 64
+    need(nb * 64 * 576 + T * (1152 + 8))
+    announce("gather at the 2^31-chunk limit", T)
+    torch.manual_seed(12)
+    cache = random_bits((nb, 64, 576), torch.uint8)
+    slots = torch.randperm(nb * 64, device=DEV)[:T].contiguous()
+    out = torch.empty(T, 576, dtype=torch.bfloat16, device=DEV)
+    scale = torch.tensor([0.625], dtype=torch.float32, device=DEV)
+    mk.mla_ctx_latent_gather(cache, slots, out, scale, "fp8")
+    torch.cuda.synchronize()
+    js = torch.from_numpy(sample(T, 60, 2)).to(DEV)
+    src = cache.view(nb * 64, 576)[slots[js]]                # the sampled rows, in order
+    mini = u8(src).reshape(-1, 1, 576)
+    ref = oracle.gather(mini, np.arange(mini.shape[0], dtype=np.int64), 0.625)
+    assert np.array_equal(u16(out[js]), ref)
+    del cache, slots, out
+    torch.cuda.empty_cache()
+
+
+def test_merge_just_below_2_31_rows(mk):
+    H, D = 64, 8
+    T = ((1 << 31) - 32) // H                  # T * H = 2^31 - 64 rows
+    need(2 * T * H * D * 2 + 2 * T * H * 4)
+    announce("merge at the 2^31-row limit", T, H, D)
+    torch.manual_seed(13)
+    acc = torch.randn(T, H, D, dtype=torch.bfloat16, device=DEV)
+    part = torch.randn(T, H, D, dtype=torch.bfloat16, device=DEV)
+    lse = 3.0 * torch.randn(H, T, device=DEV)
+    plse = 3.0 * torch.randn(H, T, device=DEV)
+    ts = torch.from_numpy(sample(T, 40, 3)).to(DEV)
+    a0, l0 = acc[ts].cpu(), lse[:, ts].cpu().numpy()
+    mk.mla_ctx_merge_chunk(acc, lse, part, plse, mk.MLA_MERGE_ACCUMULATE)
+    torch.cuda.synchronize()
+    p0, pl0 = part[ts].cpu(), plse[:, ts].cpu().numpy()
+    ro, rl = u16(a0).copy(), l0.copy()
+    oracle.merge_chunk(ro, rl, u16(p0), pl0, oracle.MERGE_ACCUMULATE)
+    merge_close(u16(acc[ts]), ro, a0, p0, l0, pl0)
+    assert np.allclose(lse[:, ts].cpu().numpy(), rl, rtol=1e-6, atol=1e-6)
+    del acc, part, lse, plse
+    torch.cuda.empty_cache()
