@@ -645,11 +645,13 @@ def main():
                   "µs/launch small batch",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16->fp8_e4m3 (fp32 math)",
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (seeded, generated on the device)",
         "config": {"workload": "long-context stress: grouped fp8 insert 5 layers x 16384 tokens "
                                "into [4096,64,576] caches + 16 chunks x 8192 tokens of fp8 gather "
                                "and fp8 full-key/V pack (64 heads, [8192,64,256] kv_b_proj output)",
+                   "io": "bf16 inputs, fp8 e4m3fn caches / keys / V, bf16 gather workspace; "
+                         "conversions computed in fp32",
                    "bytes_per_step": nbytes, "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
         "roofline": roofline,
     }
