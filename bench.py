@@ -364,13 +364,23 @@ def context_pack_component(torch, mk, dev, flush):
     def packb():
         mk.mla_ctx_kv_pack(kvb[..., :128], ws[:, 512:], keyb)
 
-    out = {"workload": "chunked-context pack, 8192 tokens x 64 heads"}
+    # one GPU's share under 8-way tensor parallelism: heads 0..7 of the same
+    # kv_b_proj output (a strided view), k_pe broadcast locally
+    key8_tp = torch.empty(8192, 8, 192, dtype=torch.uint8, device=dev)
+    v8_tp = torch.empty(8192, 8, 128, dtype=torch.uint8, device=dev)
+
+    def pack8_tp8():
+        mk.mla_ctx_kv_pack(kvb[:, :8, :128], ws[:, 512:], key8_tp, v=kvb[:, :8, 128:],
+                           v_out=v8_tp, mode=mk.MLA_PACK_KEY_V_FP8)
+
+    out = {"workload": "chunked-context pack, 8192 tokens x 64 heads (tp8 share: 8 heads)"}
     for name, fn, nbytes in (("gather", gather, gather_bytes(8192)),
                              ("gather_raw_fp8", gather_raw, gather_raw_bytes(8192)),
                              ("pack_fp8", pack8, pack_fp8_bytes(8192, 64)),
                              ("pack_fp8_kpe_raw", pack8_raw, pack_fp8_kpe_raw_bytes(8192, 64)),
                              ("pack_fp8_fp16_inputs", pack8_f16, pack_fp8_bytes(8192, 64)),
-                             ("pack_bf16", packb, pack_bf16_bytes(8192, 64))):
+                             ("pack_bf16", packb, pack_bf16_bytes(8192, 64)),
+                             ("pack_fp8_tp8_share", pack8_tp8, pack_fp8_bytes(8192, 8))):
         us, p90 = kernel_us(torch, mk, fn, flush)
         out[name] = rate(us, p90, nbytes)
     return out
