@@ -389,6 +389,8 @@ def mla_ctx_kv_proj(x, w_nk, y):
     N = w_nk.shape[0]
     if w_nk.shape[1] != K or tuple(y.shape) != (T, N):
         raise RuntimeError("shape mismatch: x [T, K], w_nk [N, K], y [T, N]")
+    if N > 1 and w_nk.stride(0) != K:
+        raise RuntimeError("w_nk must be a dense [N, K] weight (row stride K)")
     _same_device(w_nk, x, "w_nk", "x")
     _same_device(y, x, "y", "x")
     _check(lib().mla_ctx_kv_proj(_ptr(x), x.stride(0), T, K, _ptr(w_nk), N, _ptr(y),

@@ -205,8 +205,9 @@ int32_t mla_ctx_kv_epilogue(
  * hidden -> L * 576 instead of L projections hidden -> 2112).
  *   Y[t, n] = bf16( sum_k X[t, k] * W[n, k] )   fp32 accumulation (MFMA)
  * X device bf16 [T, K] row-major (row stride x_row_stride, elements).
- * W device bf16 [N, K] row-major: the linear layer's [out, in] weight
- *   storage, i.e. the transpose of the [K, N] matrix X is multiplied by.
+ * W device bf16 [N, K] row-major and dense (row stride K): the linear
+ *   layer's [out, in] weight storage, i.e. the transpose of the [K, N]
+ *   matrix X is multiplied by.
  * Y device bf16 [T, N] row-major (row stride y_row_stride).
  * K must be a multiple of 64 and N a multiple of 16; pointers and row
  * strides 16-byte aligned.  T may be any value >= 0.

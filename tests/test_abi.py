@@ -292,3 +292,14 @@ def test_sizes_beyond_one_launch_are_refused_before_launching(mk):
     assert "beyond 2^31" in mk.last_error()
     # just inside the limits the same calls pass validation (T = 0 variants are no-ops)
     assert pack_call(mk, T=0) == mk.MLA_OK
+
+
+def test_proj_binding_refuses_a_strided_weight(mk):
+    """The ABI takes W dense ([N, K], row stride K); a wider storage viewed as
+    [N, K] is refused by the binding instead of being read with the wrong stride."""
+    import torch
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    w = torch.zeros(32, 128, dtype=torch.bfloat16)[:, :64]
+    y = torch.zeros(4, 32, dtype=torch.bfloat16)
+    with pytest.raises(RuntimeError, match="row stride K"):
+        mk.mla_ctx_kv_proj(x, w, y)
