@@ -53,6 +53,7 @@ constexpr int kWBlocks = kBN / 8 / 4;  // and of W
 constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedLdsRead = 0x100;
 
 constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, one L2 each
+constexpr int kMaxLdsDevices = 64;  // devices whose LDS attribute is remembered
 constexpr int kGroupRows = 4;
 
 struct GemmArgs {
@@ -283,13 +284,18 @@ extern "C" int32_t mla_ctx_kv_proj(const void* X, int64_t x_row_stride, int64_t 
   a.tiles = static_cast<int32_t>(tiles);
   a.tiles_per_xcd = static_cast<int32_t>(ceil_div(tiles, kXcds));
   const int64_t grid = int64_t(a.tiles_per_xcd) * kXcds;
-  static bool attr_set = false;
-  if (!attr_set) {
+  // The LDS reservation is a per-device attribute of the kernel: set it once
+  // on each device the projection runs on.
+  static int attr_set[kMaxLdsDevices] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+    return fail(MLA_ERR_DEVICE, "%s: no current HIP device", fn);
+  if (dev >= kMaxLdsDevices || !__atomic_load_n(&attr_set[dev], __ATOMIC_ACQUIRE)) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kv_proj_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(kLdsBytes)) != hipSuccess)
       return fail(MLA_ERR_DEVICE, "%s: cannot reserve %zu bytes of LDS", fn, kLdsBytes);
-    attr_set = true;
+    if (dev < kMaxLdsDevices) __atomic_store_n(&attr_set[dev], 1, __ATOMIC_RELEASE);
   }
   launch(kv_proj_kernel, dim3(grid), dim3(kThreads), kLdsBytes,
                      static_cast<hipStream_t>(stream), a);
