@@ -136,12 +136,17 @@ _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream(t: torch.Tensor):
-    """torch's current HIP stream on the tensor's device (a hipStream_t)."""
+    """torch's current HIP stream on the tensor's device (a hipStream_t).  The
+    library launches on the calling thread's current device, so the tensors
+    must live there (select it with torch.cuda.device / set_device)."""
     if t.device.type != "cuda":
         raise RuntimeError(f"tensor on {t.device}, expected a GPU tensor")
+    cur = torch.cuda.current_device()
+    if t.device.index is not None and t.device.index != cur:
+        raise RuntimeError(f"tensors on {t.device} but the current device is cuda:{cur}; "
+                           f"call under torch.cuda.device({t.device.index})")
     if _raw_stream is not None:
-        return _raw_stream(t.device.index if t.device.index is not None else
-                           torch.cuda.current_device())
+        return _raw_stream(cur)
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
@@ -315,6 +320,9 @@ class PreparedInsert:
         self._fn = lib().mla_kv_insert_grouped
 
     def __call__(self):
+        if torch.cuda.current_device() != self._index:
+            raise RuntimeError(f"prepared on cuda:{self._index} but the current device is "
+                               f"cuda:{torch.cuda.current_device()}")
         self._args[-1] = (_raw_stream(self._index) if _raw_stream is not None else
                           torch.cuda.current_stream(self._index).cuda_stream)
         st = self._fn(*self._args)

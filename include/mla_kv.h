@@ -23,6 +23,10 @@
  *     marked "host".  Buffers must stay alive until the stream work is done.
  *   - All work is enqueued on `stream` (a hipStream_t; NULL = the null
  *     stream) and is asynchronous; nothing synchronises inside the library.
+ *     Kernels run on the calling thread's current HIP device: `stream` and
+ *     every device pointer must belong to it (the library reads the
+ *     device's compute-unit count, and sets the projection's LDS attribute,
+ *     on that device).
  *   - Strides are in ELEMENTS of the array they describe.
  *   - bf16 arrays hold IEEE bfloat16, fp16 arrays IEEE binary16; fp8 arrays
  *     hold OCP e4m3fn codes (bias 7, no infinity, NaN = 0x7F/0xFF, max 448)
