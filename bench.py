@@ -141,7 +141,7 @@ class LongContext:
         return (insert_bytes(L, self.T) + n * gather_bytes(self.chunk)
                 + n * pack_fp8_bytes(self.chunk, self.heads))
 
-    def step(self, time_pack=False):
+    def step(self, time_pack=False, max_blocks=0):
         """One pass over the workload, in order on the current stream.  (Issuing
         chunk c + 1's gather on a side stream during chunk c's pack measured
         slower on MI355X: the cross-stream waits cost more than they hide.)"""
@@ -153,7 +153,7 @@ class LongContext:
         for c, kvb in enumerate(self.kvb):
             mk.mla_ctx_latent_gather(self.ctx_cache,
                                      self.src_slots[c * self.chunk:(c + 1) * self.chunk],
-                                     self.ws, self.ctx_scale, "fp8")
+                                     self.ws, self.ctx_scale, "fp8", max_blocks=max_blocks)
             if time_pack and c == self.timed_chunk:
                 # events recorded by the pack kernel itself as it starts and ends
                 # (one chunk per step, rotating, so arming them costs the step
@@ -162,7 +162,7 @@ class LongContext:
                 mk.set_launch_events(e0, e1)
                 self.pack_events.append((e0, e1))
             mk.mla_ctx_kv_pack(kvb[..., :128], self.ws[:, 512:], self.key, v=kvb[..., 128:],
-                               v_out=self.v8, mode=mk.MLA_PACK_KEY_V_FP8)
+                               v_out=self.v8, mode=mk.MLA_PACK_KEY_V_FP8, max_blocks=max_blocks)
 
 
 def time_kernel(torch, fn, reps=50, warmup=5):
@@ -373,10 +373,20 @@ def context_pack_component(torch, mk, dev, flush):
         mk.mla_ctx_kv_pack(kvb[:, :8, :128], ws[:, 512:], key8_tp, v=kvb[:, :8, 128:],
                            v_out=v8_tp, mode=mk.MLA_PACK_KEY_V_FP8)
 
-    out = {"workload": "chunked-context pack, 8192 tokens x 64 heads (tp8 share: 8 heads)"}
+    # the same fp8 pack as a grid-stride loop over a capped grid (16 workgroups
+    # of 256 threads per compute unit, about 10 chunks per thread)
+    cap = 16 * torch.cuda.get_device_properties(dev).multi_processor_count
+
+    def pack8_capped():
+        mk.mla_ctx_kv_pack(kvb[..., :128], ws[:, 512:], key8, v=kvb[..., 128:], v_out=v8,
+                           mode=mk.MLA_PACK_KEY_V_FP8, max_blocks=cap)
+
+    out = {"workload": "chunked-context pack, 8192 tokens x 64 heads (tp8 share: 8 heads)",
+           "capped_grid_blocks": cap}
     for name, fn, nbytes in (("gather", gather, gather_bytes(8192)),
                              ("gather_raw_fp8", gather_raw, gather_raw_bytes(8192)),
                              ("pack_fp8", pack8, pack_fp8_bytes(8192, 64)),
+                             ("pack_fp8_capped_grid", pack8_capped, pack_fp8_bytes(8192, 64)),
                              ("pack_fp8_kpe_raw", pack8_raw, pack_fp8_kpe_raw_bytes(8192, 64)),
                              ("pack_fp8_fp16_inputs", pack8_f16, pack_fp8_bytes(8192, 64)),
                              ("pack_bf16", packb, pack_bf16_bytes(8192, 64)),
@@ -665,6 +675,21 @@ def main():
                    "bytes_per_step": nbytes, "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
         "roofline": roofline,
     }
+    # the same steps with the gather and the pack as grid-stride loops over a
+    # capped grid (16 workgroups per compute unit); the default full grid is
+    # the faster launch shape on this GPU
+    cap = 16 * torch.cuda.get_device_properties(dev).multi_processor_count
+    wl.step(max_blocks=cap)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        wl.step(max_blocks=cap)
+    torch.cuda.synchronize()
+    csecs = time.perf_counter() - t0
+    result["capped_grid_step"] = {
+        "max_blocks": cap, "ms_per_step": round(csecs / args.steps * 1e3, 4),
+        "GBps": round(nbytes * args.steps / csecs / 1e9, 1),
+        "frac_of_hbm_peak": round(nbytes * args.steps / csecs / 1e9 / HBM_PEAK_GBS, 4)}
     del wl
     torch.cuda.empty_cache()
     if not args.no_components:
