@@ -20,15 +20,20 @@
 //    (global_load_lds_dwordx4, 1 KiB per wavefront instruction), no
 //    register staging; LDS rows are 128 bytes with an XOR swizzle of the
 //    16-byte chunks, so the fragment reads are bank-conflict free;
-//  * two LDS stages and one barrier per stage, placed before the last of
-//    the four K steps: that step's MFMAs hide both the next stage's first
-//    fragment reads and the copy of the stage after it, and every other
-//    step's MFMAs hide the next step's fragment reads (the issue order is
-//    pinned with sched_group_barrier);
+//  * two LDS stages and one barrier per stage, placed after the second of
+//    the four K steps: the fragments of steps 2 and 3 are read before it
+//    (three fragment register slots, rotating by one per stage), so the
+//    copy of the stage after next can start right after it and is spread
+//    over the MFMAs of steps 2 and 3, seven 1 KiB copies under each; step
+//    3 also hides the next stage's first fragment reads, and every step's
+//    MFMAs hide the next step's fragment reads (the issue order is pinned
+//    with sched_group_barrier).  Copies issued in one burst under the last
+//    step alone measured 10% slower with cold operands;
 //  * tiles are grouped per XCD so the workgroups sharing an L2 share their
 //    X and W blocks;
 //  * rows beyond T and columns beyond N are clamped on load and masked on
 //    store, so any T >= 1 and any N that is a multiple of 16 work.
+#include <type_traits>
 #include "mla_common.hpp"
 
 namespace mla {
@@ -116,15 +121,21 @@ __global__ __launch_bounds__(kThreads, 1) void kv_proj_kernel(const GemmArgs a) 
     const int n = min(n0 + r, a.N - 1);
     wsrc[i] = a.w + int64_t(n) * a.K + ((lane & 7) ^ swz(r)) * 8;
   }
-  auto issue_stage = [&](int kb, int buf) {
+  // half h of a stage's copies: h = 0 the first 7 blocks (X blocks 0..6),
+  // h = 1 the rest (X block 7 and the 6 W blocks)
+  auto issue_half = [&](int kb, int buf, int h) {
     uint8_t* base = lds + buf * kStageBytes;
 #pragma unroll
-    for (int i = 0; i < kXBlocks; ++i)
-      copy_to_lds(xsrc[i] + kb * kBK, base + (wave * kXBlocks + i) * 1024);
-#pragma unroll
-    for (int i = 0; i < kWBlocks; ++i)
-      copy_to_lds(wsrc[i] + kb * kBK, base + kBM * kRowBytes + (wave * kWBlocks + i) * 1024);
+    for (int c = 0; c < 7; ++c) {
+      const int i = h * 7 + c;
+      if (i < kXBlocks)
+        copy_to_lds(xsrc[i] + kb * kBK, base + (wave * kXBlocks + i) * 1024);
+      else
+        copy_to_lds(wsrc[i - kXBlocks] + kb * kBK,
+                    base + kBM * kRowBytes + (wave * kWBlocks + i - kXBlocks) * 1024);
+    }
   };
+  static_assert(kXBlocks + kWBlocks == 14, "copies are issued as two halves of 7");
 
   f32x16_t acc[kSubM][kSubN];
 #pragma unroll
@@ -150,19 +161,16 @@ __global__ __launch_bounds__(kThreads, 1) void kv_proj_kernel(const GemmArgs a) 
       woff[j][kk] = kBM * kRowBytes + frag_off(wn * kWaveN + j * 32 + (lane & 31), kk);
   }
 
-  // Pipeline, per stage kb computed from buffer b = kb & 1:
-  //   steps 0..2: MFMAs of step kk with the fragments of step kk + 1 read
-  //               under them;
-  //   barrier:    this wavefront's copy of stage kb + 1 (into b ^ 1) has
-  //               landed, every wavefront's has, and all fragment reads of
-  //               buffer b are done (step 3's are already in registers);
-  //   step 3:     MFMAs, with stage kb + 1's step-0 fragments read from
-  //               b ^ 1 and stage kb + 2 copied into b under them.
-  // Each copy thus has one stage of MFMAs to land, and no fragment read
-  // waits right after a barrier.  Copies past the last stage repeat the
-  // last stage into a free buffer, so the loop body has no branches.
+  // Pipeline, per stage kb computed from buffer b = kb & 1, with three
+  // fragment register slots rotating by one per stage:
+  //   step 0: MFMAs, step 1's fragments read under them;
+  //   step 1: MFMAs, steps 2 and 3's fragments read under them;
+  //   barrier: stage kb + 1 (buffer b ^ 1) has landed everywhere and no
+  //            wavefront reads buffer b any more;
+  //   steps 2, 3: MFMAs with half of stage kb + 2's copies (into b) under
+  //            each, and stage kb + 1's step-0 fragments read under step 3.
   const int stages = a.K / kBK;
-  bf16x8_t fa[2][kSubM], fb[2][kSubN];
+  bf16x8_t fa[3][kSubM], fb[3][kSubN];
   auto read_frags = [&](int slot, const uint8_t* base, int kk) {
 #pragma unroll
     for (int i = 0; i < kSubM; ++i)
@@ -181,52 +189,85 @@ __global__ __launch_bounds__(kThreads, 1) void kv_proj_kernel(const GemmArgs a) 
   };
   constexpr int kFrags = kSubM + kSubN;          // fragment reads per step
   constexpr int kMfma = kSubM * kSubN;           // MFMAs per step
-  constexpr int kCopies = kXBlocks + kWBlocks;   // copy instructions per stage
-  constexpr int kTail = kMfma - kFrags;          // MFMAs of step 3 with no fragment read
-  constexpr int kCopiesPer = (kCopies + kTail - 1) / kTail;
+  static_assert(kFrags == 7 && kMfma == 12, "schedule below is for 7 reads / 12 MFMAs");
 
-  issue_stage(0, 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  issue_half(0, 0, 0);
+  issue_half(0, 0, 1);
+  issue_half(min(1, stages - 1), 1, 0);
+  issue_half(min(1, stages - 1), 1, 1);
+  __builtin_amdgcn_s_waitcnt(0x0F7E);  // vmcnt(14): stage 0 has landed
   __syncthreads();
-  issue_stage(min(1, stages - 1), 1);
   read_frags(0, lds, 0);
-  for (int kb = 0; kb < stages; ++kb) {
+  auto do_stage = [&](auto R, int kb) {
+    constexpr int r = decltype(R)::value;
+    constexpr int sa = r % 3, sb = (r + 1) % 3, sc = (r + 2) % 3;
     const int buf = kb & 1;
     const uint8_t* base = lds + buf * kStageBytes;
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16 - 1; ++kk) {
-      read_frags((kk + 1) & 1, base, kk + 1);
-      mfma_step(kk & 1);
-    }
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16 - 1; ++kk) {
-#pragma unroll
-      for (int q = 0; q < kFrags; ++q) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedLdsRead, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, kMfma - kFrags, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);  // the schedules above and below stay apart
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(0, lds + (buf ^ 1) * kStageBytes, 0);
-    issue_stage(min(kb + 2, stages - 1), buf);
-    mfma_step(1);
-    // the copies write LDS, so they stay behind the fragment reads
+    // step 0
+    read_frags(sb, base, 1);
+    mfma_step(sa);
 #pragma unroll
     for (int q = 0; q < kFrags; ++q) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedLdsRead, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, kMfma - kFrags, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // step 1
+    read_frags(sc, base, 2);
+    read_frags(sa, base, 3);
+    mfma_step(sb);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedLdsRead, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedLdsRead, 2, 0);
 #pragma unroll
-    for (int q = 0; q + 1 < kTail; ++q) {
+    for (int q = 0; q < 10; ++q) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, kCopiesPer, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedLdsRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): stage kb + 1 has landed
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    // step 2
+    issue_half(min(kb + 2, stages - 1), buf, 0);
+    mfma_step(sc);
+#pragma unroll
+    for (int q = 0; q < 7; ++q) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, kMfma - 7, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // step 3
+    read_frags(sb, lds + (buf ^ 1) * kStageBytes, 0);
+    issue_half(min(kb + 2, stages - 1), buf, 1);
+    mfma_step(sa);
+    // the copies write LDS, so they stay behind the fragment reads
+#pragma unroll
+    for (int q = 0; q < 7; ++q) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedLdsRead, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, kCopies - kCopiesPer * (kTail - 1), 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 2, 0);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using R0 = std::integral_constant<int, 0>;
+  using R1 = std::integral_constant<int, 1>;
+  using R2 = std::integral_constant<int, 2>;
+  for (int kb = 0; kb < stages; kb += 3) {
+    do_stage(R0{}, kb);
+    if (kb + 1 < stages) do_stage(R1{}, kb + 1);
+    if (kb + 2 < stages) do_stage(R2{}, kb + 2);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // the repeated copies have landed
 
