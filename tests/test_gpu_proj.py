@@ -73,10 +73,13 @@ def test_proj_one_hot_columns_exact(mk):
     assert np.array_equal(u16(y), u16(x)[:, perm.numpy()])
 
 
-def test_proj_strided_rows(mk):
-    announce("proj strided")
+@pytest.mark.parametrize("K", [128, 512])
+def test_proj_strided_rows(mk, K):
+    """X with a padded row stride; at K = 512 the cache-warming workgroups
+    (K stages from the third on) also read X through that stride."""
+    announce("proj strided", K)
     g = torch.Generator().manual_seed(10)
-    T, K, N = 200, 128, 96
+    T, N = 200, 96
     xb = synth.bf16_normal((T, K + 64), g)
     x = xb.to(DEV)[:, 32:32 + K]           # row stride K + 64, offset 64 bytes
     w = synth.bf16_normal((K, N), g, std=0.05)
