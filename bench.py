@@ -252,7 +252,20 @@ def small_batch(torch, mk, dev):
     wall_binding = per_call_us(call)
     wall_prepared = per_call_us(plan)
     wall_raw = per_call_us(raw)
-    kernel = time_kernel(torch, raw, reps=200)
+    around_call = time_kernel(torch, raw, reps=200)
+    # the kernel alone: events the launch itself records at its start and end
+    ek0 = torch.cuda.Event(enable_timing=True)
+    ek1 = torch.cuda.Event(enable_timing=True)
+    ek0.record()
+    ek1.record()
+    torch.cuda.synchronize()
+    kernel_times = []
+    for _ in range(200):
+        mk.set_launch_events(ek0, ek1)
+        raw()
+        ek1.synchronize()
+        kernel_times.append(ek0.elapsed_time(ek1) * 1e3)
+    kernel = statistics.median(kernel_times)
     # graph replay: 100 inserts captured once
     graph_us = None
     try:
@@ -293,6 +306,7 @@ def small_batch(torch, mk, dev):
             "us_per_launch_wall_prepared": round(wall_prepared, 2),
             "us_per_launch_wall_raw_abi": round(wall_raw, 2),
             "us_kernel": round(kernel, 2),
+            "us_stream_events_around_call": round(around_call, 2),
             "us_per_launch_graph_replay": graph_us if isinstance(graph_us, str) else round(graph_us, 2),
             "us_five_single_layer_launches": round(five_us, 2),
             "target_us": 10.0,
