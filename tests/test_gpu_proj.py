@@ -100,6 +100,22 @@ def test_proj_context_shape_sampled(mk):
     check_close(u16(y)[rows], ref, "proj C3 sampled rows")
 
 
+def test_proj_more_tiles_than_compute_units(mk):
+    """4400 x 256 . 256 x 2880: 18 x 15 = 270 tiles, more than the 256 compute
+    units, so no cache-warming workgroups run and some tiles start in a second
+    round; the last tile row is ragged (4400 = 17 * 256 + 48).  32 sampled rows,
+    the last included, against the oracle."""
+    announce("proj 270 tiles")
+    g = torch.Generator().manual_seed(12)
+    T, K, N = 4400, 256, 2880
+    x = synth.bf16_normal((T, K), g)
+    w = synth.bf16_normal((K, N), g, std=0.05)
+    y = gpu_proj(mk, x, w)
+    rows = np.concatenate([torch.randperm(T, generator=g)[:31].numpy(), [T - 1]])
+    ref = oracle.gemm_rows(u16(x), u16(w), rows)
+    check_close(u16(y)[rows], ref, "proj 270 tiles sampled rows")
+
+
 def test_proj_then_epilogue_chain(mk):
     """Projection -> epilogue on the GPU: the projection is within tolerance
     of the oracle, and the epilogue reading the [T, L, 576] projection output
