@@ -607,6 +607,80 @@ def cpu_baseline(torch):
             "host_cpu": _cpu_model()}
 
 
+def oracle_components(torch):
+    """The oracle (plain serial C, one core) timed beside the components the
+    step does not contain, each on a bounded sample of its workload and in the
+    component's unit (inputs are generated outside the timed calls)."""
+    import numpy as np
+
+    import oracle
+    from fp8_paged_insert_amd import synth
+
+    oracle.build(force=False)
+
+    def u16(t):
+        return np.ascontiguousarray(t.contiguous().view(torch.int16).numpy().view(np.uint16))
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    out = {}
+    # small-batch grouped insert: the whole 5 x 4 workload, 200 calls
+    d = synth.small_batch_fp8("cpu")
+    caches = [c.numpy().copy() for c in d["caches"]]
+    kv, pe = u16(d["kv_c"]), u16(d["k_pe"])
+    sm, sc = np.ascontiguousarray(d["slot_mapping"].numpy()), d["scales"].numpy()
+    secs = timed(lambda: [oracle.insert_grouped(kv, pe, sm, caches, sc) for _ in range(200)])
+    out["small_batch_insert"] = {"value": round(secs / 200 * 1e6, 2), "unit": "us/call",
+                                 "cores": 1,
+                                 "sample": "the whole 5 x 4 workload, 200 calls through the "
+                                           "oracle's Python wrapper"}
+    del caches
+    # projection: 16 rows of the 4096 x 7168 . 7168 x 2880 product (float64 sums)
+    g = synth.gen(3)
+    x = u16(synth.bf16_normal((16, 7168), g))
+    w = u16(synth.bf16_normal((7168, L * W), g, std=0.02))
+    secs = timed(lambda: oracle.gemm_rows(x, w))
+    flops = 2 * 16 * 7168 * L * W
+    out["context_kv_proj"] = {"value": round(flops / secs / 1e9, 3), "unit": "GFLOP/s",
+                              "cores": 1, "sample": f"16 of the 4096 rows ({secs:.2f}s)"}
+    # context epilogue: 5 layers x 1024 tokens
+    e = synth.context_epilogue("cpu", num_tokens=1024, num_blocks=16, with_gemm=False)
+    caches = [c.numpy().copy() for c in e["caches"]]
+    akv, gam = u16(e["all_kv"]), u16(e["gamma"])
+    pos, slm = e["positions"].numpy(), np.ascontiguousarray(e["slot_mapping"].numpy())
+    secs = timed(lambda: oracle.ctx_kv_epilogue(akv, gam, e["eps"], pos, slm, caches,
+                                                e["scales"].numpy()))
+    out["context_epilogue"] = {"value": round(epilogue_bytes(L, 1024) / secs / 1e9, 4),
+                               "unit": "GB/s", "cores": 1,
+                               "sample": f"5 layers x 1024 of the 4096 tokens ({secs:.2f}s)"}
+    # chunk merge: 2048 tokens x 64 heads x 128
+    m = synth.attention_partials("cpu", num_tokens=2048, heads=64, head_dim=128, chunks=2)
+    acc, part = u16(m["outs"][0]), u16(m["outs"][1])
+    lacc = np.ascontiguousarray(m["lses"][0].numpy())
+    plse = np.ascontiguousarray(m["lses"][1].numpy())
+    secs = timed(lambda: oracle.merge_chunk(acc, lacc, part, plse, oracle.MERGE_ACCUMULATE))
+    out["chunk_merge"] = {"value": round(merge_bytes(2048, 64) / secs / 1e9, 4), "unit": "GB/s",
+                          "cores": 1, "sample": f"2048 of the 16384 tokens ({secs:.2f}s)"}
+    # new-token epilogue, fp8 (plain cast): 512 tokens x 64 heads
+    n = synth.new_tokens("cpu", num_tokens=512)
+    q, kvb, lat = u16(n["q"]), u16(n["kvb"]), u16(n["kv"])
+    h = [np.ascontiguousarray(a) for a in (q[..., :128], q[..., 128:], kvb[..., :128],
+                                           lat[:, :R], lat[:, R:], kvb[..., 128:])]
+    cache, slots = n["cache"].numpy().copy(), n["slots"].numpy()
+    valid = int((slots >= 0).sum())
+    secs = timed(lambda: oracle.new_token_epilogue(
+        h[0], h[1], h[2], h[3], h[4], n["positions"].numpy(), v=h[5], mode=oracle.PACK_KEY_V_FP8,
+        cache=cache, slots=slots, cache_scale=float(n["cache_scale"][0])))
+    out["new_token_epilogue"] = {"value": round(new_token_bytes(512, 64, True, valid) / secs / 1e9,
+                                                4),
+                                 "unit": "GB/s", "cores": 1,
+                                 "sample": f"fp8, 512 of the 8192 tokens x 64 heads ({secs:.2f}s)"}
+    return out
+
+
 def _cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -718,6 +792,9 @@ def main():
         result["components"] = comps
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(torch)
+        if "components" in result:
+            for name, o in oracle_components(torch).items():
+                result["components"][name]["cpu_oracle"] = o
     print(json.dumps(result), flush=True)
 
 

@@ -46,3 +46,17 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_oracle_timed_beside_each_component():
+    """Every component outside the timed step gets the oracle's own figure on
+    a bounded sample, in the component's unit, with the sample stated."""
+    import torch
+
+    import bench
+
+    r = bench.oracle_components(torch)
+    assert set(r) == {"small_batch_insert", "context_kv_proj", "context_epilogue", "chunk_merge",
+                      "new_token_epilogue"}
+    for name, o in r.items():
+        assert o["value"] > 0 and o["cores"] == 1 and o["unit"] and o["sample"], name
