@@ -181,6 +181,26 @@ __global__ __launch_bounds__(256) void new_token_kernel(const NewTokenArgs a) {
       const uint2 kpe = ld8(a.k_pe + int64_t(t) * a.kpe_ts + 4 * j);
       uint8_t* qo = static_cast<uint8_t*>(a.q_out) + int64_t(task) * width * ob;
       uint8_t* ko = static_cast<uint8_t*>(a.key_out) + int64_t(task) * width * ob;
+      if (a.nope == 128 && (!kFp8 || a.vdim == 128)) {
+        // The MLA shape: one nope (and V) chunk per lane, every load issued
+        // before the first conversion, so a task waits on memory once (the
+        // general loop below issues V's load after the query and key stores).
+        const uint4 xq = ld16_once(qn + 8 * j);
+        const uint4 xk = ld16_once(kn + 8 * j);
+        uint4 xv = make_uint4(0, 0, 0, 0);
+        if constexpr (kFp8)
+          xv = ld16_once(a.v + int64_t(t) * a.v_ts + int64_t(h) * a.v_hs + 8 * j);
+        put8<kOut, kNtStream, kScaled>(qo + 8 * j * ob, xq, qs, qr, qf);
+        put8<kOut, kNtStream, kScaled>(ko + 8 * j * ob, xk, ks, kr, kf);
+        put4<kOut, kNtStream, kScaled>(qo + (128 + 4 * j) * ob, rope4(qpe, cv, sv, first), qs,
+                                         qr, qf);
+        put4<kOut, kNtStream, kScaled>(ko + (128 + 4 * j) * ob, rope4(kpe, cv, sv, first), ks,
+                                         kr, kf);
+        if constexpr (kFp8)
+          put8<kFmtE4M3, kNtStream, kScaled>(a.v_out + int64_t(task) * 128 + 8 * j, xv, vs, vr,
+                                             vf);
+        continue;
+      }
       for (uint32_t c = j; c < a.nope / 8; c += kLanes) {
         const uint4 xq = ld16_once(qn + 8 * c);
         const uint4 xk = ld16_once(kn + 8 * c);

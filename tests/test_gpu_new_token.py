@@ -221,3 +221,54 @@ def test_capped_grid_and_cache_only(mk):
                               kv_cache_dtype="fp8", cache_scale=g["cache_scale"])
     torch.cuda.synchronize()
     assert torch.equal(c, a[3])
+
+
+@pytest.mark.parametrize("nope,vdim", [(64, 96), (256, 128)])
+@pytest.mark.parametrize("fp8", [False, True])
+def test_other_head_widths(mk, nope, vdim, fp8):
+    """nope / V widths other than 128 (the MLA shape has its own straight-line
+    path): 64 / 96 leaves lanes of each 16-lane row idle, 256 gives each lane
+    two nope chunks.  The nope parts and V are casts (bit-exact against the
+    oracle); the rotated parts are judged as in the other cases."""
+    announce("new-token epilogue widths", nope, vdim, fp8)
+    g = synth.gen(60 + nope + vdim)
+    T, H = 37, 3
+    qn, qp = synth.bf16_normal((T, H, nope), g), synth.bf16_normal((T, H, P), g)
+    kn, v = synth.bf16_normal((T, H, nope), g), synth.bf16_normal((T, H, vdim), g)
+    kv = synth.bf16_normal((T, R + P), g)
+    pos = torch.randint(0, 4096, (T,), generator=g)
+    cs = torch.empty(4096, P, dtype=torch.float32, device=DEV)
+    mk.mla_rope_cos_sin_cache(cs, 4096, P, 10000.0)
+    kvd = kv.to(DEV)
+
+    def run(fp8_out):
+        odt = torch.uint8 if fp8_out else torch.bfloat16
+        qo = torch.empty(T, H, nope + P, dtype=odt, device=DEV)
+        ko = torch.empty(T, H, nope + P, dtype=odt, device=DEV)
+        vo = torch.empty(T, H, vdim, dtype=torch.uint8, device=DEV) if fp8_out else None
+        kw = dict(v=v.to(DEV), v_out=vo, mode=mk.MLA_PACK_KEY_V_FP8) if fp8_out else {}
+        mk.mla_new_token_epilogue(qn.to(DEV), qp.to(DEV), kn.to(DEV), kvd[:, :R], kvd[:, R:],
+                                  pos.to(DEV), cs, qo, ko, **kw)
+        torch.cuda.synchronize()
+        return qo, ko, vo
+
+    h = [u16(x) for x in (qn, qp, kn, kv[:, :R], kv[:, R:], v)]
+    qb, kb, _ = run(False)
+    qref, kref, _ = oracle.new_token_epilogue(h[0], h[1], h[2], h[3], h[4], pos.numpy())
+    assert_rope_close(u16(qb)[..., nope:], qref[..., nope:], h[1], "query rope")
+    kpe_b = np.broadcast_to(h[4][:, None, :], kref[..., nope:].shape)
+    assert_rope_close(u16(kb)[..., nope:], kref[..., nope:], kpe_b, "key rope")
+    if not fp8:
+        assert np.array_equal(u16(qb)[..., :nope], qref[..., :nope]), "query nope part"
+        assert np.array_equal(u16(kb)[..., :nope], kref[..., :nope]), "key nope part"
+        return
+    qg, kg, vg = run(True)
+    q8, k8, v8 = oracle.new_token_epilogue(h[0], h[1], h[2], h[3], h[4], pos.numpy(), v=h[5],
+                                           mode=oracle.PACK_KEY_V_FP8)
+    assert np.array_equal(u8(qg)[..., :nope], q8[..., :nope]), "query nope codes"
+    assert np.array_equal(u8(kg)[..., :nope], k8[..., :nope]), "key nope codes"
+    assert np.array_equal(u8(vg), v8), "V codes"
+    assert_codes(u8(qg)[..., nope:], q8[..., nope:], u16(qb)[..., nope:], qref[..., nope:],
+                 "query rope codes")
+    assert_codes(u8(kg)[..., nope:], k8[..., nope:], u16(kb)[..., nope:], kref[..., nope:],
+                 "key rope codes")
