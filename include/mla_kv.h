@@ -52,7 +52,7 @@ typedef void* mla_stream_t; /* hipStream_t */
 typedef enum {
   MLA_OK = 0,
   MLA_ERR_INVALID_ARGUMENT = 1, /* bad size, null pointer, wrong dtype/scale combination */
-  MLA_ERR_UNSUPPORTED = 2,      /* a valid request this build does not implement */
+  MLA_ERR_UNSUPPORTED = 2,      /* a valid request the library does not implement */
   MLA_ERR_MISALIGNED = 3,       /* a pointer or stride breaks 16-byte row alignment */
   MLA_ERR_DEVICE = 4            /* the HIP runtime reported an error at launch */
 } mla_status_t;
