@@ -1,9 +1,11 @@
 """HIP-graph capture of the library's launches.
 
 A serving loop captures its per-step kernels once and replays them with new
-inputs copied into the same buffers.  The captured step here is a grouped
-fp8 insert (5 layers x 4 tokens), a new-token epilogue (4 tokens x 8 heads,
-fp8 outputs, fp8 cache) and a chunk merge (4 tokens x 8 heads x 128).  Every
+inputs copied into the same buffers.  The captured step here is a KV-only
+projection (300 x 512 . 512 x 576: eight K stages, so its cache-warming
+workgroups run too), a grouped fp8 insert (5 layers x 4 tokens), a new-token
+epilogue (4 tokens x 8 heads, fp8 outputs, fp8 cache) and a chunk merge
+(4 tokens x 8 heads x 128).  Every
 replay runs on fresh inputs written eagerly between replays, and its results
 (caches, query / key / V rows, accumulator and lse) must equal bit for bit
 the same calls run eagerly from the same starting state.  The library records
@@ -21,7 +23,7 @@ L, T, H, NB, BS = 5, 4, 8, 64, 64
 
 
 def test_captured_step_replays_match_eager_runs(mk):
-    announce("graph capture: grouped insert + new-token epilogue + merge")
+    announce("graph capture: projection + grouped insert + new-token epilogue + merge")
     g = synth.gen(77)
     bf = torch.bfloat16
     # static buffers the graph is captured on
@@ -46,8 +48,12 @@ def test_captured_step_replays_match_eager_runs(mk):
     lacc = torch.randn(H, T, generator=g).to(DEV)
     part = torch.zeros(T, H, 128, dtype=bf, device=DEV)
     plse = torch.zeros(H, T, dtype=torch.float32, device=DEV)
+    px = torch.zeros(300, 512, dtype=bf, device=DEV)
+    pw = torch.zeros(576, 512, dtype=bf, device=DEV)
+    py = torch.empty(300, 576, dtype=bf, device=DEV)
 
     def step():
+        mk.mla_ctx_kv_proj(px, pw, py)
         mk.mla_kv_insert_grouped(kv[:, :, :512].permute(1, 0, 2), kv[:, :, 512:].permute(1, 0, 2),
                                  ptrs, slots, BS, BS * 576, 576, scales, "fp8")
         mk.mla_new_token_epilogue(q[..., :128], q[..., 128:], kvb[..., :128], lat[:, :512],
@@ -73,9 +79,11 @@ def test_captured_step_replays_match_eager_runs(mk):
         nt_slots.copy_(ns.to(DEV))
         part.copy_(synth.bf16_normal((T, H, 128), r).to(DEV))
         plse.copy_((4.0 * torch.randn(H, T, generator=r)).to(DEV))
+        px.copy_(synth.bf16_normal((300, 512), r).to(DEV))
+        pw.copy_(synth.bf16_normal((576, 512), r, std=0.05).to(DEV))
 
     state = lambda: [*caches, nt_cache, acc, lacc]             # noqa: E731
-    outputs = lambda: [*state(), q_out, k_out, v_out]         # noqa: E731
+    outputs = lambda: [*state(), q_out, k_out, v_out, py]     # noqa: E731
 
     # warm up eagerly on a side stream, then capture
     fill(1000)
