@@ -102,9 +102,13 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
 // Exactness argument, step by step:
 //  * quotient: r = RN(1/s) once; q0 = RN(x*r) is within one ulp of x/s, the
 //    remainder x - q0*s is exact under FMA, and q = RN(q0 + rem*r) is the
-//    correctly rounded x/s (Markstein; checked exhaustively on the CPU for
-//    every bf16 and every fp16 significand against every fp32 significand of
-//    s).  Where the step degenerates -- x = +-0 (the sum of signed zeros
+//    correctly rounded x/s (Markstein).  tests/quotient_exactness.c checks
+//    this on the host for every bf16 and every fp16 significand against
+//    every fp32 significand of s, and for every finite bf16 value against
+//    scales of every exponent: wherever the quotient can reach an fp8 code it
+//    is exact for 2^-85 <= |s| < 2^126 (outside that range the remainder or
+//    r leaves the normal range; such scales are a stated precondition).
+//    Where the step degenerates -- x = +-0 (the sum of signed zeros
 //    gives +0), x = +-Inf or an overflowing quotient (Inf - Inf gives NaN) --
 //    only the sign of the final code can be wrong, and it is rewritten below.
 //  * saturation: v_med3 clamps to [-max, max]; it also maps NaN onto a

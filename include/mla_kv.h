@@ -37,6 +37,12 @@
  *     (slot numbers, cache base pointers, positions) cannot be checked from
  *     the host: they are preconditions, stated per entry point.
  *   - A call with zero tokens (or zero layers) succeeds without launching.
+ *   - fp8 quantisation divides by a dequantisation scale s read from device
+ *     memory (kv_scales, k_scale, ...).  The codes equal those of the IEEE
+ *     fp32 quotient x / s for every scale with 2^-85 <= |s| < 2^126 (checked
+ *     exhaustively on the host by tests/quotient_exactness.c); scales outside
+ *     that range, zero and non-finite scales are a precondition violation
+ *     (codes may then differ from the quotient's).
  */
 #ifndef MLA_KV_H
 #define MLA_KV_H
