@@ -74,12 +74,12 @@ def merge_bytes(tokens, heads, head_dim=128):
 def new_token_bytes(tokens, heads, fp8, valid_rows, cache_elem=1, nope=128, rope=64, vdim=128):
     """Read the query [T, H, nope+rope], k_nope (and v in fp8 mode) from their
     strided views, the latent row [kv_c | k_pe], the position, the slot and
-    the cos/sin row of each token; write the query and key rows (and fp8 V)
+    the float64 cos/sin row of each token; write the query and key rows (and fp8 V)
     and one cache entry per valid token."""
     ob = 1 if fp8 else 2
     per_row = (nope + rope) * 2 + nope * 2 + (vdim * 2 if fp8 else 0)
     per_row += 2 * (nope + rope) * ob + (vdim if fp8 else 0)
-    per_tok = (R + P) * 2 + 8 + 8 + P * 4
+    per_tok = (R + P) * 2 + 8 + 8 + P * 8
     return tokens * heads * per_row + tokens * per_tok + valid_rows * W * cache_elem
 
 
@@ -89,9 +89,9 @@ def pack_bf16_bytes(tokens, heads, nope=128, rope=64):
 
 def epilogue_bytes(layers, tokens):
     """Read the [T, L, 576] projection output, slots, positions, gamma, the
-    cos/sin rows of the positions used; write one fp8 entry per row."""
+    float64 cos/sin rows of the positions used; write one fp8 entry per row."""
     return (tokens * layers * W * 2 + layers * tokens * 8 + tokens * 8 + layers * R * 2
-            + tokens * P * 4 + layers * 8 + layers * tokens * W)
+            + tokens * P * 8 + layers * 8 + layers * tokens * W)
 
 
 # --------------------------------------------------------------- workload --
@@ -415,7 +415,7 @@ def epilogue_component(torch, mk, dev, flush):
 
     d = synth.context_epilogue(dev, with_gemm=False)
     T = d["num_tokens"]
-    cs = torch.empty(T, P, dtype=torch.float32, device=dev)
+    cs = torch.empty(T, P, dtype=torch.float64, device=dev)
     mk.mla_rope_cos_sin_cache(cs, T, P, 10000.0)
     ptrs = mk.cache_ptr_table(d["caches"])
 
@@ -486,7 +486,7 @@ def new_token_component(torch, mk, dev, flush):
 
     d = synth.new_tokens(dev)
     T, H = d["num_tokens"], d["num_heads"]
-    cs = torch.empty(d["max_pos"], P, dtype=torch.float32, device=dev)
+    cs = torch.empty(d["max_pos"], P, dtype=torch.float64, device=dev)
     mk.mla_rope_cos_sin_cache(cs, d["max_pos"], P, 10000.0)
     q, kvb, kv = d["q"], d["kvb"], d["kv"]
     valid = int((d["slots"] >= 0).sum())
@@ -543,7 +543,7 @@ def projection_component(torch, mk, dev, flush):
     # end to end: the projection, then the epilogue reading its output as
     # [T, L, 576] and inserting into 5 fp8 caches (stream events around both)
     e = synth.context_epilogue(dev, with_gemm=False)
-    cs = torch.empty(4096, P, dtype=torch.float32, device=dev)
+    cs = torch.empty(4096, P, dtype=torch.float64, device=dev)
     mk.mla_rope_cos_sin_cache(cs, 4096, P, 10000.0)
     ptrs = mk.cache_ptr_table(e["caches"])
     e2e = []

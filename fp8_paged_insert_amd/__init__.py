@@ -31,6 +31,7 @@ from ._binding import (  # noqa: F401
     lib,
     mla_ctx_kv_epilogue,
     mla_ctx_kv_pack,
+    mla_ctx_kv_pack_gather,
     mla_ctx_kv_proj,
     mla_ctx_latent_gather,
     mla_ctx_merge_chunk,

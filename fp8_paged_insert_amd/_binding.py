@@ -41,7 +41,7 @@ MLA_MERGE_ACCUMULATE = 2
 EXPORTS = (
     "mla_last_error", "mla_version", "mla_parse_kv_cache_dtype", "mla_set_launch_events",
     "mla_kv_insert_grouped", "mla_rope_cos_sin_cache", "mla_ctx_kv_epilogue",
-    "mla_ctx_kv_proj", "mla_ctx_latent_gather", "mla_ctx_kv_pack",
+    "mla_ctx_kv_proj", "mla_ctx_latent_gather", "mla_ctx_kv_pack", "mla_ctx_kv_pack_gather",
     "mla_ctx_merge_chunk", "mla_ctx_neutralize_partials", "mla_new_token_epilogue",
 )
 
@@ -71,6 +71,10 @@ _SIGS = {
                                      _vp, _i64, _vp]),
     "mla_ctx_kv_pack": (_i32, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _i64,
                                _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _vp]),
+    "mla_ctx_kv_pack_gather": (_i32, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64,
+                                      _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp,
+                                      _vp, _i32, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i32,
+                                      _vp, _vp]),
     "mla_ctx_merge_chunk": (_i32, [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp,
                                    _i64, _i64, _i64, _i64, _i64, _i32, _vp]),
     "mla_ctx_neutralize_partials": (_i32, [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64,
@@ -335,10 +339,10 @@ def prepare_insert_grouped(*args, **kwargs) -> PreparedInsert:
 
 
 def mla_rope_cos_sin_cache(out, max_pos, rope_dim, base=10000.0):
-    """Fill fp32 [max_pos, rope_dim] = cos | sin table on the device."""
-    _need(out, (torch.float32,), "out")
+    """Fill the float64 [max_pos, rope_dim] = cos | sin table on the device."""
+    _need(out, (torch.float64,), "out")
     if not out.is_contiguous() or out.numel() != max_pos * rope_dim:
-        raise RuntimeError("out must be a contiguous fp32 [max_pos, rope_dim] tensor")
+        raise RuntimeError("out must be a contiguous float64 [max_pos, rope_dim] tensor")
     _check(lib().mla_rope_cos_sin_cache(_ptr(out), int(max_pos), int(rope_dim), float(base),
                                         _stream(out)), "mla_rope_cos_sin_cache")
 
@@ -350,7 +354,7 @@ def mla_ctx_kv_epilogue(all_kv, gamma, eps, positions, cos_sin, kv_cache_ptrs, s
     _need(all_kv, (torch.bfloat16,), "all_kv")
     _need(gamma, (torch.bfloat16,), "gamma")
     _need(positions, (torch.int64,), "positions")
-    _need(cos_sin, (torch.float32,), "cos_sin")
+    _need(cos_sin, (torch.float64,), "cos_sin")
     if all_kv.dim() != 3 or all_kv.stride(2) != 1:
         raise RuntimeError("all_kv must be a [T, L, width] view with contiguous rows")
     T, L, W = all_kv.shape
@@ -361,7 +365,7 @@ def mla_ctx_kv_epilogue(all_kv, gamma, eps, positions, cos_sin, kv_cache_ptrs, s
     if positions.numel() != T or not positions.is_contiguous():
         raise RuntimeError(f"positions must be contiguous [{T}]")
     if cos_sin.dim() != 2 or cos_sin.shape[1] != P or not cos_sin.is_contiguous():
-        raise RuntimeError(f"cos_sin must be contiguous [max_pos, {P}]")
+        raise RuntimeError(f"cos_sin must be a contiguous float64 [max_pos, {P}] table")
     for t, n in ((gamma, "gamma"), (positions, "positions"), (cos_sin, "cos_sin")):
         _same_device(t, all_kv, n, "all_kv")
     sm, sls = _slots_2d(slot_mapping, L, T)
@@ -405,14 +409,8 @@ def mla_ctx_kv_proj(x, w_nk, y):
                                  y.stride(0), _stream(x)), "mla_ctx_kv_proj")
 
 
-def mla_ctx_latent_gather(cache, src_slots, out, cache_scale=None, kv_cache_dtype="fp8",
-                          max_blocks=0):
-    """out[j, :] = cache row of src_slots[j]; cache [num_blocks, block_size, E].
-
-    A bf16 `out` receives bf16 rows (dequantised with cache_scale for an fp8
-    cache); a uint8 (or same-format float8) `out` receives an fp8 cache's
-    codes as they are (no cache_scale).
-    """
+def _gather_args(cache, src_slots, out, cache_scale, kv_cache_dtype):
+    """Checked argument list of the gather (without max_blocks and stream)."""
     _need(src_slots, (torch.int64,), "src_slots")
     raw = out.dtype != torch.bfloat16
     dt = _cache_dtype_code(kv_cache_dtype)
@@ -442,25 +440,30 @@ def mla_ctx_latent_gather(cache, src_slots, out, cache_scale=None, kv_cache_dtyp
         raise RuntimeError("src_slots must be contiguous")
     _same_device(src_slots, cache, "src_slots", "cache")
     _same_device(out, cache, "out", "cache")
-    st = lib().mla_ctx_latent_gather(
-        _ptr(cache), dt, _ptr(cache_scale), cache.shape[1], cache.stride(0), cache.stride(1),
-        _ptr(src_slots), T, out.shape[1], dt if raw else MLA_KV_BF16, _ptr(out),
-        int(max_blocks), _stream(cache))
-    _check(st, "mla_ctx_latent_gather")
+    return (_ptr(cache), dt, _ptr(cache_scale), cache.shape[1], cache.stride(0),
+            cache.stride(1), _ptr(src_slots), T, out.shape[1], dt if raw else MLA_KV_BF16,
+            _ptr(out))
+
+
+def mla_ctx_latent_gather(cache, src_slots, out, cache_scale=None, kv_cache_dtype="fp8",
+                          max_blocks=0):
+    """out[j, :] = cache row of src_slots[j]; cache [num_blocks, block_size, E].
+
+    A bf16 `out` receives bf16 rows (dequantised with cache_scale for an fp8
+    cache); a uint8 (or same-format float8) `out` receives an fp8 cache's
+    codes as they are (no cache_scale).
+    """
+    args = _gather_args(cache, src_slots, out, cache_scale, kv_cache_dtype)
+    _check(lib().mla_ctx_latent_gather(*args, int(max_blocks), _stream(cache)),
+           "mla_ctx_latent_gather")
 
 
 _SRC_DTYPES = {torch.bfloat16: MLA_KV_BF16, torch.float16: MLA_KV_FP16}
 _FP8_VIEWS = (torch.uint8, torch.float8_e4m3fn)
 
 
-def mla_ctx_kv_pack(k_nope, k_pe, key_out, v=None, v_out=None, mode=MLA_PACK_KEY_BF16,
-                    k_scale=None, v_scale=None, max_blocks=0):
-    """Contiguous full key [T, H, nope+rope] (+ fp8 V) from strided k_nope / k_pe / v.
-
-    k_nope and v are bf16 or fp16.  k_pe has k_nope's dtype, or -- in the fp8
-    modes -- holds fp8 codes (uint8 / float8_e4m3fn, e.g. a view of a raw fp8
-    gather), which are copied into the key as they are.
-    """
+def _pack_args(k_nope, k_pe, key_out, v, v_out, mode, k_scale, v_scale):
+    """Checked argument list of the pack (without max_blocks and stream)."""
     _need(k_nope, tuple(_SRC_DTYPES), "k_nope")
     src = _SRC_DTYPES[k_nope.dtype]
     if k_pe.dim() == 3:  # [T, 1, rope]
@@ -503,11 +506,33 @@ def mla_ctx_kv_pack(k_nope, k_pe, key_out, v=None, v_out=None, mode=MLA_PACK_KEY
                 _check_scales(sc, 1, k_nope, n)
     else:
         raise RuntimeError(f"unknown pack mode {mode}")
-    st = lib().mla_ctx_kv_pack(
-        _ptr(k_nope), k_nope.stride(0), k_nope.stride(1), _ptr(k_pe), k_pe.stride(0), _ptr(v),
-        vts, vhs, T, H, nope, rope, vd, int(mode), src, _ptr(k_scale), _ptr(v_scale),
-        _ptr(key_out), _ptr(v_out), int(max_blocks), _stream(k_nope))
-    _check(st, "mla_ctx_kv_pack")
+    return (_ptr(k_nope), k_nope.stride(0), k_nope.stride(1), _ptr(k_pe), k_pe.stride(0),
+            _ptr(v), vts, vhs, T, H, nope, rope, vd, int(mode), src, _ptr(k_scale),
+            _ptr(v_scale), _ptr(key_out), _ptr(v_out))
+
+
+def mla_ctx_kv_pack(k_nope, k_pe, key_out, v=None, v_out=None, mode=MLA_PACK_KEY_BF16,
+                    k_scale=None, v_scale=None, max_blocks=0):
+    """Contiguous full key [T, H, nope+rope] (+ fp8 V) from strided k_nope / k_pe / v.
+
+    k_nope and v are bf16 or fp16.  k_pe has k_nope's dtype, or -- in the fp8
+    modes -- holds fp8 codes (uint8 / float8_e4m3fn, e.g. a view of a raw fp8
+    gather), which are copied into the key as they are.
+    """
+    args = _pack_args(k_nope, k_pe, key_out, v, v_out, mode, k_scale, v_scale)
+    _check(lib().mla_ctx_kv_pack(*args, int(max_blocks), _stream(k_nope)), "mla_ctx_kv_pack")
+
+
+def mla_ctx_kv_pack_gather(k_nope, k_pe, key_out, cache, src_slots, gather_out, v=None,
+                           v_out=None, mode=MLA_PACK_KEY_BF16, k_scale=None, v_scale=None,
+                           cache_scale=None, kv_cache_dtype="fp8"):
+    """One launch: the pack of one chunk (arguments as mla_ctx_kv_pack) and
+    the latent gather of the next (as mla_ctx_latent_gather, into gather_out,
+    which must not overlap the pack's tensors)."""
+    pa = _pack_args(k_nope, k_pe, key_out, v, v_out, mode, k_scale, v_scale)
+    ga = _gather_args(cache, src_slots, gather_out, cache_scale, kv_cache_dtype)
+    _same_device(cache, k_nope, "cache", "k_nope")
+    _check(lib().mla_ctx_kv_pack_gather(*pa, *ga, _stream(k_nope)), "mla_ctx_kv_pack_gather")
 
 
 # ------------------------------------------------------ new-token epilogue --
@@ -520,7 +545,7 @@ def mla_new_token_epilogue(q_nope, q_pe, k_nope, kv_c, k_pe, positions, cos_sin,
     into one layer's paged cache [num_blocks, block_size, >= R + rope].
 
     q_nope / q_pe / k_nope / v: bf16 [T, H, d] views with contiguous rows;
-    kv_c / k_pe: bf16 [T, d] views; positions int64 [T]; cos_sin fp32
+    kv_c / k_pe: bf16 [T, d] views; positions int64 [T]; cos_sin float64
     [max_pos, rope] (mla_rope_cos_sin_cache).  q_out / key_out [T, H, nope+rope]
     and v_out [T, H, vdim] contiguous: bf16 in KEY_BF16 mode, fp8 e4m3fn
     (uint8 or float8_e4m3fn) in KEY_V_FP8 mode.  cache=None skips the insert.
@@ -543,9 +568,9 @@ def mla_new_token_epilogue(q_nope, q_pe, k_nope, kv_c, k_pe, positions, cos_sin,
     _need(positions, (torch.int64,), "positions")
     if positions.numel() != T or not positions.is_contiguous():
         raise RuntimeError("positions must be a contiguous int64 [T] tensor")
-    _need(cos_sin, (torch.float32,), "cos_sin")
+    _need(cos_sin, (torch.float64,), "cos_sin")
     if cos_sin.dim() != 2 or cos_sin.shape[1] != rope or not cos_sin.is_contiguous():
-        raise RuntimeError(f"cos_sin must be a contiguous fp32 [max_pos, {rope}] table")
+        raise RuntimeError(f"cos_sin must be a contiguous float64 [max_pos, {rope}] table")
     for t_, n in ((positions, "positions"), (cos_sin, "cos_sin"), (q_out, "q_out"),
                   (key_out, "key_out")):
         _same_device(t_, q_nope, n, "q_nope")

@@ -21,8 +21,10 @@
 // so every load and store instruction covers 128-256 contiguous bytes per
 // row.  The sum of squares is reduced with four in-row DPP steps (no LDS
 // round trip), RoPE's (i, i + 32) pairs sit in lanes j and j ^ 8 and swap
-// with one DPP row rotation, and the token's position indexes the fp32
-// cos/sin table directly instead of a repeated-positions buffer.
+// with one DPP row rotation, and the token's position indexes the float64
+// cos/sin table directly instead of a repeated-positions buffer.  The
+// rotation runs in float64 (a handful of operations per lane), so where its
+// two products nearly cancel the result still rounds correctly to bf16.
 #include "mla_common.hpp"
 
 namespace mla {
@@ -36,7 +38,7 @@ int32_t check_insert_common(const char* fn, const int64_t* kv_cache_ptrs,
 namespace {
 
 // -------------------------------------------------------------- rope table --
-__global__ __launch_bounds__(256) void rope_table_kernel(float* out, int64_t max_pos,
+__global__ __launch_bounds__(256) void rope_table_kernel(double* out, int64_t max_pos,
                                                          int64_t rope_dim, double base) {
   const int64_t half = rope_dim / 2;
   const int64_t n = max_pos * half;
@@ -45,8 +47,8 @@ __global__ __launch_bounds__(256) void rope_table_kernel(float* out, int64_t max
     const int64_t p = idx / half;
     const int64_t i = idx - p * half;
     const double theta = double(p) * pow(base, -2.0 * double(i) / double(rope_dim));
-    out[p * rope_dim + i] = static_cast<float>(cos(theta));
-    out[p * rope_dim + half + i] = static_cast<float>(sin(theta));
+    out[p * rope_dim + i] = cos(theta);
+    out[p * rope_dim + half + i] = sin(theta);
   }
 }
 
@@ -66,7 +68,7 @@ struct EpiArgs {
   const uint16_t* gamma;
   float eps;
   const int64_t* positions;
-  const float* cos_sin;
+  const double* cos_sin;
   int64_t max_pos;
   const int64_t* cache_ptrs;
   const float* scales;
@@ -149,9 +151,10 @@ __global__ __launch_bounds__(256) void epilogue_kernel(const EpiArgs a) {
     if constexpr (kFp8) sc = a.scales[l];
     __builtin_amdgcn_sched_barrier(0);
     const int64_t pos = min(max(pos_in, int64_t(0)), a.max_pos - 1);
-    const float* cs = a.cos_sin + pos * kP + kPe * (j & 7);
-    const uint4 cv = ld16(cs);
-    const uint4 sv = ld16(cs + kP / 2);
+    const double* cs = a.cos_sin + pos * kP + kPe * (j & 7);
+    double cc[kPe], sn[kPe];
+    ld_f64x4(cs, cc);
+    ld_f64x4(cs + kP / 2, sn);
     // Keep every load of the row here, ahead of the first wait: without this
     // fence the compiler sinks the loads used only by the stores into the
     // store branch, after the reduction, adding memory round trips.
@@ -187,17 +190,10 @@ __global__ __launch_bounds__(256) void epilogue_kernel(const EpiArgs a) {
 
     // ---- RoPE: y_i = x_i cos - x_{i+32} sin, y_{i+32} = x_{i+32} cos + x_i sin
     const float xp[kPe] = {bf16_lo(pe.x), bf16_hi(pe.x), bf16_lo(pe.y), bf16_hi(pe.y)};
-    const float cc[kPe] = {__uint_as_float(cv.x), __uint_as_float(cv.y), __uint_as_float(cv.z),
-                           __uint_as_float(cv.w)};
-    const float sn[kPe] = {__uint_as_float(sv.x), __uint_as_float(sv.y), __uint_as_float(sv.z),
-                           __uint_as_float(sv.w)};
-    float yp[kPe];
+    float xq[kPe];
 #pragma unroll
-    for (int e = 0; e < kPe; ++e) {
-      const float xq = dpp_f<kDppRor8>(xp[e]);
-      yp[e] = xp[e] * cc[e] + xq * (first_half ? -sn[e] : sn[e]);
-    }
-    const uint2 ype = make_uint2(cvt_bf16x2(yp[0], yp[1]), cvt_bf16x2(yp[2], yp[3]));
+    for (int e = 0; e < kPe; ++e) xq[e] = dpp_f<kDppRor8>(xp[e]);
+    const uint2 ype = rope4_f64(xp, xq, cc, sn, first_half);
 
     if (!active) continue;
     if (a.dbg) {
@@ -231,7 +227,7 @@ __global__ __launch_bounds__(256) void epilogue_kernel(const EpiArgs a) {
 
 using namespace mla;
 
-extern "C" int32_t mla_rope_cos_sin_cache(float* out, int64_t max_pos, int64_t rope_dim,
+extern "C" int32_t mla_rope_cos_sin_cache(double* out, int64_t max_pos, int64_t rope_dim,
                                           double base, mla_stream_t stream) {
   static const char* fn = "mla_rope_cos_sin_cache";
   clear_error();
@@ -250,7 +246,7 @@ extern "C" int32_t mla_rope_cos_sin_cache(float* out, int64_t max_pos, int64_t r
 
 extern "C" int32_t mla_ctx_kv_epilogue(
     const void* all_kv, int64_t kv_layer_stride, int64_t kv_token_stride, const void* gamma,
-    float eps, const int64_t* positions, const float* cos_sin, int64_t max_pos,
+    float eps, const int64_t* positions, const double* cos_sin, int64_t max_pos,
     const int64_t* kv_cache_ptrs, const float* kv_scales, const int64_t* slot_mapping,
     int64_t slot_layer_stride, int64_t num_layers, int64_t num_tokens, int64_t kv_lora_rank,
     int64_t pe_dim, int64_t block_size, int64_t block_stride, int64_t entry_stride,

@@ -85,6 +85,54 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
+// float64 -> bf16 bits, rounded once to nearest even (as if directly): the
+// conversion to fp32 is made round-to-odd (an inexact result is truncated
+// toward zero and its last bit set), so the second rounding, fp32 -> bf16,
+// cannot land on a tie the first one created.  NaN -> quiet NaN with sign.
+__device__ __forceinline__ uint32_t f64_to_bf16_bits(double d) {
+  const float f = static_cast<float>(d);
+  uint32_t u = __float_as_uint(f);
+  const double back = static_cast<double>(f);
+  if (back != d && d == d) {
+    if (__builtin_fabs(back) > __builtin_fabs(d)) u -= 1u;  // toward zero
+    u |= 1u;
+  }
+  return f32_to_bf16_bits(__uint_as_float(u));
+}
+
+// Rotary embedding of one lane's 4 values of a 64-wide rope row,
+// non-interleaved pairs (i, i + 32) ("PR #50585 完整报告", 关键源码片段: RoPE
+// of k_pe at the token's position; the formula itself is elided there):
+//   first half  (x = x_i,      p = x_{i+32}):  y_i      = x_i cos_i - x_{i+32} sin_i
+//   second half (x = x_{i+32}, p = x_i):       y_{i+32} = x_{i+32} cos_i + x_i sin_i
+// Each product and the sum are float64 operations (bf16 inputs make the
+// conversions exact; contraction is off so every operation rounds on its
+// own), then one rounding to bf16.  Cancellation between the two products
+// costs float64 digits, not bf16 ones.  c / s: float64 cos / sin of the
+// lane's 4 angles.
+__device__ __forceinline__ uint2 rope4_f64(const float* x, const float* p, const double* c,
+                                           const double* s, bool first) {
+#pragma clang fp contract(off)
+  uint32_t b[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const double u = static_cast<double>(x[e]) * c[e];
+    const double v = static_cast<double>(p[e]) * s[e];
+    b[e] = f64_to_bf16_bits(first ? u - v : u + v);
+  }
+  return make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+}
+
+// Four float64 values from 32 contiguous, 16-byte aligned bytes.
+__device__ __forceinline__ void ld_f64x4(const double* p, double* out) {
+  const uint4 a = *reinterpret_cast<const uint4*>(p);
+  const uint4 b = *reinterpret_cast<const uint4*>(p + 2);
+  out[0] = __hiloint2double(a.y, a.x);
+  out[1] = __hiloint2double(a.w, a.z);
+  out[2] = __hiloint2double(b.y, b.x);
+  out[3] = __hiloint2double(b.w, b.z);
+}
+
 // fp32 -> bf16 with the gfx950 converter (round to nearest even), two at a
 // time.  Used where a NaN's payload and sign are not part of the contract.
 typedef float f32x2_t __attribute__((ext_vector_type(2)));

@@ -8,6 +8,7 @@
  *   insert      mla_kv_insert_grouped  [kv_c | k_pe] -> fp8/bf16 -> paged caches, all layers
  *   gather      mla_ctx_latent_gather  paged cache rows -> contiguous bf16 (or raw fp8) workspace
  *   pack        mla_ctx_kv_pack        [k_nope | k_pe] full key (+ fp8 V), contiguous
+ *               mla_ctx_kv_pack_gather the pack of one chunk and the gather of the next, one launch
  *   merge       mla_ctx_merge_chunk    chunk attention partials -> accumulator (log-sum-exp)
  *   new tokens  mla_new_token_epilogue RoPE(q_pe, k_pe) -> query row, full key (+ fp8 V),
  *                                      and the cache insert of [kv_c | RoPE(k_pe)]
@@ -164,16 +165,18 @@ int32_t mla_kv_insert_grouped(
     int32_t kv_cache_dtype, mla_stream_t stream);
 
 /* ------------------------------------------------------------------------
- * mla_rope_cos_sin_cache -- fill the rotary table used by the epilogue.
- * out (device fp32 [max_pos, rope_dim]) row p = cos(theta_0..theta_{d/2-1})
+ * mla_rope_cos_sin_cache -- fill the rotary table used by the epilogues.
+ * out (device float64 [max_pos, rope_dim]) row p = cos(theta_0..theta_{d/2-1})
  * followed by sin(theta_0..theta_{d/2-1}), theta_i = p * base^(-2i/d),
- * evaluated in float64 on the device and rounded to fp32.
+ * evaluated in float64 on the device.  The epilogues rotate in float64
+ * with these values and round each result once to bf16, so a rotation
+ * whose two products nearly cancel still rounds correctly.
  * ([P2] 关键源码片段: RoPE of k_pe at each context position, the positions
  * being the same for every layer; the formula itself is not printed, the
  * non-interleaved form with the given base is the reading taken.)
  * rope_dim must be even and > 0; max_pos >= 0.
  * ------------------------------------------------------------------------ */
-int32_t mla_rope_cos_sin_cache(float* out, int64_t max_pos, int64_t rope_dim,
+int32_t mla_rope_cos_sin_cache(double* out, int64_t max_pos, int64_t rope_dim,
                                double base, mla_stream_t stream);
 
 /* ------------------------------------------------------------------------
@@ -188,10 +191,11 @@ int32_t mla_rope_cos_sin_cache(float* out, int64_t max_pos, int64_t rope_dim,
  * gamma   device bf16 [num_layers, kv_lora_rank] (row l = layer l's norm weight).
  * eps     RMSNorm epsilon.
  * positions device int64 [num_tokens], each in [0, max_pos).
- * cos_sin device fp32 [max_pos, pe_dim] from mla_rope_cos_sin_cache.
+ * cos_sin device float64 [max_pos, pe_dim] from mla_rope_cos_sin_cache.
  * For each (l, t):
  *   row[0:R]   = bf16(x_i * (mean(x^2) + eps)^(-1/2) * gamma[l, i])  (fp32 math)
- *   row[R:R+P] = bf16(rotation of k_pe by theta(positions[t]))   (pairs (i, i+P/2))
+ *   row[R:R+P] = bf16(rotation of k_pe by theta(positions[t]))   (pairs (i, i+P/2);
+ *                float64 math, one rounding)
  *   then row is inserted exactly as mla_kv_insert_grouped inserts [kv_c | k_pe].
  * dbg_rows  optional device bf16 [L, T, R+P] contiguous: receives every row
  *   (also those whose slot is negative); NULL to skip.
@@ -201,7 +205,7 @@ int32_t mla_rope_cos_sin_cache(float* out, int64_t max_pos, int64_t rope_dim,
  * ------------------------------------------------------------------------ */
 int32_t mla_ctx_kv_epilogue(
     const void* all_kv, int64_t kv_layer_stride, int64_t kv_token_stride,
-    const void* gamma, float eps, const int64_t* positions, const float* cos_sin,
+    const void* gamma, float eps, const int64_t* positions, const double* cos_sin,
     int64_t max_pos,
     const int64_t* kv_cache_ptrs, const float* kv_scales,
     const int64_t* slot_mapping, int64_t slot_layer_stride,
@@ -300,6 +304,37 @@ int32_t mla_ctx_kv_pack(const void* k_nope, int64_t kn_tok_stride,
                         mla_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * mla_ctx_kv_pack_gather -- one launch doing the pack of context chunk c and
+ * the latent gather of chunk c + 1 ([P1] 实现拆解 item 2: every chunk first
+ * gathers its latent rows from the cache, then runs kv_b_proj, then packs;
+ * the pack of chunk c needs nothing from chunk c + 1 and the gather of
+ * chunk c + 1 needs nothing from chunk c, so in a chunk loop
+ *   gather(0); kv_b_proj(0); pack(0) + gather(1); kv_b_proj(1); pack(1) + gather(2); ...
+ * is the same computation with one launch fewer per chunk).
+ * The first 19 arguments are those of mla_ctx_kv_pack (without max_blocks:
+ * the launch has one thread per output chunk), the next 11 those of
+ * mla_ctx_latent_gather (without max_blocks).  Result: identical to
+ *   mla_ctx_kv_pack(pack arguments, 0, stream);
+ *   mla_ctx_latent_gather(gather arguments, 0, stream);
+ * Each part is validated as its own entry point validates it, before
+ * anything is launched.  In addition gather_out must not overlap k_nope,
+ * k_pe, v, key_out or v_out (MLA_ERR_INVALID_ARGUMENT; checked on the
+ * address ranges the views span): the two parts run concurrently.  When both
+ * parts have work, the pack's sources must be bf16 with a 16-bit k_pe (modes
+ * KEY_BF16 and KEY_V_FP8; MLA_ERR_UNSUPPORTED otherwise -- call the two entry
+ * points); when one part is empty the other runs as its own entry point.
+ * ------------------------------------------------------------------------ */
+int32_t mla_ctx_kv_pack_gather(
+    const void* k_nope, int64_t kn_tok_stride, int64_t kn_head_stride, const void* k_pe,
+    int64_t kpe_tok_stride, const void* v, int64_t v_tok_stride, int64_t v_head_stride,
+    int64_t num_tokens, int64_t num_heads, int64_t nope, int64_t rope, int64_t vdim,
+    int32_t mode, int32_t src_dtype, const float* k_scale, const float* v_scale, void* key_out,
+    void* v_out, const void* cache, int32_t cache_dtype, const float* cache_scale,
+    int64_t block_size, int64_t block_stride, int64_t entry_stride, const int64_t* src_slots,
+    int64_t gather_tokens, int64_t width, int32_t out_dtype, void* gather_out,
+    mla_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * mla_ctx_merge_chunk -- fold one context chunk's attention partial into the
  * accumulator of the chunked-context loop ([P1] 实现拆解 item 3: the
  * accumulator is allocated before any chunk; a non-continuation chunk may
@@ -351,7 +386,7 @@ int32_t mla_ctx_neutralize_partials(void* out, int64_t out_tok_stride, int64_t o
  * elsewhere in this library:
  *   pe_q = RoPE(q_pe[t, h, :], pos[t]),  pe_k = RoPE(k_pe[t, :], pos[t])
  *            (half-split rotation, angles from cos_sin as in
- *            mla_ctx_kv_epilogue; fp32 math, each result rounded to bf16)
+ *            mla_ctx_kv_epilogue; float64 math, each result rounded once to bf16)
  *   q_out[t, h, :]   = [q_nope[t, h, :] | pe_q]
  *   key_out[t, h, :] = [k_nope[t, h, :] | pe_k]     (same pe_k for every head)
  *   v_out[t, h, :]   = v[t, h, :]                    (KEY_V_FP8 only)
@@ -367,7 +402,7 @@ int32_t mla_ctx_neutralize_partials(void* out, int64_t out_tok_stride, int64_t o
  *   (q_nope, q_pe, k_nope, v), [t, i] at t*tok_stride + i (kv_c, k_pe).
  * positions   device int64 [T], each in [0, max_pos) (precondition; values
  *             outside are clamped to that range).
- * cos_sin     device fp32 [max_pos, rope] = cos of the rope/2 angles | their
+ * cos_sin     device float64 [max_pos, rope] = cos of the rope/2 angles | their
  *             sin (mla_rope_cos_sin_cache fills it).
  * cache       device; element type from cache_dtype (AUTO/BF16, FP8_E4M3,
  *             FP8_E5M2); cache_scale device fp32 [1] for an fp8 cache, NULL
@@ -384,7 +419,7 @@ int32_t mla_new_token_epilogue(
     int64_t qp_tok_stride, int64_t qp_head_stride, const void* k_nope, int64_t kn_tok_stride,
     int64_t kn_head_stride, const void* v, int64_t v_tok_stride, int64_t v_head_stride,
     const void* kv_c, int64_t kv_c_tok_stride, const void* k_pe, int64_t k_pe_tok_stride,
-    const int64_t* positions, const float* cos_sin, int64_t max_pos, int64_t num_tokens,
+    const int64_t* positions, const double* cos_sin, int64_t max_pos, int64_t num_tokens,
     int64_t num_heads, int64_t nope, int64_t rope, int64_t vdim, int64_t kv_lora_rank,
     int32_t mode, const float* q_scale, const float* k_scale, const float* v_scale,
     void* q_out, void* key_out, void* v_out, void* cache, int32_t cache_dtype,

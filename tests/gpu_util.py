@@ -1,4 +1,7 @@
 """Helpers shared by the GPU parity tests (no method arithmetic here)."""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -68,3 +71,26 @@ def check_slots(slot_mapping, num_slots):
     for row in sm:
         v = row[row >= 0]
         assert v.unique().numel() == v.numel(), "duplicate slot in one layer"
+
+
+def host_threads():
+    """Host threads for slicing oracle work: the CPUs this process may use,
+    at most 16 (one GPU's share of a shared host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def run_sliced(fn, n, parts=None):
+    """fn(lo, hi) over disjoint consecutive slices of range(n), run on host
+    threads (the oracle's C calls release the GIL, so slices run in
+    parallel); the results come back in slice order.  Only the work is
+    split: each slice is the oracle's own call on that slice."""
+    parts = parts or 4 * host_threads()
+    edges = np.linspace(0, n, max(1, min(parts, n)) + 1).astype(np.int64)
+    spans = [(int(a), int(b)) for a, b in zip(edges[:-1], edges[1:]) if b > a]
+    with ThreadPoolExecutor(host_threads()) as ex:
+        futs = [ex.submit(fn, a, b) for a, b in spans]
+        return [f.result() for f in futs]

@@ -180,6 +180,44 @@ def test_gather_rejects_bad_arguments(mk, kw, status, msg):
     assert msg in mk.last_error()
 
 
+P_GATHER_OUT = 1 << 44   # a fake, 16-byte aligned address far from P16's ranges
+
+
+def pack_gather_call(mk, pack=None, gather=None):
+    a = dict(kn=P16, kn_ts=16384, kn_hs=256, kpe=P16 + 1024, kpe_ts=576, v=P16 + 256,
+             v_ts=16384, v_hs=256, T=8192, H=64, nope=128, rope=64, vdim=128,
+             mode=mk.MLA_PACK_KEY_V_FP8, src=mk.MLA_KV_BF16, ks=None, vs=None,
+             key=P16 + (1 << 32), vo=P16 + (1 << 33))
+    a.update(pack or {})
+    g = dict(cache=P16, dt=mk.MLA_KV_FP8_E4M3, scale=P16, bs=64, bstride=64 * 576,
+             estride=576, slots=P16, T=8192, width=576, odt=mk.MLA_KV_BF16, out=P_GATHER_OUT)
+    g.update(gather or {})
+    return mk.lib().mla_ctx_kv_pack_gather(
+        a["kn"], a["kn_ts"], a["kn_hs"], a["kpe"], a["kpe_ts"], a["v"], a["v_ts"], a["v_hs"],
+        a["T"], a["H"], a["nope"], a["rope"], a["vdim"], a["mode"], a["src"], a["ks"], a["vs"],
+        a["key"], a["vo"], g["cache"], g["dt"], g["scale"], g["bs"], g["bstride"], g["estride"],
+        g["slots"], g["T"], g["width"], g["odt"], g["out"], None)
+
+
+@pytest.mark.parametrize("pack,gather,status,msg", [
+    (dict(mode=7), None, 1, "unknown mode"),
+    (dict(nope=120), None, 2, "multiples of 16"),
+    (None, dict(scale=None), 1, "needs cache_scale"),
+    (None, dict(width=40), 2, "multiple of 16"),
+    (None, dict(out=P16 + (1 << 32) + 4096), 1, "overlaps"),    # inside key_out
+    (None, dict(out=P16 + 512), 1, "overlaps"),                  # inside the kv_b_proj rows
+    (dict(mode=2, kpe_ts=576), None, 2, "joint launch"),         # verbatim fp8 k_pe
+    (dict(src=4), None, 2, "joint launch"),                       # fp16 sources
+])
+def test_pack_gather_rejects_bad_arguments(mk, pack, gather, status, msg):
+    assert pack_gather_call(mk, pack, gather) == status
+    assert msg in mk.last_error()
+
+
+def test_pack_gather_both_parts_empty_is_a_noop(mk):
+    assert pack_gather_call(mk, dict(T=0), dict(T=0)) == mk.MLA_OK
+
+
 def test_rope_table_rejects(mk):
     assert mk.lib().mla_rope_cos_sin_cache(P16, 10, 63, 10000.0, None) == mk.MLA_ERR_INVALID_ARGUMENT
     assert mk.lib().mla_rope_cos_sin_cache(P16, 10, 64, -1.0, None) == mk.MLA_ERR_INVALID_ARGUMENT

@@ -35,8 +35,9 @@ def test_long_context_insert_bytes_match_the_workload():
 
 def test_new_token_bytes_are_mode_specific_sums():
     T, H = 8192, 64
-    fp8 = T * H * (384 + 256 + 256 + 192 + 192 + 128) + T * (1152 + 8 + 8 + 256) + (T - 1) * 576
-    bf16 = T * H * (384 + 256 + 384 + 384) + T * (1152 + 8 + 8 + 256) + (T - 1) * 576
+    # per token: latent row, position, slot and the float64 cos/sin row (512 B)
+    fp8 = T * H * (384 + 256 + 256 + 192 + 192 + 128) + T * (1152 + 8 + 8 + 512) + (T - 1) * 576
+    bf16 = T * H * (384 + 256 + 384 + 384) + T * (1152 + 8 + 8 + 512) + (T - 1) * 576
     assert bench.new_token_bytes(T, H, True, T - 1) == fp8
     assert bench.new_token_bytes(T, H, False, T - 1) == bf16
 

@@ -5,8 +5,11 @@ Workloads: the chunked-context pack (fp8 cache [512, 64, 576] at scale 0.5
 holding 8192 tokens in shuffled blocks; kv_b_proj output [8192, 64, 256];
 bf16 key and fp8 key + V), the test matrix of PR #51772 report (评论区精华:
 num_heads 3 and 4, num_tokens including 0), grid caps 1 / 7 / default, the
-gather -> pack chain, and the long-context pack (131072 tokens as 16 chunks
-of 8192 through the capped grid), sampled against the oracle.
+gather -> pack chain, the chunked-context pack at full size, and the
+long-context pack (131072 tokens as 16 chunks of 8192, on the default grid,
+on the capped grid-stride grid and through the joint pack + next-gather
+launch), the joint launch for every gather kind and pack mode, every output
+byte against the oracle.
 """
 import numpy as np
 import pytest
@@ -14,7 +17,7 @@ import torch
 
 import oracle
 from fp8_paged_insert_amd import synth
-from gpu_util import DEV, announce, requires_gpu, u16, u8
+from gpu_util import DEV, announce, requires_gpu, run_sliced, u16, u8
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
@@ -137,10 +140,19 @@ def test_pack_fp8_with_scales(mk):
         assert np.array_equal(u8(key), rk) and np.array_equal(u8(vo), rv), (ks, vs)
 
 
+def oracle_pack_full(kvb_np, kpe_np, fp8):
+    """The oracle's pack over every token, token slices on host threads."""
+    parts = run_sliced(lambda a, b: oracle_pack(kvb_np[a:b], kpe_np[a:b], fp8),
+                       kvb_np.shape[0])
+    key = np.concatenate([p[0] for p in parts])
+    return key, (np.concatenate([p[1] for p in parts]) if fp8 else None)
+
+
+@pytest.mark.timeout(300)
 @pytest.mark.parametrize("fp8", [False, True])
-def test_pack_context_workload_sampled(mk, fp8):
-    """8192 tokens x 64 heads at full size: 192 sampled tokens against the
-    oracle, plus the k_pe broadcast over heads checked on every token."""
+def test_pack_context_workload_full(mk, fp8):
+    """8192 tokens x 64 heads at full size, every output byte against the
+    oracle; the k_pe broadcast over heads checked on its own as well."""
     announce("pack C4 full", fp8)
     d = synth.context_pack()
     kvb = d["kvb"].to(DEV)
@@ -148,13 +160,10 @@ def test_pack_context_workload_sampled(mk, fp8):
     key, vo = gpu_pack(mk, kvb, ws[:, 512:], fp8)
     torch.cuda.synchronize()
     assert torch.equal(key[:, :, 128:], key[:, :1, 128:].expand_as(key[:, :, 128:]))
-    g = torch.Generator().manual_seed(5)
-    pick = torch.randperm(8192, generator=g)[:192]
-    rk, rv = oracle_pack(u16(d["kvb"][pick]), u16(d["workspace"][pick])[:, 512:], fp8)
-    got_k = u8(key[pick.to(DEV)]) if fp8 else u16(key[pick.to(DEV)])
-    assert np.array_equal(got_k, rk)
+    rk, rv = oracle_pack_full(u16(d["kvb"]), u16(d["workspace"])[:, 512:], fp8)
+    assert np.array_equal(u8(key) if fp8 else u16(key), rk)
     if fp8:
-        assert np.array_equal(u8(vo[pick.to(DEV)]), rv)
+        assert np.array_equal(u8(vo), rv)
 
 
 @pytest.mark.parametrize("fp8", [False, True])
@@ -173,31 +182,126 @@ def test_gather_then_pack_chain(mk, fp8):
         assert np.array_equal(u8(vo), rv)
 
 
-def test_long_context_pack_16_chunks_sampled(mk):
-    """131072 context tokens in a [4096, 64, 576] cache, 16 chunks of 8192:
-    gather + fp8 pack per chunk; 16 sampled tokens per chunk vs the oracle."""
-    announce("long-context pack 16 chunks")
+@pytest.mark.timeout(600)
+def test_long_context_pack_16_chunks_full(mk):
+    """131072 context tokens in a [4096, 64, 576] cache, 16 chunks of 8192.
+    Per chunk, on the GPU: the gather, the fp8 pack on the default grid and on
+    a capped grid of 16 workgroups per compute unit (a grid-stride loop of
+    several passes), and the chunk loop with the joint launch (pack of chunk
+    c + gather of chunk c + 1 into the other of two workspaces).  Every
+    workspace row and every key and V byte of every chunk, from each path,
+    against the oracle's gather -> pack of the same cache."""
+    announce("long-context pack 16 chunks, full")
     d = synth.context_cache(seed=55, num_blocks=4096, num_ctx=131072)
     cache, slots = d["cache"].to(DEV), d["src_slots"].to(DEV)
+    cache_np, slots_np = d["cache"].numpy(), d["src_slots"].numpy()
+    cap = 16 * torch.cuda.get_device_properties(DEV).multi_processor_count
     gk = torch.Generator(device=DEV)
     gk.manual_seed(555)
-    g = torch.Generator().manual_seed(56)
     ws = torch.empty(8192, 576, dtype=torch.bfloat16, device=DEV)
-    key = torch.empty(8192, 64, 192, dtype=torch.uint8, device=DEV)
-    vo = torch.empty(8192, 64, 128, dtype=torch.uint8, device=DEV)
+    ws2 = [torch.empty(8192, 576, dtype=torch.bfloat16, device=DEV) for _ in range(2)]
+    outs = {k: (torch.empty(8192, 64, 192, dtype=torch.uint8, device=DEV),
+                torch.empty(8192, 64, 128, dtype=torch.uint8, device=DEV))
+            for k in ("default grid", "capped grid", "joint launch")}
+    sc = torch.tensor([0.5], device=DEV)
+    chunk = lambda c: slots[c * 8192:(c + 1) * 8192]
+    mk.mla_ctx_latent_gather(cache, chunk(0), ws2[0], sc, "fp8")
     for c in range(16):
         kvb = torch.randn(8192, 64, 256, generator=gk, device=DEV).to(torch.bfloat16)
-        mk.mla_ctx_latent_gather(cache, slots[c * 8192:(c + 1) * 8192], ws,
-                                 torch.tensor([0.5], device=DEV), "fp8")
-        mk.mla_ctx_kv_pack(kvb[..., :128], ws[:, 512:], key, v=kvb[..., 128:], v_out=vo,
-                           mode=mk.MLA_PACK_KEY_V_FP8)
-        pick = torch.randperm(8192, generator=g)[:16]
-        sl = d["src_slots"][c * 8192:(c + 1) * 8192][pick].numpy()
-        ref_ws = oracle.gather(d["cache"].numpy(), sl, 0.5)
-        rk, rv = oracle_pack(u16(kvb[pick.to(DEV)]), ref_ws[:, 512:], True)
+        kn, v = kvb[..., :128], kvb[..., 128:]
+        mk.mla_ctx_latent_gather(cache, chunk(c), ws, sc, "fp8")
+        k, vo = outs["default grid"]
+        mk.mla_ctx_kv_pack(kn, ws[:, 512:], k, v=v, v_out=vo, mode=mk.MLA_PACK_KEY_V_FP8)
+        k, vo = outs["capped grid"]
+        mk.mla_ctx_kv_pack(kn, ws[:, 512:], k, v=v, v_out=vo, mode=mk.MLA_PACK_KEY_V_FP8,
+                           max_blocks=cap)
         torch.cuda.synchronize()
-        assert np.array_equal(u8(key[pick.to(DEV)]), rk), c
-        assert np.array_equal(u8(vo[pick.to(DEV)]), rv), c
+        joint_ws = u16(ws2[c % 2])            # gathered by the previous joint launch
+        k, vo = outs["joint launch"]
+        if c < 15:
+            mk.mla_ctx_kv_pack_gather(kn, ws2[c % 2][:, 512:], k, cache, chunk(c + 1),
+                                      ws2[(c + 1) % 2], v=v, v_out=vo,
+                                      mode=mk.MLA_PACK_KEY_V_FP8, cache_scale=sc)
+        else:
+            mk.mla_ctx_kv_pack(kn, ws2[c % 2][:, 512:], k, v=v, v_out=vo,
+                               mode=mk.MLA_PACK_KEY_V_FP8)
+        torch.cuda.synchronize()
+        sl = slots_np[c * 8192:(c + 1) * 8192]
+        ref_ws = np.concatenate(run_sliced(lambda a, b: oracle.gather(cache_np, sl[a:b], 0.5),
+                                           8192))
+        assert np.array_equal(u16(ws), ref_ws), f"chunk {c}: workspace"
+        assert np.array_equal(joint_ws, ref_ws), f"chunk {c}: workspace of the joint launch"
+        rk, rv = oracle_pack_full(u16(kvb), ref_ws[:, 512:], True)
+        for name, (k, vo) in outs.items():
+            assert np.array_equal(u8(k), rk), f"chunk {c}: key, {name}"
+            assert np.array_equal(u8(vo), rv), f"chunk {c}: V, {name}"
+        announce(f"chunk {c}: identical")
+
+
+@pytest.mark.parametrize("kind", ["fp8", "fp8_e5m2", "bfloat16", "raw"])
+@pytest.mark.parametrize("mode", ["bf16", "fp8", "fp8_scaled"])
+def test_pack_gather_joint_launch(mk, kind, mode):
+    """The joint launch against the oracle's pack of one chunk and gather of
+    the next, for every gather kind and both 16-bit-source pack modes, on a
+    ragged shape (300 tokens x 3 heads packed, 437 tokens gathered)."""
+    announce("pack + gather joint launch", kind, mode)
+    g = torch.Generator().manual_seed(300 + len(kind) + len(mode))
+    T, H, Tg = 300, 3, 437
+    kvb = synth.bf16_normal((T, H, 256), g, std=40.0 if mode == "fp8_scaled" else 1.0)
+    ws = synth.bf16_normal((T, 576), g)
+    if kind == "bfloat16":
+        cache = synth.random_bf16_bits((16, 64, 576), g)
+        cache_np = u16(cache).reshape(16, 64, 576)
+    else:
+        cache = synth.random_bytes((16, 64, 576), g)
+        cache_np = cache.numpy()
+    blocks = torch.randperm(16, generator=g)[:7]
+    sl = synth.block_table_slots(blocks, 64, Tg)
+    dkvb, dws = kvb.to(DEV), ws.to(DEV)
+    fp8 = mode != "bf16"
+    key = torch.empty(T, H, 192, dtype=torch.uint8 if fp8 else torch.bfloat16, device=DEV)
+    vo = torch.empty(T, H, 128, dtype=torch.uint8, device=DEV) if fp8 else None
+    out = torch.empty(Tg, 576, dtype=torch.uint8 if kind == "raw" else torch.bfloat16,
+                      device=DEV)
+    ks = torch.tensor([0.7312], device=DEV) if mode == "fp8_scaled" else None
+    vs = torch.tensor([1.37], device=DEV) if mode == "fp8_scaled" else None
+    cs = None if kind in ("bfloat16", "raw") else torch.tensor([0.8125], device=DEV)
+    dt = {"raw": "fp8", "fp8": "fp8", "fp8_e5m2": "fp8_e5m2", "bfloat16": "bfloat16"}[kind]
+    kw = dict(v=dkvb[..., 128:], v_out=vo, mode=mk.MLA_PACK_KEY_V_FP8, k_scale=ks,
+              v_scale=vs) if fp8 else {}
+    mk.mla_ctx_kv_pack_gather(dkvb[..., :128], dws[:, 512:], key, cache.to(DEV), sl.to(DEV), out,
+                              cache_scale=cs, kv_cache_dtype=dt, **kw)
+    torch.cuda.synchronize()
+    fmt = "e5m2" if kind == "fp8_e5m2" else "e4m3"
+    ref_g = oracle.gather(cache_np, sl.numpy(), 0.8125 if cs is not None else 1.0,
+                          raw=kind == "raw", fp8_format=fmt)
+    assert np.array_equal(u8(out) if kind == "raw" else u16(out), ref_g), "gather part"
+    rk, rv = oracle_pack(u16(kvb), u16(ws)[:, 512:], fp8, 0.7312 if ks is not None else 1.0,
+                         1.37 if vs is not None else 1.0)
+    assert np.array_equal(u8(key) if fp8 else u16(key), rk), "pack key"
+    if fp8:
+        assert np.array_equal(u8(vo), rv), "pack V"
+
+
+@pytest.mark.timeout(300)
+def test_pack_gather_joint_launch_context_workload(mk):
+    """The chunked-context shape (8192 tokens x 64 heads packed, 8192 tokens
+    gathered from a [512, 64, 576] fp8 cache): every byte against the oracle."""
+    announce("pack + gather joint launch, C4 shape")
+    d = synth.context_pack()
+    kvb, ws = d["kvb"].to(DEV), d["workspace"].to(DEV)
+    key = torch.empty(8192, 64, 192, dtype=torch.uint8, device=DEV)
+    vo = torch.empty(8192, 64, 128, dtype=torch.uint8, device=DEV)
+    out = torch.empty(8192, 576, dtype=torch.bfloat16, device=DEV)
+    mk.mla_ctx_kv_pack_gather(kvb[..., :128], ws[:, 512:], key, d["cache"].to(DEV),
+                              d["src_slots"].to(DEV), out, v=kvb[..., 128:], v_out=vo,
+                              mode=mk.MLA_PACK_KEY_V_FP8,
+                              cache_scale=torch.tensor([0.5], device=DEV))
+    torch.cuda.synchronize()
+    ref_g = oracle.gather(d["cache"].numpy(), d["src_slots"].numpy(), 0.5)
+    assert np.array_equal(u16(out), ref_g)
+    rk, rv = oracle_pack_full(u16(d["kvb"]), u16(d["workspace"])[:, 512:], True)
+    assert np.array_equal(u8(key), rk) and np.array_equal(u8(vo), rv)
 
 
 def test_launch_events_bracket_one_kernel(mk):
