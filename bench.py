@@ -42,6 +42,16 @@ def insert_bytes(layers, tokens, valid_rows=None, cache_elem=1):
             + valid * W * cache_elem)
 
 
+def small_insert_bytes(valid_rows, slot_entries, layers, fp8):
+    """Algorithmic bytes of a small-batch insert: only the rows that are
+    written need their inputs read (a skipped token moves nothing); plus the
+    slot entries, and for fp8 the per-layer scale and cache pointer.
+    5 layers x 4 tokens with one -1 (fp8): 15 x (1152 + 576) + 32 + 20 + 40 =
+    26,012 B; one layer x 16 tokens (bf16): 16 x (1152 + 1152) + 128 = 36,992 B."""
+    return (valid_rows * W * 2 + valid_rows * W * (1 if fp8 else 2) + slot_entries * 8
+            + (layers * 12 if fp8 else 0))
+
+
 def gather_bytes(tokens, width=W):
     """Read one fp8 cache row and one slot per token; write a bf16 row."""
     return tokens * width + tokens * 8 + 4 + tokens * width * 2
@@ -74,12 +84,12 @@ def merge_bytes(tokens, heads, head_dim=128):
 def new_token_bytes(tokens, heads, fp8, valid_rows, cache_elem=1, nope=128, rope=64, vdim=128):
     """Read the query [T, H, nope+rope], k_nope (and v in fp8 mode) from their
     strided views, the latent row [kv_c | k_pe], the position, the slot and
-    the float64 cos/sin row of each token; write the query and key rows (and fp8 V)
+    the fp32 cos/sin row of each token; write the query and key rows (and fp8 V)
     and one cache entry per valid token."""
     ob = 1 if fp8 else 2
     per_row = (nope + rope) * 2 + nope * 2 + (vdim * 2 if fp8 else 0)
     per_row += 2 * (nope + rope) * ob + (vdim if fp8 else 0)
-    per_tok = (R + P) * 2 + 8 + 8 + P * 8
+    per_tok = (R + P) * 2 + 8 + 8 + P * 4
     return tokens * heads * per_row + tokens * per_tok + valid_rows * W * cache_elem
 
 
@@ -89,9 +99,11 @@ def pack_bf16_bytes(tokens, heads, nope=128, rope=64):
 
 def epilogue_bytes(layers, tokens):
     """Read the [T, L, 576] projection output, slots, positions, gamma, the
-    float64 cos/sin rows of the positions used; write one fp8 entry per row."""
+    fp32 cos/sin rows of the positions used (the rotation's fast path reads
+    only those; the low-order table words are read where it falls back);
+    write one fp8 entry per row."""
     return (tokens * layers * W * 2 + layers * tokens * 8 + tokens * 8 + layers * R * 2
-            + tokens * P * 8 + layers * 8 + layers * tokens * W)
+            + tokens * P * 4 + layers * 8 + layers * tokens * W)
 
 
 # --------------------------------------------------------------- workload --
@@ -118,6 +130,7 @@ class LongContext:
         self.kvb = [synth.kv_b_proj_output(chunk, g2, dev, heads=heads)
                     for _ in range(num_ctx // chunk)]
         self.ws = torch.empty(chunk, W, dtype=torch.bfloat16, device=dev)
+        self.ws2 = [torch.empty(chunk, W, dtype=torch.bfloat16, device=dev) for _ in range(2)]
         self.key = torch.empty(chunk, heads, 192, dtype=torch.uint8, device=dev)
         self.v8 = torch.empty(chunk, heads, 128, dtype=torch.uint8, device=dev)
         self.pack_events = []
@@ -141,26 +154,48 @@ class LongContext:
         return (insert_bytes(L, self.T) + n * gather_bytes(self.chunk)
                 + n * pack_fp8_bytes(self.chunk, self.heads))
 
-    def step(self, time_pack=False, max_blocks=0):
-        """One pass over the workload, in order on the current stream.  (Issuing
-        chunk c + 1's gather on a side stream during chunk c's pack measured
-        slower on MI355X: the cross-stream waits cost more than they hide.)"""
-        mk, torch = self.mk, self.torch
+    def step(self, time_pack=False):
+        """One pass over the workload, in order on the current stream: the
+        grouped insert, then the chunk loop with the joint launch -- gather of
+        chunk 0, then for every chunk c the pack of c together with the gather
+        of c + 1 into the other workspace (the last chunk packs alone).  With
+        time_pack, one joint launch per step (the chunk index rotating)
+        records its own start and end events."""
+        mk = self.mk
         mk.mla_kv_insert_grouped(self.kv_c, self.k_pe, self.ptrs, self.slots, 64, 64 * W, W,
                                  self.scales, "fp8")
+        n = len(self.kvb)
         if time_pack:
-            self.timed_chunk = (self.timed_chunk + 1) % len(self.kvb)
+            self.timed_chunk = (self.timed_chunk + 1) % (n - 1)
+        mk.mla_ctx_latent_gather(self.ctx_cache, self.src_slots[:self.chunk], self.ws2[0],
+                                 self.ctx_scale, "fp8")
+        for c, kvb in enumerate(self.kvb):
+            ws = self.ws2[c % 2]
+            if c + 1 < n:
+                if time_pack and c == self.timed_chunk:
+                    e0, e1 = self.event_pool.pop()
+                    mk.set_launch_events(e0, e1)
+                    self.pack_events.append((e0, e1))
+                nxt = self.src_slots[(c + 1) * self.chunk:(c + 2) * self.chunk]
+                mk.mla_ctx_kv_pack_gather(kvb[..., :128], ws[:, 512:], self.key, self.ctx_cache,
+                                          nxt, self.ws2[(c + 1) % 2], v=kvb[..., 128:],
+                                          v_out=self.v8, mode=mk.MLA_PACK_KEY_V_FP8,
+                                          cache_scale=self.ctx_scale)
+            else:
+                mk.mla_ctx_kv_pack(kvb[..., :128], ws[:, 512:], self.key, v=kvb[..., 128:],
+                                   v_out=self.v8, mode=mk.MLA_PACK_KEY_V_FP8)
+
+    def step_separate(self, max_blocks=0):
+        """The same work with the gather and the pack of every chunk as launches
+        of their own (max_blocks > 0: both as grid-stride loops over a capped
+        grid)."""
+        mk = self.mk
+        mk.mla_kv_insert_grouped(self.kv_c, self.k_pe, self.ptrs, self.slots, 64, 64 * W, W,
+                                 self.scales, "fp8")
         for c, kvb in enumerate(self.kvb):
             mk.mla_ctx_latent_gather(self.ctx_cache,
                                      self.src_slots[c * self.chunk:(c + 1) * self.chunk],
                                      self.ws, self.ctx_scale, "fp8", max_blocks=max_blocks)
-            if time_pack and c == self.timed_chunk:
-                # events recorded by the pack kernel itself as it starts and ends
-                # (one chunk per step, rotating, so arming them costs the step
-                # one launch's worth of overhead, not sixteen)
-                e0, e1 = self.event_pool.pop()
-                mk.set_launch_events(e0, e1)
-                self.pack_events.append((e0, e1))
             mk.mla_ctx_kv_pack(kvb[..., :128], self.ws[:, 512:], self.key, v=kvb[..., 128:],
                                v_out=self.v8, mode=mk.MLA_PACK_KEY_V_FP8, max_blocks=max_blocks)
 
@@ -181,7 +216,7 @@ def time_kernel(torch, fn, reps=50, warmup=5):
     return statistics.median(times)
 
 
-PACK_TRAFFIC = os.path.join(ROOT, "profiles", "pack_fp8_long_context_hbm_traffic.json")
+TRAFFIC = os.path.join(ROOT, "profiles", "pack_gather_long_context_hbm_traffic.json")
 
 
 def sources_sha256(paths):
@@ -194,11 +229,11 @@ def sources_sha256(paths):
     return h.hexdigest()
 
 
-def measured_pack_traffic():
-    """HBM bytes per pack launch from the rocprofv3 counter runs recorded in
+def measured_traffic():
+    """HBM bytes per joint launch from the rocprofv3 counter runs recorded in
     profiles/, or None when the kernel's sources changed since they ran."""
     try:
-        with open(PACK_TRAFFIC) as f:
+        with open(TRAFFIC) as f:
             d = json.load(f)
         if sources_sha256(d["sources"]) != d["sources_sha256"]:
             return None
@@ -310,7 +345,82 @@ def small_batch(torch, mk, dev):
             "us_per_launch_graph_replay": graph_us if isinstance(graph_us, str) else round(graph_us, 2),
             "us_five_single_layer_launches": round(five_us, 2),
             "target_us": 10.0,
-            "bytes": insert_bytes(L, 4, valid_rows=15)}
+            "bytes": small_insert_bytes(15, 4, L, True)}
+
+
+def single_layer_component(torch, mk, dev):
+    """Single-layer bf16 concat-and-cache (16 tokens into a [4, 16, 576]
+    cache, no norm / rope): latency per launch, as for the small batch."""
+    from fp8_paged_insert_amd import synth
+
+    d = synth.single_layer_bf16(dev)
+    cache = d["caches"][0]
+    ptrs = mk.cache_ptr_table([cache])
+    kv, pe, sm = d["kv_c"], d["k_pe"], d["slot_mapping"]
+    T = kv.shape[1]
+    lib = mk.lib()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    raw_args = (kv.data_ptr(), kv.stride(0), kv.stride(1), pe.data_ptr(), pe.stride(0),
+                pe.stride(1), ptrs.data_ptr(), None, sm.data_ptr(), 0, 1, T, R, P, 16,
+                cache.stride(0), cache.stride(1), mk.MLA_KV_AUTO, stream)
+
+    def call():
+        mk.mla_kv_insert_grouped(kv, pe, ptrs, sm, 16, cache.stride(0), cache.stride(1), None,
+                                 "auto")
+
+    def raw():
+        lib.mla_kv_insert_grouped(*raw_args)
+
+    def per_call_us(fn, n=1000):
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / n * 1e6
+
+    ek0 = torch.cuda.Event(enable_timing=True)
+    ek1 = torch.cuda.Event(enable_timing=True)
+    ek0.record()
+    ek1.record()
+    torch.cuda.synchronize()
+    kernel_times = []
+    for _ in range(200):
+        mk.set_launch_events(ek0, ek1)
+        raw()
+        ek1.synchronize()
+        kernel_times.append(ek0.elapsed_time(ek1) * 1e3)
+    return {"workload": "single-layer bf16 insert, 16 tokens into a [4,16,576] cache",
+            "us_per_launch_wall": round(per_call_us(call), 2),
+            "us_per_launch_wall_raw_abi": round(per_call_us(raw), 2),
+            "us_kernel": round(statistics.median(kernel_times), 2),
+            "bytes": small_insert_bytes(T, T, 1, False)}
+
+
+def copy_ceiling(torch, dev):
+    """A plain 1 GiB device-to-device copy (torch's copy kernel), median of 10
+    after 3 warm-up copies: the HBM rate a streaming kernel reaches on this
+    GPU, next to the 8 TB/s peak the roofline uses."""
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    times = []
+    for _ in range(10):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    us = statistics.median(times)
+    del src, dst
+    return {"bytes": 2 * n, "us": round(us, 2), "GBps": round(2 * n / us / 1e3, 1),
+            "frac_of_peak": round(2 * n / us / 1e3 / HBM_PEAK_GBS, 4)}
 
 
 def kernel_us(torch, mk, fn, flush, reps=100, warm=10):
@@ -415,7 +525,7 @@ def epilogue_component(torch, mk, dev, flush):
 
     d = synth.context_epilogue(dev, with_gemm=False)
     T = d["num_tokens"]
-    cs = torch.empty(T, P, dtype=torch.float64, device=dev)
+    cs = torch.empty(T, 2 * P, dtype=torch.float32, device=dev)
     mk.mla_rope_cos_sin_cache(cs, T, P, 10000.0)
     ptrs = mk.cache_ptr_table(d["caches"])
 
@@ -486,7 +596,7 @@ def new_token_component(torch, mk, dev, flush):
 
     d = synth.new_tokens(dev)
     T, H = d["num_tokens"], d["num_heads"]
-    cs = torch.empty(d["max_pos"], P, dtype=torch.float64, device=dev)
+    cs = torch.empty(d["max_pos"], 2 * P, dtype=torch.float32, device=dev)
     mk.mla_rope_cos_sin_cache(cs, d["max_pos"], P, 10000.0)
     q, kvb, kv = d["q"], d["kvb"], d["kv"]
     valid = int((d["slots"] >= 0).sum())
@@ -543,7 +653,7 @@ def projection_component(torch, mk, dev, flush):
     # end to end: the projection, then the epilogue reading its output as
     # [T, L, 576] and inserting into 5 fp8 caches (stream events around both)
     e = synth.context_epilogue(dev, with_gemm=False)
-    cs = torch.empty(4096, P, dtype=torch.float64, device=dev)
+    cs = torch.empty(4096, 2 * P, dtype=torch.float32, device=dev)
     mk.mla_rope_cos_sin_cache(cs, 4096, P, 10000.0)
     ptrs = mk.cache_ptr_table(e["caches"])
     e2e = []
@@ -760,15 +870,18 @@ def main():
     nbytes = wl.bytes_per_step()
     value = nbytes * args.steps / secs / 1e9
 
-    pack_us = statistics.mean(e0.elapsed_time(e1) * 1e3 for e0, e1 in wl.pack_events)
-    pack_b = pack_fp8_bytes(wl.chunk, wl.heads)
-    achieved = pack_b / pack_us / 1e3
-    roofline = {"bound": "hbm", "kernel": "pack_fp8_kernel", "achieved": round(achieved, 1),
+    joint_us = statistics.mean(e0.elapsed_time(e1) * 1e3 for e0, e1 in wl.pack_events)
+    joint_b = pack_fp8_bytes(wl.chunk, wl.heads) + gather_bytes(wl.chunk)
+    achieved = joint_b / joint_us / 1e3
+    roofline = {"bound": "hbm", "kernel": "pack_gather_kernel",
+                "launch": "fp8 full-key + V pack of one 8192-token x 64-head chunk and the "
+                          "dequantising gather of the next chunk's 8192 latent rows",
+                "achieved": round(achieved, 1),
                 "timing": "HIP events recorded by the kernel launch itself (start/stop of its "
-                          "execution) on one pack per timed step, chunk index rotating",
+                          "execution) on one joint launch per timed step, chunk index rotating",
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_pack_traffic(), "bytes_per_launch": pack_b,
-                "avg_launch_us": round(pack_us, 2), "launches": len(wl.pack_events)}
+                "traffic": measured_traffic(), "bytes_per_launch": joint_b,
+                "avg_launch_us": round(joint_us, 2), "launches": len(wl.pack_events)}
 
     result = {
         "metric": "grouped MLA KV insert/pack: effective HBM GB/s (% of peak); "
@@ -782,29 +895,34 @@ def main():
                                "and fp8 full-key/V pack (64 heads, [8192,64,256] kv_b_proj output)",
                    "io": "bf16 inputs, fp8 e4m3fn caches / keys / V, bf16 gather workspace; "
                          "conversions computed in fp32",
+                   "launches": "insert; gather of chunk 0; 15 joint launches (pack of chunk c + "
+                               "gather of chunk c + 1); pack of chunk 15",
                    "bytes_per_step": nbytes, "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
         "roofline": roofline,
     }
-    # the same steps with the gather and the pack as grid-stride loops over a
-    # capped grid (16 workgroups per compute unit); the default full grid is
-    # the faster launch shape on this GPU
+    # the same work with the gather and the pack as launches of their own, on
+    # the default full grid and as grid-stride loops over a capped grid (16
+    # workgroups per compute unit)
     cap = 16 * torch.cuda.get_device_properties(dev).multi_processor_count
-    wl.step(max_blocks=cap)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        wl.step(max_blocks=cap)
-    torch.cuda.synchronize()
-    csecs = time.perf_counter() - t0
-    result["capped_grid_step"] = {
-        "max_blocks": cap, "ms_per_step": round(csecs / args.steps * 1e3, 4),
-        "GBps": round(nbytes * args.steps / csecs / 1e9, 1),
-        "frac_of_hbm_peak": round(nbytes * args.steps / csecs / 1e9 / HBM_PEAK_GBS, 4)}
+    for name, mb in (("separate_launch_step", 0), ("capped_grid_step", cap)):
+        wl.step_separate(max_blocks=mb)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            wl.step_separate(max_blocks=mb)
+        torch.cuda.synchronize()
+        csecs = time.perf_counter() - t0
+        result[name] = {
+            "max_blocks": mb, "ms_per_step": round(csecs / args.steps * 1e3, 4),
+            "GBps": round(nbytes * args.steps / csecs / 1e9, 1),
+            "frac_of_hbm_peak": round(nbytes * args.steps / csecs / 1e9 / HBM_PEAK_GBS, 4)}
     del wl
     torch.cuda.empty_cache()
     if not args.no_components:
         flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        result["copy_ceiling"] = copy_ceiling(torch, dev)
         comps = {"small_batch_insert": small_batch(torch, mk, dev),
+                 "single_layer_insert": single_layer_component(torch, mk, dev),
                  "context_pack": context_pack_component(torch, mk, dev, flush),
                  "context_epilogue": epilogue_component(torch, mk, dev, flush),
                  "cache_dtypes": cache_dtype_component(torch, mk, dev, flush),

@@ -339,10 +339,11 @@ def prepare_insert_grouped(*args, **kwargs) -> PreparedInsert:
 
 
 def mla_rope_cos_sin_cache(out, max_pos, rope_dim, base=10000.0):
-    """Fill the float64 [max_pos, rope_dim] = cos | sin table on the device."""
-    _need(out, (torch.float64,), "out")
-    if not out.is_contiguous() or out.numel() != max_pos * rope_dim:
-        raise RuntimeError("out must be a contiguous float64 [max_pos, rope_dim] tensor")
+    """Fill the fp32 [max_pos, 2 * rope_dim] rotary table (cos hi | sin hi |
+    cos lo | sin lo of each position's angles) on the device."""
+    _need(out, (torch.float32,), "out")
+    if not out.is_contiguous() or out.numel() != max_pos * 2 * rope_dim:
+        raise RuntimeError("out must be a contiguous fp32 [max_pos, 2 * rope_dim] tensor")
     _check(lib().mla_rope_cos_sin_cache(_ptr(out), int(max_pos), int(rope_dim), float(base),
                                         _stream(out)), "mla_rope_cos_sin_cache")
 
@@ -354,7 +355,7 @@ def mla_ctx_kv_epilogue(all_kv, gamma, eps, positions, cos_sin, kv_cache_ptrs, s
     _need(all_kv, (torch.bfloat16,), "all_kv")
     _need(gamma, (torch.bfloat16,), "gamma")
     _need(positions, (torch.int64,), "positions")
-    _need(cos_sin, (torch.float64,), "cos_sin")
+    _need(cos_sin, (torch.float32,), "cos_sin")
     if all_kv.dim() != 3 or all_kv.stride(2) != 1:
         raise RuntimeError("all_kv must be a [T, L, width] view with contiguous rows")
     T, L, W = all_kv.shape
@@ -364,8 +365,8 @@ def mla_ctx_kv_epilogue(all_kv, gamma, eps, positions, cos_sin, kv_cache_ptrs, s
         raise RuntimeError(f"gamma must be contiguous [{L}, {R}]")
     if positions.numel() != T or not positions.is_contiguous():
         raise RuntimeError(f"positions must be contiguous [{T}]")
-    if cos_sin.dim() != 2 or cos_sin.shape[1] != P or not cos_sin.is_contiguous():
-        raise RuntimeError(f"cos_sin must be a contiguous float64 [max_pos, {P}] table")
+    if cos_sin.dim() != 2 or cos_sin.shape[1] != 2 * P or not cos_sin.is_contiguous():
+        raise RuntimeError(f"cos_sin must be a contiguous fp32 [max_pos, {2 * P}] table")
     for t, n in ((gamma, "gamma"), (positions, "positions"), (cos_sin, "cos_sin")):
         _same_device(t, all_kv, n, "all_kv")
     sm, sls = _slots_2d(slot_mapping, L, T)
@@ -545,8 +546,8 @@ def mla_new_token_epilogue(q_nope, q_pe, k_nope, kv_c, k_pe, positions, cos_sin,
     into one layer's paged cache [num_blocks, block_size, >= R + rope].
 
     q_nope / q_pe / k_nope / v: bf16 [T, H, d] views with contiguous rows;
-    kv_c / k_pe: bf16 [T, d] views; positions int64 [T]; cos_sin float64
-    [max_pos, rope] (mla_rope_cos_sin_cache).  q_out / key_out [T, H, nope+rope]
+    kv_c / k_pe: bf16 [T, d] views; positions int64 [T]; cos_sin fp32
+    [max_pos, 2 * rope] (mla_rope_cos_sin_cache).  q_out / key_out [T, H, nope+rope]
     and v_out [T, H, vdim] contiguous: bf16 in KEY_BF16 mode, fp8 e4m3fn
     (uint8 or float8_e4m3fn) in KEY_V_FP8 mode.  cache=None skips the insert.
     """
@@ -568,9 +569,9 @@ def mla_new_token_epilogue(q_nope, q_pe, k_nope, kv_c, k_pe, positions, cos_sin,
     _need(positions, (torch.int64,), "positions")
     if positions.numel() != T or not positions.is_contiguous():
         raise RuntimeError("positions must be a contiguous int64 [T] tensor")
-    _need(cos_sin, (torch.float64,), "cos_sin")
-    if cos_sin.dim() != 2 or cos_sin.shape[1] != rope or not cos_sin.is_contiguous():
-        raise RuntimeError(f"cos_sin must be a contiguous float64 [max_pos, {rope}] table")
+    _need(cos_sin, (torch.float32,), "cos_sin")
+    if cos_sin.dim() != 2 or cos_sin.shape[1] != 2 * rope or not cos_sin.is_contiguous():
+        raise RuntimeError(f"cos_sin must be a contiguous fp32 [max_pos, {2 * rope}] table")
     for t_, n in ((positions, "positions"), (cos_sin, "cos_sin"), (q_out, "q_out"),
                   (key_out, "key_out")):
         _same_device(t_, q_nope, n, "q_nope")

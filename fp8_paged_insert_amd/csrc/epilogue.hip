@@ -21,10 +21,10 @@
 // so every load and store instruction covers 128-256 contiguous bytes per
 // row.  The sum of squares is reduced with four in-row DPP steps (no LDS
 // round trip), RoPE's (i, i + 32) pairs sit in lanes j and j ^ 8 and swap
-// with one DPP row rotation, and the token's position indexes the float64
-// cos/sin table directly instead of a repeated-positions buffer.  The
-// rotation runs in float64 (a handful of operations per lane), so where its
-// two products nearly cancel the result still rounds correctly to bf16.
+// with one DPP row rotation, and the token's position indexes the cos/sin
+// table directly instead of a repeated-positions buffer.  The rotation is
+// rounded correctly to bf16 even where its two products nearly cancel
+// (rope4: an fp32 fast path with an exact float64 fallback).
 #include "mla_common.hpp"
 
 namespace mla {
@@ -38,7 +38,7 @@ int32_t check_insert_common(const char* fn, const int64_t* kv_cache_ptrs,
 namespace {
 
 // -------------------------------------------------------------- rope table --
-__global__ __launch_bounds__(256) void rope_table_kernel(double* out, int64_t max_pos,
+__global__ __launch_bounds__(256) void rope_table_kernel(float* out, int64_t max_pos,
                                                          int64_t rope_dim, double base) {
   const int64_t half = rope_dim / 2;
   const int64_t n = max_pos * half;
@@ -47,8 +47,13 @@ __global__ __launch_bounds__(256) void rope_table_kernel(double* out, int64_t ma
     const int64_t p = idx / half;
     const int64_t i = idx - p * half;
     const double theta = double(p) * pow(base, -2.0 * double(i) / double(rope_dim));
-    out[p * rope_dim + i] = cos(theta);
-    out[p * rope_dim + half + i] = sin(theta);
+    const double c = cos(theta), s = sin(theta);
+    const float ch = static_cast<float>(c), sh = static_cast<float>(s);
+    float* row = out + p * 2 * rope_dim;
+    row[i] = ch;
+    row[half + i] = sh;
+    row[rope_dim + i] = static_cast<float>(c - static_cast<double>(ch));
+    row[rope_dim + half + i] = static_cast<float>(s - static_cast<double>(sh));
   }
 }
 
@@ -68,7 +73,7 @@ struct EpiArgs {
   const uint16_t* gamma;
   float eps;
   const int64_t* positions;
-  const double* cos_sin;
+  const float* cos_sin;  // [max_pos, 2 * 64]: cos hi | sin hi | cos lo | sin lo
   int64_t max_pos;
   const int64_t* cache_ptrs;
   const float* scales;
@@ -114,7 +119,7 @@ __device__ __forceinline__ int64_t entry_offset(int64_t s, const EpiArgs& a) {
 // Rows are numbered token-major (row = t * L + l), the order of the
 // projection output, so the 4 rows of a wavefront are adjacent in memory.
 template <int kFmt>
-__global__ __launch_bounds__(256) void epilogue_kernel(const EpiArgs a) {
+__global__ __launch_bounds__(256, 5) void epilogue_kernel(const EpiArgs a) {
   constexpr bool kFp8 = kFmt != kFmtBf16, kE5M2 = kFmt == kFmtE5M2;
   const int lane = threadIdx.x & 63;
   const int j = lane & (kRowLanes - 1);       // lane within the row
@@ -151,49 +156,56 @@ __global__ __launch_bounds__(256) void epilogue_kernel(const EpiArgs a) {
     if constexpr (kFp8) sc = a.scales[l];
     __builtin_amdgcn_sched_barrier(0);
     const int64_t pos = min(max(pos_in, int64_t(0)), a.max_pos - 1);
-    const double* cs = a.cos_sin + pos * kP + kPe * (j & 7);
-    double cc[kPe], sn[kPe];
-    ld_f64x4(cs, cc);
-    ld_f64x4(cs + kP / 2, sn);
+    const float* cs = a.cos_sin + pos * (2 * kP) + kPe * (j & 7);
+    const uint4 cv = ld16(cs);
+    const uint4 sv = ld16(cs + kP / 2);
     // Keep every load of the row here, ahead of the first wait: without this
     // fence the compiler sinks the loads used only by the stores into the
     // store branch, after the reduction, adding memory round trips.
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
-    // ---- RMSNorm: fp32 sum of squares over the row's 16 lanes
-    float x[8 * kChunks];
+    // ---- RoPE first (its table words and partner values are dead before the
+    // normed row is built): y_i = x_i cos - x_{i+32} sin, y_{i+32} = x_{i+32} cos + x_i sin
+    const float xp[kPe] = {bf16_lo(pe.x), bf16_hi(pe.x), bf16_lo(pe.y), bf16_hi(pe.y)};
+    const float cc[kPe] = {__uint_as_float(cv.x), __uint_as_float(cv.y), __uint_as_float(cv.z),
+                           __uint_as_float(cv.w)};
+    const float sn[kPe] = {__uint_as_float(sv.x), __uint_as_float(sv.y), __uint_as_float(sv.z),
+                           __uint_as_float(sv.w)};
+    float xq[kPe];
+#pragma unroll
+    for (int e = 0; e < kPe; ++e) xq[e] = dpp_f<kDppRor8>(xp[e]);
+    const uint2 ype = rope4(xp, xq, cc, sn, first_half, cs + kP, cs + kP + kP / 2);
+
+    // ---- RMSNorm: fp32 sum of squares over the row's 16 lanes.  The fp32
+    // values are taken from the bf16 words twice (a shift or a mask each)
+    // instead of being kept: 32 fewer live registers, so more wavefronts fit.
+    float ss = 0.0f;
 #pragma unroll
     for (int q = 0; q < kChunks; ++q) {
       const uint32_t w[4] = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        x[8 * q + 2 * i] = bf16_lo(w[i]);
-        x[8 * q + 2 * i + 1] = bf16_hi(w[i]);
+        ss = __builtin_fmaf(bf16_lo(w[i]), bf16_lo(w[i]), ss);
+        ss = __builtin_fmaf(bf16_hi(w[i]), bf16_hi(w[i]), ss);
       }
     }
-    float ss = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8 * kChunks; ++i) ss = __builtin_fmaf(x[i], x[i], ss);
     ss = row_sum(ss);
     const float rinv = 1.0f / __builtin_sqrtf(ss * (1.0f / kR) + a.eps);
     uint4 y[kChunks];
 #pragma unroll
     for (int q = 0; q < kChunks; ++q) {
+      // an empty asm that "changes" the words, so the conversions above are
+      // not kept alive across the reduction for reuse here
+      uint32_t w[4] = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
+      asm volatile("" : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]));
       const uint32_t gw[4] = {gv[q].x, gv[q].y, gv[q].z, gv[q].w};
       uint32_t yw[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        yw[i] = cvt_bf16x2(x[8 * q + 2 * i] * rinv * bf16_lo(gw[i]),
-                           x[8 * q + 2 * i + 1] * rinv * bf16_hi(gw[i]));
+        yw[i] = cvt_bf16x2(bf16_lo(w[i]) * rinv * bf16_lo(gw[i]),
+                           bf16_hi(w[i]) * rinv * bf16_hi(gw[i]));
       y[q] = make_uint4(yw[0], yw[1], yw[2], yw[3]);
     }
-
-    // ---- RoPE: y_i = x_i cos - x_{i+32} sin, y_{i+32} = x_{i+32} cos + x_i sin
-    const float xp[kPe] = {bf16_lo(pe.x), bf16_hi(pe.x), bf16_lo(pe.y), bf16_hi(pe.y)};
-    float xq[kPe];
-#pragma unroll
-    for (int e = 0; e < kPe; ++e) xq[e] = dpp_f<kDppRor8>(xp[e]);
-    const uint2 ype = rope4_f64(xp, xq, cc, sn, first_half);
 
     if (!active) continue;
     if (a.dbg) {
@@ -227,7 +239,7 @@ __global__ __launch_bounds__(256) void epilogue_kernel(const EpiArgs a) {
 
 using namespace mla;
 
-extern "C" int32_t mla_rope_cos_sin_cache(double* out, int64_t max_pos, int64_t rope_dim,
+extern "C" int32_t mla_rope_cos_sin_cache(float* out, int64_t max_pos, int64_t rope_dim,
                                           double base, mla_stream_t stream) {
   static const char* fn = "mla_rope_cos_sin_cache";
   clear_error();
@@ -246,7 +258,7 @@ extern "C" int32_t mla_rope_cos_sin_cache(double* out, int64_t max_pos, int64_t 
 
 extern "C" int32_t mla_ctx_kv_epilogue(
     const void* all_kv, int64_t kv_layer_stride, int64_t kv_token_stride, const void* gamma,
-    float eps, const int64_t* positions, const double* cos_sin, int64_t max_pos,
+    float eps, const int64_t* positions, const float* cos_sin, int64_t max_pos,
     const int64_t* kv_cache_ptrs, const float* kv_scales, const int64_t* slot_mapping,
     int64_t slot_layer_stride, int64_t num_layers, int64_t num_tokens, int64_t kv_lora_rank,
     int64_t pe_dim, int64_t block_size, int64_t block_stride, int64_t entry_stride,

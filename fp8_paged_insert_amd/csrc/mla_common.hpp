@@ -85,6 +85,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
+// fp32 -> bf16 with the gfx950 converter (round to nearest even), two at a
+// time.  Used where a NaN's payload and sign are not part of the contract.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 // float64 -> bf16 bits, rounded once to nearest even (as if directly): the
 // conversion to fp32 is made round-to-odd (an inexact result is truncated
 // toward zero and its last bit set), so the second rounding, fp32 -> bf16,
@@ -100,47 +109,65 @@ __device__ __forceinline__ uint32_t f64_to_bf16_bits(double d) {
   return f32_to_bf16_bits(__uint_as_float(u));
 }
 
-// Rotary embedding of one lane's 4 values of a 64-wide rope row,
-// non-interleaved pairs (i, i + 32) ("PR #50585 完整报告", 关键源码片段: RoPE
-// of k_pe at the token's position; the formula itself is elided there):
-//   first half  (x = x_i,      p = x_{i+32}):  y_i      = x_i cos_i - x_{i+32} sin_i
-//   second half (x = x_{i+32}, p = x_i):       y_{i+32} = x_{i+32} cos_i + x_i sin_i
-// Each product and the sum are float64 operations (bf16 inputs make the
-// conversions exact; contraction is off so every operation rounds on its
-// own), then one rounding to bf16.  Cancellation between the two products
-// costs float64 digits, not bf16 ones.  c / s: float64 cos / sin of the
-// lane's 4 angles.
-__device__ __forceinline__ uint2 rope4_f64(const float* x, const float* p, const double* c,
-                                           const double* s, bool first) {
+// Rotary embedding of one lane's 4 values of a rope row, non-interleaved
+// pairs (i, i + P/2) ("PR #50585 完整报告", 关键源码片段: RoPE of k_pe at the
+// token's position; the formula itself is elided there):
+//   first half  (x = x_i,       p = x_{i+P/2}):  y_i       = x_i cos_i - x_{i+P/2} sin_i
+//   second half (x = x_{i+P/2}, p = x_i):        y_{i+P/2} = x_{i+P/2} cos_i + x_i sin_i
+// rounded once to bf16.  The table holds each cos / sin as an fp32 pair
+// hi + lo (hi = RN32(v), lo = RN32(v - hi): about 48 significant bits).
+// Fast path, fp32 with the hi values: y32 = fma(x, c, -+ p s) is within
+// B = 2^-22 (|x| + |p|) of the exact rotation (table rounding 2^-24 per
+// coefficient, the product and the fma 2^-24 each).  The bf16 rounding
+// boundary nearest to y32 is the midpoint of y32's bf16 interval (the other
+// boundaries are a bf16 ulp away); when y32 lies farther than B from it,
+// RNE(y32) is the correctly rounded result.  That test also catches the
+// products nearly cancelling (then B exceeds half a bf16 ulp of y32, and no
+// value is farther than that from the midpoint).  Otherwise the whole
+// wavefront takes the exact path (a uniform branch, taken by about one
+// wavefront in a hundred): the rotation in float64 with hi + lo, then one
+// correct rounding to bf16.
+// c / s: the lane's 4 cos / sin hi values; lo_c / lo_s: where the matching
+// lo values sit in the table (read only on the exact path).
+// One rotated value in float64 from the exact table values hi + lo (each
+// operation rounded on its own, then one correct rounding to bf16).
+__device__ __forceinline__ uint32_t rope1_exact(float x, float p, float ch, float cl, float sh,
+                                                float sl, bool first) {
 #pragma clang fp contract(off)
-  uint32_t b[4];
+  const double c = static_cast<double>(ch) + static_cast<double>(cl);  // exact
+  const double s = static_cast<double>(sh) + static_cast<double>(sl);  // exact
+  const double u = static_cast<double>(x) * c;
+  const double v = static_cast<double>(p) * s;
+  return f64_to_bf16_bits(first ? u - v : u + v);
+}
+
+__device__ __forceinline__ uint2 rope4(const float* x, const float* p, const float* c,
+                                       const float* s, bool first, const float* lo_c,
+                                       const float* lo_s) {
+  float y[4];
+  bool safe = true;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const double u = static_cast<double>(x[e]) * c[e];
-    const double v = static_cast<double>(p[e]) * s[e];
-    b[e] = f64_to_bf16_bits(first ? u - v : u + v);
+    const float ps = p[e] * s[e];
+    y[e] = __builtin_fmaf(x[e], c[e], first ? -ps : ps);
+    const float bound = 0x1p-22f * (__builtin_fabsf(x[e]) + __builtin_fabsf(p[e]));
+    const float mid = __uint_as_float((__float_as_uint(y[e]) & 0xFFFF0000u) | 0x8000u);
+    // false for NaN (and for an infinite bound), which then takes the exact path
+    safe = safe && __builtin_fabsf(y[e] - mid) > bound;
   }
-  return make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(!safe) != 0, 0)) {
+    const float4 cl = *reinterpret_cast<const float4*>(lo_c);
+    const float4 sl = *reinterpret_cast<const float4*>(lo_s);
+    const float cls[4] = {cl.x, cl.y, cl.z, cl.w}, sls[4] = {sl.x, sl.y, sl.z, sl.w};
+    uint32_t b[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) b[e] = rope1_exact(x[e], p[e], c[e], cls[e], s[e], sls[e], first);
+    return make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+  }
+  // no NaN reaches here, so the hardware converter (RNE) serves
+  return make_uint2(cvt_bf16x2(y[0], y[1]), cvt_bf16x2(y[2], y[3]));
 }
 
-// Four float64 values from 32 contiguous, 16-byte aligned bytes.
-__device__ __forceinline__ void ld_f64x4(const double* p, double* out) {
-  const uint4 a = *reinterpret_cast<const uint4*>(p);
-  const uint4 b = *reinterpret_cast<const uint4*>(p + 2);
-  out[0] = __hiloint2double(a.y, a.x);
-  out[1] = __hiloint2double(a.w, a.z);
-  out[2] = __hiloint2double(b.y, b.x);
-  out[3] = __hiloint2double(b.w, b.z);
-}
-
-// fp32 -> bf16 with the gfx950 converter (round to nearest even), two at a
-// time.  Used where a NaN's payload and sign are not part of the contract.
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
-  const f32x2_t v = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-}
 
 // ---------------------------------------------------------------------------
 // bf16 (or fp16) -> fp8 with a per-tensor dequantisation scale s:

@@ -54,7 +54,7 @@ struct NewTokenArgs {
   const uint16_t* k_pe;
   int64_t kpe_ts;
   const int64_t* positions;
-  const double* cos_sin;  // [max_pos, 64]: cos of the 32 angles, then their sin
+  const float* cos_sin;  // [max_pos, 128]: cos hi | sin hi | cos lo | sin lo of the 32 angles
   int64_t max_pos;
   const float* q_scale;
   const float* k_scale;
@@ -109,16 +109,21 @@ __device__ __forceinline__ void st4(void* p, uint32_t v) {
     *reinterpret_cast<uint32_t*>(p) = v;
 }
 
-// Lane j's rope values [4j, 4j + 4) (two bf16 words) rotated with the
-// float64 table values c / sn of angles 4 (j mod 8) ..:  first half (j < 8)
-//   y_i = x_i cos_i - x_{i+32} sin_i,  second half  y_{i+32} = x_{i+32} cos_i + x_i sin_i,
-// in float64 and rounded once to bf16 (rope4_f64).
+// Lane j's rope values [4j, 4j + 4) (two bf16 words) rotated with the table
+// words cv / sv of angles 4 (j mod 8) .. (tab: the lane's cos hi entries):
+//   first half (j < 8)  y_i = x_i cos_i - x_{i+32} sin_i,
+//   second half         y_{i+32} = x_{i+32} cos_i + x_i sin_i,
+// each rounded once to bf16 (rope4).
 // Every lane of the DPP row must execute it (the partner comes from lane j +- 8).
-__device__ __forceinline__ uint2 rope4(uint2 x, const double* c, const double* sn, bool first) {
+__device__ __forceinline__ uint2 rope4w(uint2 x, uint4 cv, uint4 sv, bool first, const float* tab) {
   const uint2 p = make_uint2(dpp_ror8(x.x), dpp_ror8(x.y));
   const float xf[4] = {bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y)};
   const float pf[4] = {bf16_lo(p.x), bf16_hi(p.x), bf16_lo(p.y), bf16_hi(p.y)};
-  return rope4_f64(xf, pf, c, sn, first);
+  const float c[4] = {__uint_as_float(cv.x), __uint_as_float(cv.y), __uint_as_float(cv.z),
+                      __uint_as_float(cv.w)};
+  const float sn[4] = {__uint_as_float(sv.x), __uint_as_float(sv.y), __uint_as_float(sv.z),
+                       __uint_as_float(sv.w)};
+  return rope4(xf, pf, c, sn, first, tab + kRope, tab + kRope + kRope / 2);
 }
 
 // 8 bf16 -> one output chunk: 8 e4m3fn / e5m2 codes (kFmt) of x / s, or of x
@@ -167,10 +172,8 @@ __global__ __launch_bounds__(256) void new_token_kernel(const NewTokenArgs a) {
       const uint32_t t = fdiv(task, a.heads);
       const uint32_t h = task - t * a.heads.d;
       const int64_t pos = min(max(a.positions[t], int64_t(0)), a.max_pos - 1);
-      const double* tab = a.cos_sin + pos * kRope + 4 * (j & 7);
-      double cv[4], sv[4];
-      ld_f64x4(tab, cv);
-      ld_f64x4(tab + kRope / 2, sv);
+      const float* tab = a.cos_sin + pos * (2 * kRope) + 4 * (j & 7);
+      const uint4 cv = ld16(tab), sv = ld16(tab + kRope / 2);
       const uint16_t* qn = a.q_nope + int64_t(t) * a.qn_ts + int64_t(h) * a.qn_hs;
       const uint16_t* kn = a.k_nope + int64_t(t) * a.kn_ts + int64_t(h) * a.kn_hs;
       const uint2 qpe = ld8(a.q_pe + int64_t(t) * a.qp_ts + int64_t(h) * a.qp_hs + 4 * j);
@@ -188,9 +191,9 @@ __global__ __launch_bounds__(256) void new_token_kernel(const NewTokenArgs a) {
           xv = ld16_once(a.v + int64_t(t) * a.v_ts + int64_t(h) * a.v_hs + 8 * j);
         put8<kOut, kNtStream, kScaled>(qo + 8 * j * ob, xq, qs, qr, qf);
         put8<kOut, kNtStream, kScaled>(ko + 8 * j * ob, xk, ks, kr, kf);
-        put4<kOut, kNtStream, kScaled>(qo + (128 + 4 * j) * ob, rope4(qpe, cv, sv, first), qs,
+        put4<kOut, kNtStream, kScaled>(qo + (128 + 4 * j) * ob, rope4w(qpe, cv, sv, first, tab), qs,
                                          qr, qf);
-        put4<kOut, kNtStream, kScaled>(ko + (128 + 4 * j) * ob, rope4(kpe, cv, sv, first), ks,
+        put4<kOut, kNtStream, kScaled>(ko + (128 + 4 * j) * ob, rope4w(kpe, cv, sv, first, tab), ks,
                                          kr, kf);
         if constexpr (kFp8)
           put8<kFmtE4M3, kNtStream, kScaled>(a.v_out + int64_t(task) * 128 + 8 * j, xv, vs, vr,
@@ -203,9 +206,9 @@ __global__ __launch_bounds__(256) void new_token_kernel(const NewTokenArgs a) {
         put8<kOut, kNtStream, kScaled>(qo + 8 * c * ob, xq, qs, qr, qf);
         put8<kOut, kNtStream, kScaled>(ko + 8 * c * ob, xk, ks, kr, kf);
       }
-      put4<kOut, kNtStream, kScaled>(qo + (a.nope + 4 * j) * ob, rope4(qpe, cv, sv, first), qs,
+      put4<kOut, kNtStream, kScaled>(qo + (a.nope + 4 * j) * ob, rope4w(qpe, cv, sv, first, tab), qs,
                                        qr, qf);
-      put4<kOut, kNtStream, kScaled>(ko + (a.nope + 4 * j) * ob, rope4(kpe, cv, sv, first), ks,
+      put4<kOut, kNtStream, kScaled>(ko + (a.nope + 4 * j) * ob, rope4w(kpe, cv, sv, first, tab), ks,
                                        kr, kf);
       if constexpr (kFp8) {
         const uint16_t* vi = a.v + int64_t(t) * a.v_ts + int64_t(h) * a.v_hs;
@@ -219,16 +222,14 @@ __global__ __launch_bounds__(256) void new_token_kernel(const NewTokenArgs a) {
       const int64_t slot = a.slots[t];
       if (slot < 0) continue;  // padded token: the whole row skips
       const int64_t pos = min(max(a.positions[t], int64_t(0)), a.max_pos - 1);
-      const double* tab = a.cos_sin + pos * kRope + 4 * (j & 7);
-      double cv[4], sv[4];
-      ld_f64x4(tab, cv);
-      ld_f64x4(tab + kRope / 2, sv);
+      const float* tab = a.cos_sin + pos * (2 * kRope) + 4 * (j & 7);
+      const uint4 cv = ld16(tab), sv = ld16(tab + kRope / 2);
       const uint2 kpe = ld8(a.k_pe + int64_t(t) * a.kpe_ts + 4 * j);
       const uint16_t* kc = a.kv_c + int64_t(t) * a.kvc_ts;
       uint8_t* dst = static_cast<uint8_t*>(a.cache) + entry_offset(slot, a) * cb;
       for (uint32_t c = j; c < a.kv_lora_rank / 8; c += kLanes)
         put8<kCacheFmt, kNtStream>(dst + 8 * c * cb, ld16(kc + 8 * c), cs, cr, cf);
-      put4<kCacheFmt, kNtStream>(dst + (a.kv_lora_rank + 4 * j) * cb, rope4(kpe, cv, sv, first),
+      put4<kCacheFmt, kNtStream>(dst + (a.kv_lora_rank + 4 * j) * cb, rope4w(kpe, cv, sv, first, tab),
                                  cs, cr, cf);
     }
   }
@@ -254,7 +255,7 @@ extern "C" int32_t mla_new_token_epilogue(
     int64_t qp_tok_stride, int64_t qp_head_stride, const void* k_nope, int64_t kn_tok_stride,
     int64_t kn_head_stride, const void* v, int64_t v_tok_stride, int64_t v_head_stride,
     const void* kv_c, int64_t kv_c_tok_stride, const void* k_pe, int64_t k_pe_tok_stride,
-    const int64_t* positions, const double* cos_sin, int64_t max_pos, int64_t num_tokens,
+    const int64_t* positions, const float* cos_sin, int64_t max_pos, int64_t num_tokens,
     int64_t num_heads, int64_t nope, int64_t rope, int64_t vdim, int64_t kv_lora_rank,
     int32_t mode, const float* q_scale, const float* k_scale, const float* v_scale,
     void* q_out, void* key_out, void* v_out, void* cache, int32_t cache_dtype,

@@ -166,17 +166,22 @@ int32_t mla_kv_insert_grouped(
 
 /* ------------------------------------------------------------------------
  * mla_rope_cos_sin_cache -- fill the rotary table used by the epilogues.
- * out (device float64 [max_pos, rope_dim]) row p = cos(theta_0..theta_{d/2-1})
- * followed by sin(theta_0..theta_{d/2-1}), theta_i = p * base^(-2i/d),
- * evaluated in float64 on the device.  The epilogues rotate in float64
- * with these values and round each result once to bf16, so a rotation
- * whose two products nearly cancel still rounds correctly.
+ * out (device fp32 [max_pos, 2 * rope_dim]) row p holds, for the angles
+ * theta_i = p * base^(-2i/d), i < d/2, evaluated in float64 on the device:
+ *   [0, d/2)      cos_hi = RN32(cos theta_i)     [d/2, d)   sin_hi = RN32(sin theta_i)
+ *   [d, 3d/2)     cos_lo = RN32(cos - cos_hi)    [3d/2, 2d) sin_lo = RN32(sin - sin_hi)
+ * (hi + lo carries about 48 significant bits of each value).  The epilogues
+ * rotate with the hi values in fp32 and, where that result could round to
+ * a different bf16 value than the exact rotation (the two products nearly
+ * cancelling, or the fp32 value next to a rounding boundary), recompute it
+ * in float64 from hi + lo; every rotated value is thus the correctly
+ * rounded bf16 of the rotation.
  * ([P2] 关键源码片段: RoPE of k_pe at each context position, the positions
  * being the same for every layer; the formula itself is not printed, the
  * non-interleaved form with the given base is the reading taken.)
  * rope_dim must be even and > 0; max_pos >= 0.
  * ------------------------------------------------------------------------ */
-int32_t mla_rope_cos_sin_cache(double* out, int64_t max_pos, int64_t rope_dim,
+int32_t mla_rope_cos_sin_cache(float* out, int64_t max_pos, int64_t rope_dim,
                                double base, mla_stream_t stream);
 
 /* ------------------------------------------------------------------------
@@ -191,11 +196,11 @@ int32_t mla_rope_cos_sin_cache(double* out, int64_t max_pos, int64_t rope_dim,
  * gamma   device bf16 [num_layers, kv_lora_rank] (row l = layer l's norm weight).
  * eps     RMSNorm epsilon.
  * positions device int64 [num_tokens], each in [0, max_pos).
- * cos_sin device float64 [max_pos, pe_dim] from mla_rope_cos_sin_cache.
+ * cos_sin device fp32 [max_pos, 2 * pe_dim] from mla_rope_cos_sin_cache.
  * For each (l, t):
  *   row[0:R]   = bf16(x_i * (mean(x^2) + eps)^(-1/2) * gamma[l, i])  (fp32 math)
  *   row[R:R+P] = bf16(rotation of k_pe by theta(positions[t]))   (pairs (i, i+P/2);
- *                float64 math, one rounding)
+ *                correctly rounded, see mla_rope_cos_sin_cache)
  *   then row is inserted exactly as mla_kv_insert_grouped inserts [kv_c | k_pe].
  * dbg_rows  optional device bf16 [L, T, R+P] contiguous: receives every row
  *   (also those whose slot is negative); NULL to skip.
@@ -205,7 +210,7 @@ int32_t mla_rope_cos_sin_cache(double* out, int64_t max_pos, int64_t rope_dim,
  * ------------------------------------------------------------------------ */
 int32_t mla_ctx_kv_epilogue(
     const void* all_kv, int64_t kv_layer_stride, int64_t kv_token_stride,
-    const void* gamma, float eps, const int64_t* positions, const double* cos_sin,
+    const void* gamma, float eps, const int64_t* positions, const float* cos_sin,
     int64_t max_pos,
     const int64_t* kv_cache_ptrs, const float* kv_scales,
     const int64_t* slot_mapping, int64_t slot_layer_stride,
@@ -386,7 +391,7 @@ int32_t mla_ctx_neutralize_partials(void* out, int64_t out_tok_stride, int64_t o
  * elsewhere in this library:
  *   pe_q = RoPE(q_pe[t, h, :], pos[t]),  pe_k = RoPE(k_pe[t, :], pos[t])
  *            (half-split rotation, angles from cos_sin as in
- *            mla_ctx_kv_epilogue; float64 math, each result rounded once to bf16)
+ *            mla_ctx_kv_epilogue; each result correctly rounded to bf16)
  *   q_out[t, h, :]   = [q_nope[t, h, :] | pe_q]
  *   key_out[t, h, :] = [k_nope[t, h, :] | pe_k]     (same pe_k for every head)
  *   v_out[t, h, :]   = v[t, h, :]                    (KEY_V_FP8 only)
@@ -402,8 +407,7 @@ int32_t mla_ctx_neutralize_partials(void* out, int64_t out_tok_stride, int64_t o
  *   (q_nope, q_pe, k_nope, v), [t, i] at t*tok_stride + i (kv_c, k_pe).
  * positions   device int64 [T], each in [0, max_pos) (precondition; values
  *             outside are clamped to that range).
- * cos_sin     device float64 [max_pos, rope] = cos of the rope/2 angles | their
- *             sin (mla_rope_cos_sin_cache fills it).
+ * cos_sin     device fp32 [max_pos, 2 * rope] (mla_rope_cos_sin_cache fills it).
  * cache       device; element type from cache_dtype (AUTO/BF16, FP8_E4M3,
  *             FP8_E5M2); cache_scale device fp32 [1] for an fp8 cache, NULL
  *             for bf16; slot_mapping device int64 [T] with distinct
@@ -419,7 +423,7 @@ int32_t mla_new_token_epilogue(
     int64_t qp_tok_stride, int64_t qp_head_stride, const void* k_nope, int64_t kn_tok_stride,
     int64_t kn_head_stride, const void* v, int64_t v_tok_stride, int64_t v_head_stride,
     const void* kv_c, int64_t kv_c_tok_stride, const void* k_pe, int64_t k_pe_tok_stride,
-    const int64_t* positions, const double* cos_sin, int64_t max_pos, int64_t num_tokens,
+    const int64_t* positions, const float* cos_sin, int64_t max_pos, int64_t num_tokens,
     int64_t num_heads, int64_t nope, int64_t rope, int64_t vdim, int64_t kv_lora_rank,
     int32_t mode, const float* q_scale, const float* k_scale, const float* v_scale,
     void* q_out, void* key_out, void* v_out, void* cache, int32_t cache_dtype,

@@ -22,6 +22,11 @@ import bench  # noqa: E402
     (bench.gather_bytes, (8192,), 8192 * (576 + 1152 + 8) + 4),
     # merge: accumulator read + write and the partial read (bf16 rows), three fp32 lse
     (bench.merge_bytes, (16384, 64), 16384 * 64 * (3 * 256 + 3 * 4)),
+    # small-batch grouped fp8 insert, 5 layers x 4 tokens, one skipped: 15 rows read and
+    # written, 4 shared slots, 5 scales and 5 cache pointers
+    (bench.small_insert_bytes, (15, 4, 5, True), 26012),
+    # single-layer bf16 insert of 16 tokens: 16 rows read and written, 16 slots
+    (bench.small_insert_bytes, (16, 16, 1, False), 36992),
 ])
 def test_byte_formulas(fn, args, want):
     assert fn(*args) == want
@@ -35,9 +40,9 @@ def test_long_context_insert_bytes_match_the_workload():
 
 def test_new_token_bytes_are_mode_specific_sums():
     T, H = 8192, 64
-    # per token: latent row, position, slot and the float64 cos/sin row (512 B)
-    fp8 = T * H * (384 + 256 + 256 + 192 + 192 + 128) + T * (1152 + 8 + 8 + 512) + (T - 1) * 576
-    bf16 = T * H * (384 + 256 + 384 + 384) + T * (1152 + 8 + 8 + 512) + (T - 1) * 576
+    # per token: latent row, position, slot and the fp32 cos/sin row (256 B)
+    fp8 = T * H * (384 + 256 + 256 + 192 + 192 + 128) + T * (1152 + 8 + 8 + 256) + (T - 1) * 576
+    bf16 = T * H * (384 + 256 + 384 + 384) + T * (1152 + 8 + 8 + 256) + (T - 1) * 576
     assert bench.new_token_bytes(T, H, True, T - 1) == fp8
     assert bench.new_token_bytes(T, H, False, T - 1) == bf16
 

@@ -53,7 +53,7 @@ def test_context_kv_projection_epilogue_chain_full(mk):
     # --- GPU: projection, then the epilogue reading its output through strides
     y = torch.empty(T, L * 576, dtype=torch.bfloat16, device=DEV)
     mk.mla_ctx_kv_proj(x.to(DEV), w_kn.t().contiguous().to(DEV), y)
-    cs = torch.empty(T, 64, dtype=torch.float64, device=DEV)
+    cs = torch.empty(T, 2 * 64, dtype=torch.float32, device=DEV)
     mk.mla_rope_cos_sin_cache(cs, T, 64, d["rope_base"])
     caches = [c.to(DEV) for c in d["caches"]]
     rows = torch.empty(L, T, 576, dtype=torch.bfloat16, device=DEV)

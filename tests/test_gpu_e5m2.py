@@ -137,7 +137,7 @@ def test_epilogue_context_shape(mk):
     d = synth.context_epilogue(with_gemm=False, fp8=True)
     L, T = d["num_layers"], d["num_tokens"]
     g = to_dev(d)
-    cs = torch.empty(T, 64, dtype=torch.float64, device=DEV)
+    cs = torch.empty(T, 2 * 64, dtype=torch.float32, device=DEV)
     mk.mla_rope_cos_sin_cache(cs, T, 64, d["rope_base"])
     rows = torch.empty(L, T, 576, dtype=torch.bfloat16, device=DEV)
     caches = g["caches"]

@@ -2,7 +2,7 @@
 CPU oracle.
 
 Tolerances (RMSNorm is computed in fp32 on the GPU and in float64 in the
-oracle; RoPE in float64 on both sides, from a float64 table): every normed /
+oracle; each rotated value is correctly rounded on both sides): every normed /
 rotated bf16 value within 1 bf16 ulp; every fp8
 cache code within 1 code; and wherever the GPU's bf16 row value equals the
 oracle's, the fp8 code is identical (the quantisation itself is exact).
@@ -31,32 +31,40 @@ pytestmark = [pytest.mark.gpu, requires_gpu]
 
 
 def test_rope_table_matches_f64(mk):
-    """The float64 table against numpy's float64 cos / sin of the same angles
-    theta = p * 10000^(-2i/64).  The device's and the host's pow may differ in
-    the last bit of the frequency, which moves theta (up to 4095 rad) by a few
-    float64 ulps of theta; so the bound is absolute: |d| <= 4 * 2^-53 *
-    (1 + theta), far below anything a bf16 rotation can resolve."""
+    """The fp32 hi / lo table against numpy's float64 cos / sin of the same
+    angles theta = p * 10000^(-2i/64): hi is the fp32 rounding of the value
+    (up to one fp32 ulp where the two libraries' float64 values straddle an
+    fp32 rounding boundary), and hi + lo is within 2^-47 + 4 * 2^-53 *
+    (1 + theta) of it (lo's own rounding, and the device's and the host's
+    pow differing in the last bit of the frequency, which moves theta, up to
+    4095 rad, by a few float64 ulps of theta)."""
     announce("rope table")
     P, maxp = 64, 4096
-    cs = torch.empty(maxp, P, dtype=torch.float64, device=DEV)
+    cs = torch.empty(maxp, 2 * P, dtype=torch.float32, device=DEV)
     mk.mla_rope_cos_sin_cache(cs, maxp, P, 10000.0)
     got = cs.cpu().numpy()
     p = np.arange(maxp, dtype=np.float64)[:, None]
     i = np.arange(P // 2, dtype=np.float64)[None, :]
     theta = p * np.power(10000.0, -2.0 * i / P)
     ref = np.concatenate([np.cos(theta), np.sin(theta)], axis=1)
-    bound = 4 * 2.0 ** -53 * (1.0 + np.concatenate([theta, theta], axis=1))
-    err = np.abs(got - ref)
+    hi, lo = got[:, :P], got[:, P:]
+    hulp = np.abs(hi.view(np.int32).astype(np.int64) - ref.astype(np.float32).view(np.int32))
+    assert np.all(hulp <= 1) and np.mean(hulp == 0) > 0.999
+    assert np.all(np.abs(lo) <= np.spacing(np.abs(hi)))           # lo below hi's ulp
+    both = hi.astype(np.float64) + lo.astype(np.float64)
+    th = np.concatenate([theta, theta], axis=1)
+    err = np.abs(both - ref)
+    bound = 2.0 ** -47 + 4 * 2.0 ** -53 * (1.0 + th)
     assert np.all(err <= bound), float((err / bound).max())
-    announce(f"rope table: {np.mean(got == ref):.5f} identical, "
-             f"max |d| / bound {float((err / bound).max()):.3f}")
+    announce(f"rope table: hi {np.mean(hulp == 0):.5f} identical to RN32, "
+             f"max |hi + lo - ref| / bound {float((err / bound).max()):.3f}")
 
 
 def run_epilogue(mk, d, dtype, dbg=True):
     g = to_dev(d)
     L, T = d["num_layers"], d["num_tokens"]
     maxp = int(d["positions"].max()) + 1
-    cs = torch.empty(maxp, 64, dtype=torch.float64, device=DEV)
+    cs = torch.empty(maxp, 2 * 64, dtype=torch.float32, device=DEV)
     mk.mla_rope_cos_sin_cache(cs, maxp, 64, d["rope_base"])
     rows = torch.empty(L, T, 576, dtype=torch.bfloat16, device=DEV) if dbg else None
     caches = g["caches"]
@@ -152,6 +160,36 @@ def test_epilogue_without_debug_rows_matches(mk):
     c2, _ = run_epilogue(mk, d, "fp8", dbg=False)
     for a, b in zip(c1, c2):
         assert torch.equal(a, b)
+
+
+def test_epilogue_rope_near_cancellation(mk):
+    """k_pe rows built so that the first half of every rotation nearly
+    cancels (x_{i+32} = bf16(x_i cos / sin), so x_i cos - x_{i+32} sin is a
+    few bf16 roundings of x_i), which sends most wavefronts down the exact
+    path of the rotation: every rotated value within 1 bf16 ulp of the
+    oracle's, and identical to it almost everywhere."""
+    announce("epilogue RoPE near cancellation")
+    d = synth.context_epilogue(num_tokens=512, num_blocks=16, with_gemm=False, seed=61)
+    g = torch.Generator().manual_seed(62)
+    T, L = d["num_tokens"], d["num_layers"]
+    pos = torch.randint(1, 4096, (T,), generator=g, dtype=torch.int64)
+    i = np.arange(32, dtype=np.float64)
+    theta = pos.numpy()[:, None].astype(np.float64) * np.power(10000.0, -2.0 * i / 64)
+    akv = d["all_kv"].clone()
+    x = akv[:, :, 512:544].float().numpy().astype(np.float64)
+    ratio = np.cos(theta) / np.sin(theta)
+    partner = np.where(np.abs(ratio)[:, None, :] < 8, x * ratio[:, None, :], x)
+    akv[:, :, 544:576] = torch.from_numpy(partner.astype(np.float32)).to(torch.bfloat16)
+    d["all_kv"] = akv
+    d["positions"] = pos
+    caches, rows = run_epilogue(mk, d, "fp8")
+    ref_rows = oracle.ctx_kv_epilogue(u16(d["all_kv"]), u16(d["gamma"]), d["eps"],
+                                      pos.numpy(), None, None)
+    got = u16(rows)[..., 512:]
+    ul = bf16_ulps(got, ref_rows[..., 512:])
+    announce(f"near cancellation: rope part {np.mean(ul == 0):.6f} identical, max {ul.max()} ulp")
+    assert ul.max() <= 1 and np.mean(ul == 0) > 0.999
+    check_rows_insert(d, caches, rows, "fp8")
 
 
 def test_epilogue_one_hot_rows(mk):

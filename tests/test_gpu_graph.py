@@ -36,7 +36,7 @@ def test_captured_step_replays_match_eager_runs(mk):
     kvb = torch.zeros(T, H, 256, dtype=bf, device=DEV)
     lat = torch.zeros(T, 576, dtype=bf, device=DEV)
     pos = torch.zeros(T, dtype=torch.int64, device=DEV)
-    cs = torch.empty(4096, 64, dtype=torch.float64, device=DEV)
+    cs = torch.empty(4096, 2 * 64, dtype=torch.float32, device=DEV)
     mk.mla_rope_cos_sin_cache(cs, 4096, 64, 10000.0)
     nt_cache = synth.random_bytes((16, BS, 576), g).to(DEV)
     nt_slots = torch.zeros(T, dtype=torch.int64, device=DEV)

@@ -7,9 +7,9 @@ pack + RoPE of q_pe and k_pe + query row + insert of [kv_c | RoPE(k_pe)]).
 
 Bars: the nope parts, V and the cache's kv_c part are casts or copies, so
 bit-exact; the rotated parts follow the context epilogue's RoPE bar -- within
-1 bf16 ulp of the float64 oracle (both sides rotate in float64 from float64
-angles and round once; they can differ only where the device's and the
-host's cos / sin differ in the last float64 bit and that moves a rounding);
+1 bf16 ulp of the float64 oracle (both sides round the rotation correctly
+to bf16; they can differ only where the device's and the host's cos / sin
+differ in their last bits and that moves a rounding);
 their fp8 codes are identical wherever the GPU's bf16 rotation equals the
 oracle's, else within one code.  Workloads: strided views of the model's tensors (query
 [T, H, 192], kv_b_proj output [T, H, 256], latent row [T, 576]), 1 to 300
@@ -69,7 +69,7 @@ class Case:
         check_slots(d["slots"], d["cache"].shape[0] * d["cache"].shape[1])
         self.g = {k: v.to(DEV) for k, v in d.items() if isinstance(v, torch.Tensor)}
         self.max_pos = d["max_pos"]
-        self.cs = torch.empty(self.max_pos, P, dtype=torch.float64, device=DEV)
+        self.cs = torch.empty(self.max_pos, 2 * P, dtype=torch.float32, device=DEV)
         import fp8_paged_insert_amd as mk
         mk.mla_rope_cos_sin_cache(self.cs, self.max_pos, P, 10000.0)
 
@@ -247,7 +247,7 @@ def test_other_head_widths(mk, nope, vdim, fp8):
     kn, v = synth.bf16_normal((T, H, nope), g), synth.bf16_normal((T, H, vdim), g)
     kv = synth.bf16_normal((T, R + P), g)
     pos = torch.randint(0, 4096, (T,), generator=g)
-    cs = torch.empty(4096, P, dtype=torch.float64, device=DEV)
+    cs = torch.empty(4096, 2 * P, dtype=torch.float32, device=DEV)
     mk.mla_rope_cos_sin_cache(cs, 4096, P, 10000.0)
     kvd = kv.to(DEV)
 

@@ -117,7 +117,7 @@ def test_proj_then_epilogue_chain(mk):
     ref_y = oracle.gemm_rows(u16(d["x"]), u16(d["w_kn"]))
     check_close(u16(y), ref_y, "chain projection")
     all_kv = y.view(T, L, 576)
-    cs = torch.empty(T, 64, dtype=torch.float64, device=DEV)
+    cs = torch.empty(T, 2 * 64, dtype=torch.float32, device=DEV)
     mk.mla_rope_cos_sin_cache(cs, T, 64, 10000.0)
     caches = [c.to(DEV) for c in d["caches"]]
     rows = torch.empty(L, T, 576, dtype=torch.bfloat16, device=DEV)
