@@ -399,28 +399,41 @@ def single_layer_component(torch, mk, dev):
             "bytes": small_insert_bytes(T, T, 1, False)}
 
 
-def copy_ceiling(torch, dev):
-    """A plain 1 GiB device-to-device copy (torch's copy kernel), median of 10
-    after 3 warm-up copies: the HBM rate a streaming kernel reaches on this
-    GPU, next to the 8 TB/s peak the roofline uses."""
+def copy_ceiling(torch, mk, dev, flush):
+    """Device-to-device copies as the ceiling the HBM-bound kernels are
+    compared with: the runtime's copy (torch copy_, 1 GiB) and the library's
+    streaming copy (the launch shape of its streaming kernels) at 1 GiB and
+    at the total size of the context epilogue (36.6 MB moved) and of one
+    gather (14.2 MB moved); each timed by its own launch events after a
+    cache flush (the runtime's copy with stream events), median of 20."""
+    out = {}
     n = 1 << 30
     src = torch.ones(n, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
     times = []
-    for _ in range(10):
+    for i in range(23):
+        flush_llc(torch, flush)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
         dst.copy_(src)
         e1.record()
         e1.synchronize()
-        times.append(e0.elapsed_time(e1) * 1e3)
+        if i >= 3:
+            times.append(e0.elapsed_time(e1) * 1e3)
     us = statistics.median(times)
+    out["runtime_copy_1GiB"] = {"bytes": 2 * n, "us": round(us, 2),
+                                "GBps": round(2 * n / us / 1e3, 1),
+                                "frac_of_peak": round(2 * n / us / 1e3 / HBM_PEAK_GBS, 4)}
+    for name, moved in (("stream_copy_1GiB", 2 * n),
+                        ("stream_copy_epilogue_size", epilogue_bytes(L, 4096)),
+                        ("stream_copy_gather_size", gather_bytes(8192))):
+        half = (moved // 2) // 16 * 16
+        us, p90 = kernel_us(torch, mk, lambda: mk.mla_stream_copy(dst[:half], src[:half]), flush,
+                            reps=20, warm=3)
+        out[name] = rate(us, p90, 2 * half)
     del src, dst
-    return {"bytes": 2 * n, "us": round(us, 2), "GBps": round(2 * n / us / 1e3, 1),
-            "frac_of_peak": round(2 * n / us / 1e3 / HBM_PEAK_GBS, 4)}
+    return out
 
 
 def kernel_us(torch, mk, fn, flush, reps=100, warm=10):
@@ -497,20 +510,27 @@ def context_pack_component(torch, mk, dev, flush):
         mk.mla_ctx_kv_pack(kvb[:, :8, :128], ws[:, 512:], key8_tp, v=kvb[:, :8, 128:],
                            v_out=v8_tp, mode=mk.MLA_PACK_KEY_V_FP8)
 
-    # the same fp8 pack as a grid-stride loop over a capped grid (16 workgroups
-    # of 256 threads per compute unit, about 10 chunks per thread)
-    cap = 16 * torch.cuda.get_device_properties(dev).multi_processor_count
+    # the same fp8 pack as a grid-stride loop over capped grids of 16, 32 and
+    # 64 workgroups of 256 threads per compute unit (about 10, 5 and 2.5
+    # chunks per thread; the full grid has one)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
 
-    def pack8_capped():
-        mk.mla_ctx_kv_pack(kvb[..., :128], ws[:, 512:], key8, v=kvb[..., 128:], v_out=v8,
-                           mode=mk.MLA_PACK_KEY_V_FP8, max_blocks=cap)
+    def pack8_capped(per_cu):
+        return lambda: mk.mla_ctx_kv_pack(kvb[..., :128], ws[:, 512:], key8, v=kvb[..., 128:],
+                                          v_out=v8, mode=mk.MLA_PACK_KEY_V_FP8,
+                                          max_blocks=per_cu * cus)
 
     out = {"workload": "chunked-context pack, 8192 tokens x 64 heads (tp8 share: 8 heads)",
-           "capped_grid_blocks": cap}
+           "full_grid_blocks": (8192 * 64 * (12 + 8) + 255) // 256}
     for name, fn, nbytes in (("gather", gather, gather_bytes(8192)),
                              ("gather_raw_fp8", gather_raw, gather_raw_bytes(8192)),
                              ("pack_fp8", pack8, pack_fp8_bytes(8192, 64)),
-                             ("pack_fp8_capped_grid", pack8_capped, pack_fp8_bytes(8192, 64)),
+                             ("pack_fp8_capped_16_per_cu", pack8_capped(16),
+                              pack_fp8_bytes(8192, 64)),
+                             ("pack_fp8_capped_32_per_cu", pack8_capped(32),
+                              pack_fp8_bytes(8192, 64)),
+                             ("pack_fp8_capped_64_per_cu", pack8_capped(64),
+                              pack_fp8_bytes(8192, 64)),
                              ("pack_fp8_kpe_raw", pack8_raw, pack_fp8_kpe_raw_bytes(8192, 64)),
                              ("pack_fp8_fp16_inputs", pack8_f16, pack_fp8_bytes(8192, 64)),
                              ("pack_bf16", packb, pack_bf16_bytes(8192, 64)),
@@ -631,7 +651,12 @@ def projection_component(torch, mk, dev, flush):
 
     g = synth.gen(3, dev)
     x = synth.bf16_normal((4096, 7168), g, dev)
-    w_nk = synth.bf16_normal((7168, L * W), g, dev, std=0.02).t().contiguous()
+    # the weight as the workload states it, the [K, N] matrix, converted
+    # into the [N, K] storage the projection reads by the library's transpose
+    w_kn = synth.bf16_normal((7168, L * W), g, dev, std=0.02)
+    w_nk = torch.empty(L * W, 7168, dtype=torch.bfloat16, device=dev)
+    mk.mla_transpose_bf16(w_kn, w_nk)
+    tr_us, tr_p90 = kernel_us(torch, mk, lambda: mk.mla_transpose_bf16(w_kn, w_nk), flush)
     y = torch.empty(4096, L * W, dtype=torch.bfloat16, device=dev)
     try:
         us, p90 = kernel_us(torch, mk, lambda: mk.mla_ctx_kv_proj(x, w_nk, y), flush)
@@ -656,25 +681,33 @@ def projection_component(torch, mk, dev, flush):
     cs = torch.empty(4096, 2 * P, dtype=torch.float32, device=dev)
     mk.mla_rope_cos_sin_cache(cs, 4096, P, 10000.0)
     ptrs = mk.cache_ptr_table(e["caches"])
-    e2e = []
+    e2e, e2e_tr = [], []
     for i in range(25):
-        flush_llc(torch, flush)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        mk.mla_ctx_kv_proj(x, w_nk, y)
-        mk.mla_ctx_kv_epilogue(y.view(4096, L, W), e["gamma"], e["eps"], e["positions"], cs,
-                               ptrs, e["slot_mapping"], 64, 64 * W, W, e["scales"], "fp8")
-        e1.record()
-        e1.synchronize()
-        if i >= 3:
-            e2e.append(e0.elapsed_time(e1) * 1e3)
+        for with_tr, acc in ((False, e2e), (True, e2e_tr)):
+            flush_llc(torch, flush)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            if with_tr:
+                mk.mla_transpose_bf16(w_kn, w_nk)
+            mk.mla_ctx_kv_proj(x, w_nk, y)
+            mk.mla_ctx_kv_epilogue(y.view(4096, L, W), e["gamma"], e["eps"], e["positions"], cs,
+                                   ptrs, e["slot_mapping"], 64, 64 * W, W, e["scales"], "fp8")
+            e1.record()
+            e1.synchronize()
+            if i >= 3:
+                acc.append(e0.elapsed_time(e1) * 1e3)
     flops = 2 * 4096 * 7168 * L * W
     return {"workload": "context_kv_proj 4096x7168 . 7168x2880 (bf16 MFMA, fp32 acc)",
             "us": round(us, 2), "p90_us": round(p90, 2), "TFLOPs": round(flops / us / 1e6, 1),
             "frac_of_peak": round(flops / us / 1e6 / 2500.0, 4),
             "torch_matmul_us_stream_events": round(statistics.median(ref), 2),
-            "with_epilogue_us_stream_events": round(statistics.median(e2e), 2)}
+            "with_epilogue_us_stream_events": round(statistics.median(e2e), 2),
+            "weight_transpose": {"us": round(tr_us, 2), "p90_us": round(tr_p90, 2),
+                                 "bytes": 2 * 7168 * L * W * 2,
+                                 "note": "[7168, 2880] -> [2880, 7168], once per weight"},
+            "with_weight_transpose_and_epilogue_us_stream_events": round(statistics.median(e2e_tr),
+                                                                         2)}
 
 
 # ----------------------------------------------------------- CPU baseline --
@@ -901,9 +934,11 @@ def main():
         "roofline": roofline,
     }
     # the same work with the gather and the pack as launches of their own, on
-    # the default full grid and as grid-stride loops over a capped grid (16
-    # workgroups per compute unit)
-    cap = 16 * torch.cuda.get_device_properties(dev).multi_processor_count
+    # the default full grid and as grid-stride loops over a capped grid (64
+    # workgroups of 256 threads per compute unit: 16384 workgroups, 2.5 chunks
+    # per thread, against 40960 for one chunk per thread; the fastest of the
+    # caps 16, 32 and 64 per compute unit, which the components report)
+    cap = 64 * torch.cuda.get_device_properties(dev).multi_processor_count
     for name, mb in (("separate_launch_step", 0), ("capped_grid_step", cap)):
         wl.step_separate(max_blocks=mb)
         torch.cuda.synchronize()
@@ -920,7 +955,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_components:
         flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        result["copy_ceiling"] = copy_ceiling(torch, dev)
+        result["copy_ceiling"] = copy_ceiling(torch, mk, dev, flush)
         comps = {"small_batch_insert": small_batch(torch, mk, dev),
                  "single_layer_insert": single_layer_component(torch, mk, dev),
                  "context_pack": context_pack_component(torch, mk, dev, flush),

@@ -39,6 +39,8 @@ from ._binding import (  # noqa: F401
     mla_new_token_epilogue,
     mla_kv_insert_grouped,
     mla_rope_cos_sin_cache,
+    mla_stream_copy,
+    mla_transpose_bf16,
     parse_kv_cache_dtype,
     prepare_insert_grouped,
     PreparedInsert,

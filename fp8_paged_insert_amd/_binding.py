@@ -43,6 +43,7 @@ EXPORTS = (
     "mla_kv_insert_grouped", "mla_rope_cos_sin_cache", "mla_ctx_kv_epilogue",
     "mla_ctx_kv_proj", "mla_ctx_latent_gather", "mla_ctx_kv_pack", "mla_ctx_kv_pack_gather",
     "mla_ctx_merge_chunk", "mla_ctx_neutralize_partials", "mla_new_token_epilogue",
+    "mla_stream_copy", "mla_transpose_bf16",
 )
 
 
@@ -75,6 +76,8 @@ _SIGS = {
                                       _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp,
                                       _vp, _i32, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i32,
                                       _vp, _vp]),
+    "mla_stream_copy": (_i32, [_vp, _vp, _i64, _vp]),
+    "mla_transpose_bf16": (_i32, [_vp, _i64, _i64, _i64, _vp, _i64, _vp]),
     "mla_ctx_merge_chunk": (_i32, [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp,
                                    _i64, _i64, _i64, _i64, _i64, _i32, _vp]),
     "mla_ctx_neutralize_partials": (_i32, [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64,
@@ -446,6 +449,22 @@ def _gather_args(cache, src_slots, out, cache_scale, kv_cache_dtype):
             _ptr(out))
 
 
+def mla_transpose_bf16(src, dst):
+    """dst[c, r] = src[r, c]: src bf16 [rows, cols] with contiguous rows,
+    dst bf16 [cols, rows] with contiguous rows (weight preparation for
+    mla_ctx_kv_proj: the [K, N] matrix -> its [N, K] storage)."""
+    _need(src, (torch.bfloat16,), "src")
+    _need(dst, (torch.bfloat16,), "dst")
+    if src.dim() != 2 or dst.dim() != 2 or tuple(dst.shape) != (src.shape[1], src.shape[0]):
+        raise RuntimeError("src [rows, cols] and dst [cols, rows] expected")
+    for t, n in ((src, "src"), (dst, "dst")):
+        if t.shape[1] > 1 and t.stride(1) != 1:
+            raise RuntimeError(f"{n} must have contiguous rows")
+    _same_device(dst, src, "dst", "src")
+    _check(lib().mla_transpose_bf16(_ptr(src), src.shape[0], src.shape[1], src.stride(0),
+                                    _ptr(dst), dst.stride(0), _stream(src)), "mla_transpose_bf16")
+
+
 def mla_ctx_latent_gather(cache, src_slots, out, cache_scale=None, kv_cache_dtype="fp8",
                           max_blocks=0):
     """out[j, :] = cache row of src_slots[j]; cache [num_blocks, block_size, E].
@@ -676,3 +695,16 @@ def mla_ctx_neutralize_partials(out, lse, no_context):
         _ptr(out), out.stride(0), out.stride(1), _ptr(lse), lse.stride(0), lse.stride(1),
         _ptr(no_context), T, H, D, _stream(out))
     _check(st, "mla_ctx_neutralize_partials")
+
+
+# ------------------------------------------------------------ measurement --
+def mla_stream_copy(dst, src):
+    """dst <- src (same number of bytes, contiguous, 16-byte multiples), with
+    the library's streaming launch shape: a measurement aid."""
+    if not (dst.is_contiguous() and src.is_contiguous()):
+        raise RuntimeError("dst and src must be contiguous")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise RuntimeError("dst and src must have the same size in bytes")
+    _same_device(dst, src, "dst", "src")
+    _check(lib().mla_stream_copy(_ptr(dst), _ptr(src), nbytes, _stream(src)), "mla_stream_copy")

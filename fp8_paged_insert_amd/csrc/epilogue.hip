@@ -159,6 +159,8 @@ __global__ __launch_bounds__(256, 5) void epilogue_kernel(const EpiArgs a) {
     const float* cs = a.cos_sin + pos * (2 * kP) + kPe * (j & 7);
     const uint4 cv = ld16(cs);
     const uint4 sv = ld16(cs + kP / 2);
+    const uint4 clv = ld16(cs + kP);
+    const uint4 slv = ld16(cs + kP + kP / 2);
     // Keep every load of the row here, ahead of the first wait: without this
     // fence the compiler sinks the loads used only by the stores into the
     // store branch, after the reduction, adding memory round trips.
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(256, 5) void epilogue_kernel(const EpiArgs a) {
     float xq[kPe];
 #pragma unroll
     for (int e = 0; e < kPe; ++e) xq[e] = dpp_f<kDppRor8>(xp[e]);
-    const uint2 ype = rope4(xp, xq, cc, sn, first_half, cs + kP, cs + kP + kP / 2);
+    const uint2 ype = rope4v(xp, xq, cc, sn, first_half, clv, slv);
 
     // ---- RMSNorm: fp32 sum of squares over the row's 16 lanes.  The fp32
     // values are taken from the bf16 words twice (a shift or a mask each)

@@ -69,18 +69,9 @@ constexpr int kGroupRows = 4;
 
 // Workgroups that only warm the last-level cache (see prefetch_operands):
 // at most this many, and only on compute units the tiles leave idle.
-#ifndef MLA_PROJ_PREFETCH_WGS
-#define MLA_PROJ_PREFETCH_WGS 16
-#endif
-#ifndef MLA_PROJ_PREFETCH_FIRST
-#define MLA_PROJ_PREFETCH_FIRST 2
-#endif
-constexpr int kPrefetchWgs = MLA_PROJ_PREFETCH_WGS;
-constexpr int kPrefetchFirst = MLA_PROJ_PREFETCH_FIRST;  // first K stage they touch
-#ifndef MLA_PROJ_PREFETCH_BATCH
-#define MLA_PROJ_PREFETCH_BATCH 16
-#endif
-constexpr int kPrefetchBatch = MLA_PROJ_PREFETCH_BATCH;   // loads in flight per lane
+constexpr int kPrefetchWgs = 16;
+constexpr int kPrefetchFirst = 2;    // first K stage they touch
+constexpr int kPrefetchBatch = 16;   // loads in flight per lane
 
 struct GemmArgs {
   const uint16_t* x;

@@ -126,9 +126,9 @@ __device__ __forceinline__ uint32_t f64_to_bf16_bits(double d) {
 // value is farther than that from the midpoint).  Otherwise the whole
 // wavefront takes the exact path (a uniform branch, taken by about one
 // wavefront in a hundred): the rotation in float64 with hi + lo, then one
-// correct rounding to bf16.
-// c / s: the lane's 4 cos / sin hi values; lo_c / lo_s: where the matching
-// lo values sit in the table (read only on the exact path).
+// correct rounding to bf16.  In the helpers below x, p, c, s are the lane's
+// 4 values, their partners and the 4 cos / sin hi values.
+
 // One rotated value in float64 from the exact table values hi + lo (each
 // operation rounded on its own, then one correct rounding to bf16).
 __device__ __forceinline__ uint32_t rope1_exact(float x, float p, float ch, float cl, float sh,
@@ -141,31 +141,62 @@ __device__ __forceinline__ uint32_t rope1_exact(float x, float p, float ch, floa
   return f64_to_bf16_bits(first ? u - v : u + v);
 }
 
-__device__ __forceinline__ uint2 rope4(const float* x, const float* p, const float* c,
-                                       const float* s, bool first, const float* lo_c,
-                                       const float* lo_s) {
+// The fast path of the four values: the fp32 rotations and whether every
+// one of them is known to round correctly (see above).
+struct Rope4Fast {
   float y[4];
-  bool safe = true;
+  bool safe;
+};
+__device__ __forceinline__ Rope4Fast rope4_fast(const float* x, const float* p, const float* c,
+                                                const float* s, bool first) {
+  Rope4Fast r;
+  r.safe = true;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const float ps = p[e] * s[e];
-    y[e] = __builtin_fmaf(x[e], c[e], first ? -ps : ps);
+    r.y[e] = __builtin_fmaf(x[e], c[e], first ? -ps : ps);
     const float bound = 0x1p-22f * (__builtin_fabsf(x[e]) + __builtin_fabsf(p[e]));
-    const float mid = __uint_as_float((__float_as_uint(y[e]) & 0xFFFF0000u) | 0x8000u);
+    const float mid = __uint_as_float((__float_as_uint(r.y[e]) & 0xFFFF0000u) | 0x8000u);
     // false for NaN (and for an infinite bound), which then takes the exact path
-    safe = safe && __builtin_fabsf(y[e] - mid) > bound;
+    r.safe = r.safe && __builtin_fabsf(r.y[e] - mid) > bound;
   }
-  if (__builtin_expect(__builtin_amdgcn_ballot_w64(!safe) != 0, 0)) {
-    const float4 cl = *reinterpret_cast<const float4*>(lo_c);
-    const float4 sl = *reinterpret_cast<const float4*>(lo_s);
-    const float cls[4] = {cl.x, cl.y, cl.z, cl.w}, sls[4] = {sl.x, sl.y, sl.z, sl.w};
-    uint32_t b[4];
+  return r;
+}
+
+__device__ __forceinline__ uint2 rope4_exact(const float* x, const float* p, const float* c,
+                                             const float* s, bool first, uint4 cl, uint4 sl) {
+  const float cls[4] = {__uint_as_float(cl.x), __uint_as_float(cl.y), __uint_as_float(cl.z),
+                        __uint_as_float(cl.w)};
+  const float sls[4] = {__uint_as_float(sl.x), __uint_as_float(sl.y), __uint_as_float(sl.z),
+                        __uint_as_float(sl.w)};
+  uint32_t b[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) b[e] = rope1_exact(x[e], p[e], c[e], cls[e], s[e], sls[e], first);
-    return make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
-  }
+  for (int e = 0; e < 4; ++e) b[e] = rope1_exact(x[e], p[e], c[e], cls[e], s[e], sls[e], first);
+  return make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+}
+
+// lo_c / lo_s: where the lo values of the lane's angles sit in the table;
+// read only when the exact path runs.
+__device__ __forceinline__ uint2 rope4(const float* x, const float* p, const float* c,
+                                       const float* s, bool first, const float* lo_c,
+                                       const float* lo_s) {
+  const Rope4Fast r = rope4_fast(x, p, c, s, first);
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(!r.safe) != 0, 0))
+    return rope4_exact(x, p, c, s, first, *reinterpret_cast<const uint4*>(lo_c),
+                       *reinterpret_cast<const uint4*>(lo_s));
   // no NaN reaches here, so the hardware converter (RNE) serves
-  return make_uint2(cvt_bf16x2(y[0], y[1]), cvt_bf16x2(y[2], y[3]));
+  return make_uint2(cvt_bf16x2(r.y[0], r.y[1]), cvt_bf16x2(r.y[2], r.y[3]));
+}
+
+// rope4 with the lo values already in registers, loaded together with the
+// hi ones: for a latency-bound caller (the context epilogue) the rare exact
+// path then adds no dependent load to its wavefront.
+__device__ __forceinline__ uint2 rope4v(const float* x, const float* p, const float* c,
+                                        const float* s, bool first, uint4 cl, uint4 sl) {
+  const Rope4Fast r = rope4_fast(x, p, c, s, first);
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(!r.safe) != 0, 0))
+    return rope4_exact(x, p, c, s, first, cl, sl);
+  return make_uint2(cvt_bf16x2(r.y[0], r.y[1]), cvt_bf16x2(r.y[2], r.y[3]));
 }
 
 
@@ -374,21 +405,9 @@ __device__ __forceinline__ void st8(void* p, uint2 v) {
 // large contiguous outputs that the next kernel of a chunk loop does not
 // re-read from cache, so they stream; the insert and epilogue scatter
 // 576-byte rows, where ordinary stores let the last-level cache merge lines.
-#ifndef MLA_PACK_STREAM
-#define MLA_PACK_STREAM 1
-#endif
-#ifndef MLA_GATHER_STREAM
-#define MLA_GATHER_STREAM 1
-#endif
-#ifndef MLA_INSERT_STREAM
-#define MLA_INSERT_STREAM 0
-#endif
-#ifndef MLA_EPI_STREAM
-#define MLA_EPI_STREAM 0
-#endif
-constexpr bool kPackStream = MLA_PACK_STREAM != 0;
-constexpr bool kGatherStream = MLA_GATHER_STREAM != 0;
-constexpr bool kInsertStream = MLA_INSERT_STREAM != 0;
-constexpr bool kEpiStream = MLA_EPI_STREAM != 0;
+constexpr bool kPackStream = true;
+constexpr bool kGatherStream = true;
+constexpr bool kInsertStream = false;
+constexpr bool kEpiStream = false;
 
 }  // namespace mla

@@ -4,6 +4,7 @@
  * The library computes the data-parallel path around the MLA latent KV cache
  * of a multi-layer draft model:
  *   projection  mla_ctx_kv_proj        Y = X . W  (one KV-only GEMM for all layers)
+ *               mla_transpose_bf16     [K, N] weight -> the [N, K] storage the projection reads
  *   epilogue    mla_ctx_kv_epilogue    RMSNorm(kv_c) | RoPE(k_pe) -> fp8/bf16 -> paged caches
  *   insert      mla_kv_insert_grouped  [kv_c | k_pe] -> fp8/bf16 -> paged caches, all layers
  *   gather      mla_ctx_latent_gather  paged cache rows -> contiguous bf16 (or raw fp8) workspace
@@ -226,7 +227,8 @@ int32_t mla_ctx_kv_epilogue(
  * X device bf16 [T, K] row-major (row stride x_row_stride, elements).
  * W device bf16 [N, K] row-major and dense (row stride K): the linear
  *   layer's [out, in] weight storage, i.e. the transpose of the [K, N]
- *   matrix X is multiplied by.
+ *   matrix X is multiplied by.  A caller holding the [K, N] matrix converts
+ *   it once with mla_transpose_bf16 (rows K, cols N).
  * Y device bf16 [T, N] row-major (row stride y_row_stride).
  * K must be a multiple of 64 and N a multiple of 16; pointers and row
  * strides 16-byte aligned.  T may be any value >= 0.
@@ -237,6 +239,23 @@ int32_t mla_ctx_kv_epilogue(
 int32_t mla_ctx_kv_proj(const void* X, int64_t x_row_stride, int64_t T,
                         int64_t K, const void* W, int64_t N, void* Y,
                         int64_t y_row_stride, mla_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * mla_transpose_bf16 -- weight preparation for mla_ctx_kv_proj: dst[c, r] =
+ * src[r, c] for r < rows, c < cols, bit for bit ([P2] 实现拆解 item 2: the
+ * merged linear layer holds its weight as [out, in]; a weight held as the
+ * [in, out] = [K, N] matrix that X is multiplied by is converted once with
+ * this call into the [N, K] storage mla_ctx_kv_proj reads).  A weight does
+ * not change between calls, so the conversion is not part of the
+ * per-call path.
+ * src device bf16 [rows, cols] (row stride src_row_stride >= cols);
+ * dst device bf16 [cols, rows] (row stride dst_row_stride >= rows).
+ * rows and cols multiples of 8; addresses and row strides 16-byte aligned
+ * (MLA_ERR_UNSUPPORTED / MLA_ERR_MISALIGNED otherwise); src and dst must not
+ * overlap (MLA_ERR_INVALID_ARGUMENT).
+ * ------------------------------------------------------------------------ */
+int32_t mla_transpose_bf16(const void* src, int64_t rows, int64_t cols, int64_t src_row_stride,
+                           void* dst, int64_t dst_row_stride, mla_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * mla_ctx_latent_gather -- read one sequence's context rows out of a paged
@@ -429,6 +448,17 @@ int32_t mla_new_token_epilogue(
     void* q_out, void* key_out, void* v_out, void* cache, int32_t cache_dtype,
     const float* cache_scale, const int64_t* slot_mapping, int64_t block_size,
     int64_t block_stride, int64_t entry_stride, int64_t max_blocks, mla_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * mla_stream_copy -- measurement aid, not a step of the path: copy `bytes`
+ * bytes from src to dst (device, 16-byte aligned, size a multiple of 16, no
+ * overlap) with the launch shape of the library's streaming kernels (one
+ * 16-byte chunk per thread over the full grid, cache-bypassing loads,
+ * streaming stores).  Its rate at a given size is the ceiling the
+ * bandwidth-bound kernels are compared with (the roofline's "measured
+ * device-to-device copy bandwidth").
+ * ------------------------------------------------------------------------ */
+int32_t mla_stream_copy(void* dst, const void* src, int64_t bytes, mla_stream_t stream);
 
 #ifdef __cplusplus
 }

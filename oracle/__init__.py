@@ -115,6 +115,7 @@ def _load():
                                    _i64, _i64, _i64, _i64, _i64, _int]),
         "orc_neutralize_partials": (_int, [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64,
                                            _i64]),
+        "orc_transpose_u16": (_int, [_vp, _i64, _i64, _i64, _vp, _i64]),
         "orc_e5m2_decode": (_f64, [ctypes.c_uint8]),
         "orc_e5m2_encode": (ctypes.c_uint8, [_f64]),
         "orc_e5m2_encode_f32_n": (None, [_vp, _i64, _vp]),
@@ -515,3 +516,17 @@ def neutralize_partials(out, lse, no_context):
         _ptr(lse), lse.strides[0] // 4, lse.strides[1] // 4, _ptr(m), T, H, D)
     _check(rc, "neutralize_partials")
     return out, lse
+
+
+# ------------------------------------------------------ weight preparation --
+def transpose(src: np.ndarray) -> np.ndarray:
+    """[rows, cols] 16-bit bit patterns (rows may be strided) -> the
+    contiguous [cols, rows] transpose."""
+    _need(src, np.uint16, "src")
+    rows, cols = src.shape
+    if cols and src.strides[1] != 2:
+        raise ValueError("src rows must be contiguous")
+    out = np.empty((cols, rows), np.uint16)
+    _check(_load().orc_transpose_u16(_ptr(src), rows, cols, src.strides[0] // 2, _ptr(out), rows),
+           "transpose")
+    return out

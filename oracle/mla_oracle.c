@@ -813,3 +813,17 @@ int orc_neutralize_partials(uint16_t* out, int64_t out_tok_stride, int64_t out_h
   }
   return ORC_OK;
 }
+
+/*
+ * Weight preparation for the fused KV projection ([P2] 实现拆解 item 2: the
+ * merged linear layer holds its weight as [out, in]; the fused context-KV
+ * workload states the weight as the [in, out] matrix).  The definition of
+ * a transpose: dst[c][r] = src[r][c], bit for bit.
+ */
+int orc_transpose_u16(const uint16_t* src, int64_t rows, int64_t cols, int64_t src_row_stride,
+                      uint16_t* dst, int64_t dst_row_stride) {
+  if (rows < 0 || cols < 0) return ORC_EINVAL;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < cols; ++c) dst[c * dst_row_stride + r] = src[r * src_row_stride + c];
+  return ORC_OK;
+}

@@ -140,6 +140,10 @@ int orc_neutralize_partials(uint16_t* out, int64_t out_tok_stride, int64_t out_h
                             const uint8_t* no_context, int64_t num_tokens,
                             int64_t num_heads, int64_t head_dim);
 
+/* dst[c][r] = src[r][c] (16-bit elements, bit for bit). */
+int orc_transpose_u16(const uint16_t* src, int64_t rows, int64_t cols, int64_t src_row_stride,
+                      uint16_t* dst, int64_t dst_row_stride);
+
 #ifdef __cplusplus
 }
 #endif

@@ -218,6 +218,28 @@ def test_pack_gather_both_parts_empty_is_a_noop(mk):
     assert pack_gather_call(mk, dict(T=0), dict(T=0)) == mk.MLA_OK
 
 
+def test_stream_copy_rejects(mk):
+    lib = mk.lib()
+    assert lib.mla_stream_copy(P16, P16 + (1 << 20), -16, None) == mk.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_stream_copy(P16, P16 + (1 << 20), 0, None) == mk.MLA_OK
+    assert lib.mla_stream_copy(P_ODD, P16 + (1 << 20), 64, None) == mk.MLA_ERR_MISALIGNED
+    assert lib.mla_stream_copy(P16, P16 + (1 << 20), 40, None) == mk.MLA_ERR_MISALIGNED
+    assert lib.mla_stream_copy(P16, P16 + 32, 64, None) == mk.MLA_ERR_INVALID_ARGUMENT
+    assert "overlap" in mk.last_error()
+
+
+def test_transpose_rejects(mk):
+    lib = mk.lib()
+    far = P16 + (1 << 32)
+    assert lib.mla_transpose_bf16(P16, -8, 8, 8, far, 8, None) == mk.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_transpose_bf16(P16, 0, 8, 8, far, 8, None) == mk.MLA_OK
+    assert lib.mla_transpose_bf16(P16, 12, 8, 8, far, 12, None) == mk.MLA_ERR_UNSUPPORTED
+    assert lib.mla_transpose_bf16(P16, 16, 16, 8, far, 16, None) == mk.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_transpose_bf16(P_ODD, 16, 16, 16, far, 16, None) == mk.MLA_ERR_MISALIGNED
+    assert lib.mla_transpose_bf16(P16, 16, 16, 16, P16 + 64, 16, None) == mk.MLA_ERR_INVALID_ARGUMENT
+    assert "overlap" in mk.last_error()
+
+
 def test_rope_table_rejects(mk):
     assert mk.lib().mla_rope_cos_sin_cache(P16, 10, 63, 10000.0, None) == mk.MLA_ERR_INVALID_ARGUMENT
     assert mk.lib().mla_rope_cos_sin_cache(P16, 10, 64, -1.0, None) == mk.MLA_ERR_INVALID_ARGUMENT

@@ -7,7 +7,9 @@ output viewed as [T, L, 576] and split into kv_c and k_pe, the grouped
 RMSNorm of kv_c, RoPE of k_pe at the context positions, then the grouped
 insert of "PR #55356 完整报告" (关键源码片段, the grouped path).
 
-Workload: X [4096, 7168] ~ N(0, 1), W [7168, 5 * 576] ~ N(0, 0.02), gamma
+Workload: X [4096, 7168] ~ N(0, 1), W [7168, 5 * 576] ~ N(0, 0.02) (the
+[K, N] matrix, converted on the GPU into the projection's [N, K] storage
+with mla_transpose_bf16), gamma
 ~ U(0.8, 1.2), eps 1e-6, positions 0..4095, per-layer fp8 scales ~ U(0.5, 2),
 5 e4m3fn caches [512, 64, 576] of random bytes, per-layer distinct slots.
 
@@ -50,9 +52,13 @@ def test_context_kv_projection_epilogue_chain_full(mk):
     x, w_kn = d["x"], d["w_kn"]
     check_slots(d["slot_mapping"], d["caches"][0].shape[0] * d["block_size"])
 
-    # --- GPU: projection, then the epilogue reading its output through strides
+    # --- GPU: the weight as stated ([K, N]) into the projection's [N, K]
+    # storage, the projection, then the epilogue reading its output through
+    # strides
+    w_nk = torch.empty(L * 576, x.shape[1], dtype=torch.bfloat16, device=DEV)
+    mk.mla_transpose_bf16(w_kn.to(DEV), w_nk)
     y = torch.empty(T, L * 576, dtype=torch.bfloat16, device=DEV)
-    mk.mla_ctx_kv_proj(x.to(DEV), w_kn.t().contiguous().to(DEV), y)
+    mk.mla_ctx_kv_proj(x.to(DEV), w_nk, y)
     cs = torch.empty(T, 2 * 64, dtype=torch.float32, device=DEV)
     mk.mla_rope_cos_sin_cache(cs, T, 64, d["rope_base"])
     caches = [c.to(DEV) for c in d["caches"]]

@@ -102,3 +102,18 @@ def test_merge_just_below_2_31_rows(mk):
     assert np.allclose(lse[:, ts].cpu().numpy(), rl, rtol=1e-6, atol=1e-6)
     del acc, part, lse, plse
     torch.cuda.empty_cache()
+
+
+def test_stream_copy_is_a_byte_copy(mk):
+    """The measurement copy moves every byte (sizes with a partial last
+    workgroup, and one empty copy)."""
+    announce("stream copy")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(77)
+    for n in (16, 4096 + 48, (1 << 24) + 16 * 37):
+        src = torch.randint(0, 256, (n,), generator=g, device=DEV, dtype=torch.int32).to(torch.uint8)
+        dst = torch.zeros_like(src)
+        mk.mla_stream_copy(dst, src)
+        torch.cuda.synchronize()
+        assert torch.equal(dst, src), n
+    mk.mla_stream_copy(src[:0], dst[:0])

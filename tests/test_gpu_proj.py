@@ -131,3 +131,33 @@ def test_proj_then_epilogue_chain(mk):
     torch.cuda.synchronize()
     for a, b in zip(caches, caches2):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("rows,cols,pad", [(8, 8, 0), (72, 136, 8), (520, 64, 24), (64, 2880, 0)])
+def test_transpose_bf16_matches_oracle(mk, rows, cols, pad):
+    """mla_transpose_bf16 bit for bit against the oracle's transpose, with
+    padded source and destination rows and partial edge tiles."""
+    announce("transpose", rows, cols, pad)
+    g = torch.Generator().manual_seed(rows + cols + pad)
+    srcb = synth.random_bf16_bits((rows, cols + pad), g)
+    src = srcb.to(DEV)[:, :cols]
+    dstb = torch.zeros(cols, rows + pad, dtype=torch.bfloat16, device=DEV)
+    mk.mla_transpose_bf16(src, dstb[:, :rows])
+    torch.cuda.synchronize()
+    ref = oracle.transpose(u16(srcb)[:, :cols])
+    got = u16(dstb)
+    assert np.array_equal(got[:, :rows], ref)
+    assert not got[:, rows:].any()                 # padding untouched
+
+
+def test_transpose_of_the_context_weight(mk):
+    """The fused context-KV weight as the workload states it, [7168, 2880]
+    (the [K, N] matrix), into the [2880, 7168] storage the projection reads:
+    every element against the oracle."""
+    announce("transpose C3 weight")
+    d = synth.context_epilogue("cpu")
+    w = d["w_kn"]
+    out = torch.empty(w.shape[1], w.shape[0], dtype=torch.bfloat16, device=DEV)
+    mk.mla_transpose_bf16(w.to(DEV), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(u16(out), oracle.transpose(u16(w)))
