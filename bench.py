@@ -154,13 +154,14 @@ class LongContext:
         return (insert_bytes(L, self.T) + n * gather_bytes(self.chunk)
                 + n * pack_fp8_bytes(self.chunk, self.heads))
 
-    def step(self, time_pack=False):
+    def step(self, time_pack=False, max_blocks=0):
         """One pass over the workload, in order on the current stream: the
         grouped insert, then the chunk loop with the joint launch -- gather of
         chunk 0, then for every chunk c the pack of c together with the gather
         of c + 1 into the other workspace (the last chunk packs alone).  With
         time_pack, one joint launch per step (the chunk index rotating)
-        records its own start and end events."""
+        records its own start and end events.  max_blocks > 0 caps the
+        pack's grid (grid-stride loop)."""
         mk = self.mk
         mk.mla_kv_insert_grouped(self.kv_c, self.k_pe, self.ptrs, self.slots, 64, 64 * W, W,
                                  self.scales, "fp8")
@@ -180,24 +181,24 @@ class LongContext:
                 mk.mla_ctx_kv_pack_gather(kvb[..., :128], ws[:, 512:], self.key, self.ctx_cache,
                                           nxt, self.ws2[(c + 1) % 2], v=kvb[..., 128:],
                                           v_out=self.v8, mode=mk.MLA_PACK_KEY_V_FP8,
-                                          cache_scale=self.ctx_scale)
+                                          cache_scale=self.ctx_scale, max_blocks=max_blocks)
             else:
                 mk.mla_ctx_kv_pack(kvb[..., :128], ws[:, 512:], self.key, v=kvb[..., 128:],
-                                   v_out=self.v8, mode=mk.MLA_PACK_KEY_V_FP8)
+                                   v_out=self.v8, mode=mk.MLA_PACK_KEY_V_FP8,
+                                   max_blocks=max_blocks)
 
-    def step_separate(self, max_blocks=0):
+    def step_separate(self):
         """The same work with the gather and the pack of every chunk as launches
-        of their own (max_blocks > 0: both as grid-stride loops over a capped
-        grid)."""
+        of their own."""
         mk = self.mk
         mk.mla_kv_insert_grouped(self.kv_c, self.k_pe, self.ptrs, self.slots, 64, 64 * W, W,
                                  self.scales, "fp8")
         for c, kvb in enumerate(self.kvb):
             mk.mla_ctx_latent_gather(self.ctx_cache,
                                      self.src_slots[c * self.chunk:(c + 1) * self.chunk],
-                                     self.ws, self.ctx_scale, "fp8", max_blocks=max_blocks)
+                                     self.ws, self.ctx_scale, "fp8")
             mk.mla_ctx_kv_pack(kvb[..., :128], self.ws[:, 512:], self.key, v=kvb[..., 128:],
-                               v_out=self.v8, mode=mk.MLA_PACK_KEY_V_FP8, max_blocks=max_blocks)
+                               v_out=self.v8, mode=mk.MLA_PACK_KEY_V_FP8)
 
 
 def time_kernel(torch, fn, reps=50, warmup=5):
@@ -933,18 +934,19 @@ def main():
                    "bytes_per_step": nbytes, "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
         "roofline": roofline,
     }
-    # the same work with the gather and the pack as launches of their own, on
-    # the default full grid and as grid-stride loops over a capped grid (64
+    # the same work with the pack as a grid-stride loop over a capped grid (64
     # workgroups of 256 threads per compute unit: 16384 workgroups, 2.5 chunks
     # per thread, against 40960 for one chunk per thread; the fastest of the
-    # caps 16, 32 and 64 per compute unit, which the components report)
+    # caps 16, 32 and 64 per compute unit, which the components report), and
+    # with the gather and the pack of every chunk as launches of their own
     cap = 64 * torch.cuda.get_device_properties(dev).multi_processor_count
-    for name, mb in (("separate_launch_step", 0), ("capped_grid_step", cap)):
-        wl.step_separate(max_blocks=mb)
+    for name, mb, fn in (("capped_grid_step", cap, lambda: wl.step(max_blocks=cap)),
+                         ("separate_launch_step", 0, wl.step_separate)):
+        fn()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(args.steps):
-            wl.step_separate(max_blocks=mb)
+            fn()
         torch.cuda.synchronize()
         csecs = time.perf_counter() - t0
         result[name] = {

@@ -75,7 +75,7 @@ _SIGS = {
     "mla_ctx_kv_pack_gather": (_i32, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64,
                                       _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp,
                                       _vp, _i32, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i32,
-                                      _vp, _vp]),
+                                      _vp, _i64, _vp]),
     "mla_stream_copy": (_i32, [_vp, _vp, _i64, _vp]),
     "mla_transpose_bf16": (_i32, [_vp, _i64, _i64, _i64, _vp, _i64, _vp]),
     "mla_ctx_merge_chunk": (_i32, [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp,
@@ -545,14 +545,16 @@ def mla_ctx_kv_pack(k_nope, k_pe, key_out, v=None, v_out=None, mode=MLA_PACK_KEY
 
 def mla_ctx_kv_pack_gather(k_nope, k_pe, key_out, cache, src_slots, gather_out, v=None,
                            v_out=None, mode=MLA_PACK_KEY_BF16, k_scale=None, v_scale=None,
-                           cache_scale=None, kv_cache_dtype="fp8"):
-    """One launch: the pack of one chunk (arguments as mla_ctx_kv_pack) and
-    the latent gather of the next (as mla_ctx_latent_gather, into gather_out,
-    which must not overlap the pack's tensors)."""
+                           cache_scale=None, kv_cache_dtype="fp8", max_blocks=0):
+    """One launch: the pack of one chunk (arguments as mla_ctx_kv_pack;
+    max_blocks caps its part of the grid) and the latent gather of the next
+    (as mla_ctx_latent_gather, into gather_out, which must not overlap the
+    pack's tensors)."""
     pa = _pack_args(k_nope, k_pe, key_out, v, v_out, mode, k_scale, v_scale)
     ga = _gather_args(cache, src_slots, gather_out, cache_scale, kv_cache_dtype)
     _same_device(cache, k_nope, "cache", "k_nope")
-    _check(lib().mla_ctx_kv_pack_gather(*pa, *ga, _stream(k_nope)), "mla_ctx_kv_pack_gather")
+    _check(lib().mla_ctx_kv_pack_gather(*pa, *ga, int(max_blocks), _stream(k_nope)),
+           "mla_ctx_kv_pack_gather")
 
 
 # ------------------------------------------------------ new-token epilogue --

@@ -452,8 +452,9 @@ void launch_pack_fp8(const PackPlan& p, dim3 g, hipStream_t s) {
 }
 
 template <class Op>
-void launch_pack_gather(const PackPlan& p, const GatherPlan& q, hipStream_t s) {
-  const dim3 g(static_cast<uint32_t>(p.full_blocks + q.blocks)), b(256);
+void launch_pack_gather(const PackPlan& p, const GatherPlan& q, int64_t pack_blocks,
+                        hipStream_t s) {
+  const dim3 g(static_cast<uint32_t>(pack_blocks + q.blocks)), b(256);
   const uint32_t gb = static_cast<uint32_t>(q.blocks);
   switch (q.kind) {
     case kGatherCopy16:
@@ -551,14 +552,14 @@ extern "C" int32_t mla_ctx_kv_pack_gather(
     void* v_out, const void* cache, int32_t cache_dtype, const float* cache_scale,
     int64_t block_size, int64_t block_stride, int64_t entry_stride, const int64_t* src_slots,
     int64_t gather_tokens, int64_t width, int32_t out_dtype, void* gather_out,
-    mla_stream_t stream) {
+    int64_t max_blocks, mla_stream_t stream) {
   static const char* fn = "mla_ctx_kv_pack_gather";
   clear_error();
   PackPlan p;
   GatherPlan q;
   int32_t st = plan_pack(fn, k_nope, kn_tok_stride, kn_head_stride, k_pe, kpe_tok_stride, v,
                          v_tok_stride, v_head_stride, num_tokens, num_heads, nope, rope, vdim,
-                         mode, src_dtype, k_scale, v_scale, key_out, v_out, 0, &p);
+                         mode, src_dtype, k_scale, v_scale, key_out, v_out, max_blocks, &p);
   if (st != MLA_OK) return st;
   st = plan_gather(fn, cache, cache_dtype, cache_scale, block_size, block_stride, entry_stride,
                    src_slots, gather_tokens, width, out_dtype, gather_out, 0, &q);
@@ -586,23 +587,24 @@ extern "C" int32_t mla_ctx_kv_pack_gather(
       return fail(MLA_ERR_UNSUPPORTED,
                   "%s: the joint launch takes bf16 sources and a 16-bit k_pe; "
                   "call mla_ctx_kv_pack and mla_ctx_latent_gather", fn);
-    if (p.full_blocks + q.blocks > 0x7FFFFFFF)
-      return fail(MLA_ERR_UNSUPPORTED, "%s: too many chunks for one launch", fn);
   }
+  const int64_t pack_blocks = max_blocks > 0 ? std::min(p.full_blocks, max_blocks) : p.full_blocks;
+  if (pack_blocks + q.blocks > 0x7FFFFFFF)
+    return fail(MLA_ERR_UNSUPPORTED, "%s: too many chunks for one launch", fn);
   auto s = static_cast<hipStream_t>(stream);
   if (q.a.total == 0)
     return mla_ctx_kv_pack(k_nope, kn_tok_stride, kn_head_stride, k_pe, kpe_tok_stride, v,
                            v_tok_stride, v_head_stride, num_tokens, num_heads, nope, rope, vdim,
-                           mode, src_dtype, k_scale, v_scale, key_out, v_out, 0, stream);
+                           mode, src_dtype, k_scale, v_scale, key_out, v_out, max_blocks, stream);
   if (p.a.total == 0)
     return mla_ctx_latent_gather(cache, cache_dtype, cache_scale, block_size, block_stride,
                                  entry_stride, src_slots, gather_tokens, width, out_dtype,
                                  gather_out, 0, stream);
   if (!p.fp8)
-    launch_pack_gather<PackBf16>(p, q, s);
+    launch_pack_gather<PackBf16>(p, q, pack_blocks, s);
   else if (p.scaled)
-    launch_pack_gather<PackFp8<true, false, false>>(p, q, s);
+    launch_pack_gather<PackFp8<true, false, false>>(p, q, pack_blocks, s);
   else
-    launch_pack_gather<PackFp8<false, false, false>>(p, q, s);
+    launch_pack_gather<PackFp8<false, false, false>>(p, q, pack_blocks, s);
   return launch_status(fn);
 }

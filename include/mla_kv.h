@@ -335,10 +335,11 @@ int32_t mla_ctx_kv_pack(const void* k_nope, int64_t kn_tok_stride,
  * chunk c + 1 needs nothing from chunk c, so in a chunk loop
  *   gather(0); kv_b_proj(0); pack(0) + gather(1); kv_b_proj(1); pack(1) + gather(2); ...
  * is the same computation with one launch fewer per chunk).
- * The first 19 arguments are those of mla_ctx_kv_pack (without max_blocks:
- * the launch has one thread per output chunk), the next 11 those of
- * mla_ctx_latent_gather (without max_blocks).  Result: identical to
- *   mla_ctx_kv_pack(pack arguments, 0, stream);
+ * The first 19 arguments are those of mla_ctx_kv_pack, the next 11 those of
+ * mla_ctx_latent_gather; max_blocks caps the pack's part of the grid (0 =
+ * one thread per output chunk; the pack then loops grid-stride), the
+ * gather's part has one thread per chunk.  Result: identical to
+ *   mla_ctx_kv_pack(pack arguments, max_blocks, stream);
  *   mla_ctx_latent_gather(gather arguments, 0, stream);
  * Each part is validated as its own entry point validates it, before
  * anything is launched.  In addition gather_out must not overlap k_nope,
@@ -356,7 +357,7 @@ int32_t mla_ctx_kv_pack_gather(
     void* v_out, const void* cache, int32_t cache_dtype, const float* cache_scale,
     int64_t block_size, int64_t block_stride, int64_t entry_stride, const int64_t* src_slots,
     int64_t gather_tokens, int64_t width, int32_t out_dtype, void* gather_out,
-    mla_stream_t stream);
+    int64_t max_blocks, mla_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * mla_ctx_merge_chunk -- fold one context chunk's attention partial into the

@@ -196,7 +196,7 @@ def pack_gather_call(mk, pack=None, gather=None):
         a["kn"], a["kn_ts"], a["kn_hs"], a["kpe"], a["kpe_ts"], a["v"], a["v_ts"], a["v_hs"],
         a["T"], a["H"], a["nope"], a["rope"], a["vdim"], a["mode"], a["src"], a["ks"], a["vs"],
         a["key"], a["vo"], g["cache"], g["dt"], g["scale"], g["bs"], g["bstride"], g["estride"],
-        g["slots"], g["T"], g["width"], g["odt"], g["out"], None)
+        g["slots"], g["T"], g["width"], g["odt"], g["out"], a.get("maxb", 0), None)
 
 
 @pytest.mark.parametrize("pack,gather,status,msg", [
@@ -208,6 +208,7 @@ def pack_gather_call(mk, pack=None, gather=None):
     (None, dict(out=P16 + 512), 1, "overlaps"),                  # inside the kv_b_proj rows
     (dict(mode=2, kpe_ts=576), None, 2, "joint launch"),         # verbatim fp8 k_pe
     (dict(src=4), None, 2, "joint launch"),                       # fp16 sources
+    (dict(maxb=-1), None, 1, "negative"),
 ])
 def test_pack_gather_rejects_bad_arguments(mk, pack, gather, status, msg):
     assert pack_gather_call(mk, pack, gather) == status

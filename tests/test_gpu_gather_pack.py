@@ -187,8 +187,9 @@ def test_long_context_pack_16_chunks_full(mk):
     """131072 context tokens in a [4096, 64, 576] cache, 16 chunks of 8192.
     Per chunk, on the GPU: the gather, the fp8 pack on the default grid and on
     a capped grid of 16 workgroups per compute unit (a grid-stride loop of
-    several passes), and the chunk loop with the joint launch (pack of chunk
-    c + gather of chunk c + 1 into the other of two workspaces).  Every
+    about 10 passes), and the chunk loop with the joint launch (pack of chunk
+    c + gather of chunk c + 1 into the other of two workspaces), its pack
+    capped at 64 workgroups per compute unit.  Every
     workspace row and every key and V byte of every chunk, from each path,
     against the oracle's gather -> pack of the same cache."""
     announce("long-context pack 16 chunks, full")
@@ -202,7 +203,7 @@ def test_long_context_pack_16_chunks_full(mk):
     ws2 = [torch.empty(8192, 576, dtype=torch.bfloat16, device=DEV) for _ in range(2)]
     outs = {k: (torch.empty(8192, 64, 192, dtype=torch.uint8, device=DEV),
                 torch.empty(8192, 64, 128, dtype=torch.uint8, device=DEV))
-            for k in ("default grid", "capped grid", "joint launch")}
+            for k in ("default grid", "capped grid", "joint launch, capped pack")}
     sc = torch.tensor([0.5], device=DEV)
     chunk = lambda c: slots[c * 8192:(c + 1) * 8192]
     mk.mla_ctx_latent_gather(cache, chunk(0), ws2[0], sc, "fp8")
@@ -217,14 +218,15 @@ def test_long_context_pack_16_chunks_full(mk):
                            max_blocks=cap)
         torch.cuda.synchronize()
         joint_ws = u16(ws2[c % 2])            # gathered by the previous joint launch
-        k, vo = outs["joint launch"]
+        k, vo = outs["joint launch, capped pack"]
         if c < 15:
             mk.mla_ctx_kv_pack_gather(kn, ws2[c % 2][:, 512:], k, cache, chunk(c + 1),
                                       ws2[(c + 1) % 2], v=v, v_out=vo,
-                                      mode=mk.MLA_PACK_KEY_V_FP8, cache_scale=sc)
+                                      mode=mk.MLA_PACK_KEY_V_FP8, cache_scale=sc,
+                                      max_blocks=4 * cap)
         else:
             mk.mla_ctx_kv_pack(kn, ws2[c % 2][:, 512:], k, v=v, v_out=vo,
-                               mode=mk.MLA_PACK_KEY_V_FP8)
+                               mode=mk.MLA_PACK_KEY_V_FP8, max_blocks=4 * cap)
         torch.cuda.synchronize()
         sl = slots_np[c * 8192:(c + 1) * 8192]
         ref_ws = np.concatenate(run_sliced(lambda a, b: oracle.gather(cache_np, sl[a:b], 0.5),
