@@ -214,7 +214,7 @@ __global__ __launch_bounds__(256, 5) void epilogue_kernel(const EpiArgs a) {
       uint16_t* d = a.dbg + (int64_t(l) * a.tokens + t) * (kR + kP);
 #pragma unroll
       for (int q = 0; q < kChunks; ++q) st16(d + 8 * (j + kRowLanes * q), y[q]);
-      *reinterpret_cast<uint2*>(d + kR + kPe * j) = ype;
+      st8(d + kR + kPe * j, ype);
     }
     // ---- insert (slot -> block, offset; a negative slot skips the row)
     if (slot < 0) continue;
@@ -226,12 +226,12 @@ __global__ __launch_bounds__(256, 5) void epilogue_kernel(const EpiArgs a) {
 #pragma unroll
       for (int q = 0; q < kChunks; ++q)
         st8<kEpiStream>(dst + 8 * (j + kRowLanes * q), quant8<true, false, kE5M2>(y[q], sc, rc, flip));
-      *reinterpret_cast<uint32_t*>(dst + kR + kPe * j) = quant4<true, kE5M2>(ype, sc, rc, flip);
+      st4<kEpiStream>(dst + kR + kPe * j, quant4<true, kE5M2>(ype, sc, rc, flip));
     } else {
       uint16_t* dst = reinterpret_cast<uint16_t*>(cbase) + entry;
 #pragma unroll
       for (int q = 0; q < kChunks; ++q) st16<kEpiStream>(dst + 8 * (j + kRowLanes * q), y[q]);
-      *reinterpret_cast<uint2*>(dst + kR + kPe * j) = ype;
+      st8<kEpiStream>(dst + kR + kPe * j, ype);
     }
   }
 }

@@ -164,17 +164,17 @@ __global__ __launch_bounds__(256) void row_insert_kernel(const RowInsertArgs a) 
         st8<kInsertStream>(dst + 8 * (j + kLanes * q), quant8<true, false, kE5M2>(v[q], sc, rc, flip));
       const uint32_t c = quant4<true, kE5M2>(pe, sc, rc, flip);
       if constexpr (kPe == 4)
-        *reinterpret_cast<uint32_t*>(dst + kRowR + 4 * j) = c;
+        st4<kInsertStream>(dst + kRowR + 4 * j, c);
       else
-        *reinterpret_cast<uint16_t*>(dst + kRowR + 2 * j) = static_cast<uint16_t>(c);
+        st2(dst + kRowR + 2 * j, static_cast<uint16_t>(c));
     } else {
       uint16_t* dst = reinterpret_cast<uint16_t*>(cb) + entry;
 #pragma unroll
       for (int q = 0; q < kChunks; ++q) st16<kInsertStream>(dst + 8 * (j + kLanes * q), v[q]);
       if constexpr (kPe == 4)
-        *reinterpret_cast<uint2*>(dst + kRowR + 4 * j) = pe;
+        st8<kInsertStream>(dst + kRowR + 4 * j, pe);
       else
-        *reinterpret_cast<uint32_t*>(dst + kRowR + 2 * j) = pe.x;
+        st4<kInsertStream>(dst + kRowR + 2 * j, pe.x);
     }
   }
 }

@@ -382,24 +382,41 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// Every output of the library lives in device memory, so stores go through
+// the global address space.  A pointer the compiler cannot trace to a kernel
+// argument (a cache base read from a pointer table, an address built from
+// 64-bit integer offsets) would otherwise give flat stores, and while a flat
+// access is outstanding the compiler's wait for any earlier load becomes a
+// wait for every outstanding memory operation, the stores' included.
+template <class T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* global_ptr(void* p) {
+  return (__attribute__((address_space(1))) T*)(reinterpret_cast<uintptr_t>(p));
+}
+
 template <bool kStream = false>
 __device__ __forceinline__ void st16(void* p, uint4 v) {
-  if constexpr (kStream) {
-    u32x4 w = {v.x, v.y, v.z, v.w};
-    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
-  } else {
-    *reinterpret_cast<uint4*>(p) = v;
-  }
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  if constexpr (kStream)
+    __builtin_nontemporal_store(w, global_ptr<u32x4>(p));
+  else
+    *global_ptr<u32x4>(p) = w;
 }
 template <bool kStream = false>
 __device__ __forceinline__ void st8(void* p, uint2 v) {
-  if constexpr (kStream) {
-    u32x2 w = {v.x, v.y};
-    __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(p));
-  } else {
-    *reinterpret_cast<uint2*>(p) = v;
-  }
+  const u32x2 w = {v.x, v.y};
+  if constexpr (kStream)
+    __builtin_nontemporal_store(w, global_ptr<u32x2>(p));
+  else
+    *global_ptr<u32x2>(p) = w;
 }
+template <bool kStream = false>
+__device__ __forceinline__ void st4(void* p, uint32_t v) {
+  if constexpr (kStream)
+    __builtin_nontemporal_store(v, global_ptr<uint32_t>(p));
+  else
+    *global_ptr<uint32_t>(p) = v;
+}
+__device__ __forceinline__ void st2(void* p, uint16_t v) { *global_ptr<uint16_t>(p) = v; }
 
 // Store policy per kernel (measured on MI355X): the pack and gather write
 // large contiguous outputs that the next kernel of a chunk loop does not

@@ -101,14 +101,6 @@ __device__ __forceinline__ uint4 ld16_once(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-template <bool kStream>
-__device__ __forceinline__ void st4(void* p, uint32_t v) {
-  if constexpr (kStream)
-    __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
-  else
-    *reinterpret_cast<uint32_t*>(p) = v;
-}
-
 // Lane j's rope values [4j, 4j + 4) (two bf16 words) rotated with the table
 // words cv / sv of angles 4 (j mod 8) .. (tab: the lane's cos hi entries):
 //   first half (j < 8)  y_i = x_i cos_i - x_{i+32} sin_i,
