@@ -24,7 +24,10 @@
 // with one DPP row rotation, and the token's position indexes the cos/sin
 // table directly instead of a repeated-positions buffer.  The rotation is
 // rounded correctly to bf16 even where its two products nearly cancel
-// (rope4: an fp32 fast path with an exact float64 fallback).
+// (rope4: an fp32 fast path with an exact float64 fallback).  For up to 8
+// layers the layers' RMSNorm weights are read into LDS once per workgroup
+// (epilogue_lds_kernel); otherwise each row group reads its layer's weights
+// from global memory (epilogue_kernel).
 #include "mla_common.hpp"
 
 namespace mla {
@@ -116,16 +119,94 @@ __device__ __forceinline__ int64_t entry_offset(int64_t s, const EpiArgs& a) {
   return blk * a.block_stride + (s - blk * a.block_size) * a.entry_stride;
 }
 
+// The part of a row after its loads: RoPE, RMSNorm, bf16 rounding, the
+// optional debug copy of the row, fp8 (or bf16) conversion and the cache
+// store.  gamma_chunk(q) yields the layer's weight chunk q of this lane.
+template <int kFmt, class GammaChunk>
+__device__ __forceinline__ void finish_row(const EpiArgs& a, const uint4* xv,
+                                           GammaChunk gamma_chunk, uint2 pe, uint4 cv, uint4 sv,
+                                           uint4 clv, uint4 slv, int64_t slot, int64_t cbase,
+                                           float sc, uint32_t l, uint32_t t, bool active, int j) {
+  constexpr bool kFp8 = kFmt != kFmtBf16, kE5M2 = kFmt == kFmtE5M2;
+  const bool first_half = j < kRowLanes / 2;  // holds k_pe[i], i < 32
+  // ---- RoPE first (its table words and partner values are dead before the
+  // normed row is built): y_i = x_i cos - x_{i+32} sin, y_{i+32} = x_{i+32} cos + x_i sin
+  const float xp[kPe] = {bf16_lo(pe.x), bf16_hi(pe.x), bf16_lo(pe.y), bf16_hi(pe.y)};
+  const float cc[kPe] = {__uint_as_float(cv.x), __uint_as_float(cv.y), __uint_as_float(cv.z),
+                         __uint_as_float(cv.w)};
+  const float sn[kPe] = {__uint_as_float(sv.x), __uint_as_float(sv.y), __uint_as_float(sv.z),
+                         __uint_as_float(sv.w)};
+  float xq[kPe];
+#pragma unroll
+  for (int e = 0; e < kPe; ++e) xq[e] = dpp_f<kDppRor8>(xp[e]);
+  const uint2 ype = rope4v(xp, xq, cc, sn, first_half, clv, slv);
+
+  // ---- RMSNorm: fp32 sum of squares over the row's 16 lanes, two squares
+  // per bf16 word (v_dot2c_f32_bf16: the squares of bf16 values are exact in
+  // fp32), four partial sums per lane.
+  float ss4[kChunks];
+#pragma unroll
+  for (int q = 0; q < kChunks; ++q) {
+    ss4[q] = 0.0f;
+    const uint32_t w[4] = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16x2_t b = __builtin_bit_cast(bf16x2_t, w[i]);
+      ss4[q] = __builtin_amdgcn_fdot2_f32_bf16(b, b, ss4[q], false);
+    }
+  }
+  float ss = (ss4[0] + ss4[1]) + (ss4[2] + ss4[3]);
+  ss = row_sum(ss);
+  const float rinv = 1.0f / __builtin_sqrtf(ss * (1.0f / kR) + a.eps);
+  uint4 y[kChunks];
+#pragma unroll
+  for (int q = 0; q < kChunks; ++q) {
+    const uint32_t w[4] = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
+    const uint4 g = gamma_chunk(q);
+    const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
+    uint32_t yw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      yw[i] = cvt_bf16x2(bf16_lo(w[i]) * rinv * bf16_lo(gw[i]),
+                         bf16_hi(w[i]) * rinv * bf16_hi(gw[i]));
+    y[q] = make_uint4(yw[0], yw[1], yw[2], yw[3]);
+  }
+
+  if (!active) return;
+  if (a.dbg) {
+    uint16_t* d = a.dbg + (int64_t(l) * a.tokens + t) * (kR + kP);
+#pragma unroll
+    for (int q = 0; q < kChunks; ++q) st16(d + 8 * (j + kRowLanes * q), y[q]);
+    st8(d + kR + kPe * j, ype);
+  }
+  // ---- insert (slot -> block, offset; a negative slot skips the row)
+  if (slot < 0) return;
+  const int64_t entry = entry_offset(slot, a);
+  if constexpr (kFp8) {
+    const float rc = 1.0f / sc;
+    const uint32_t flip = sign_flip_of(sc);
+    uint8_t* dst = reinterpret_cast<uint8_t*>(cbase) + entry;
+#pragma unroll
+    for (int q = 0; q < kChunks; ++q)
+      st8<kEpiStream>(dst + 8 * (j + kRowLanes * q), quant8<true, false, kE5M2>(y[q], sc, rc, flip));
+    st4<kEpiStream>(dst + kR + kPe * j, quant4<true, kE5M2>(ype, sc, rc, flip));
+  } else {
+    uint16_t* dst = reinterpret_cast<uint16_t*>(cbase) + entry;
+#pragma unroll
+    for (int q = 0; q < kChunks; ++q) st16<kEpiStream>(dst + 8 * (j + kRowLanes * q), y[q]);
+    st8<kEpiStream>(dst + kR + kPe * j, ype);
+  }
+}
+
 // Rows are numbered token-major (row = t * L + l), the order of the
 // projection output, so the 4 rows of a wavefront are adjacent in memory.
+// One row per 16-lane group per pass; the general form (any layer count).
 template <int kFmt>
 __global__ __launch_bounds__(256, 5) void epilogue_kernel(const EpiArgs a) {
-  constexpr bool kFp8 = kFmt != kFmtBf16, kE5M2 = kFmt == kFmtE5M2;
   const int lane = threadIdx.x & 63;
   const int j = lane & (kRowLanes - 1);       // lane within the row
   const int grp = lane / kRowLanes;           // row within the wavefront
   const uint32_t wave = threadIdx.x >> 6;
-  const bool first_half = j < kRowLanes / 2;  // holds k_pe[i], i < 32
   for (uint32_t r0 = (blockIdx.x * kWavesPerBlock + wave) * kRowsPerWave; r0 < a.rows;
        r0 += gridDim.x * kRowsPerBlock) {
     const uint32_t r = r0 + grp;
@@ -153,7 +234,7 @@ __global__ __launch_bounds__(256, 5) void epilogue_kernel(const EpiArgs a) {
     const int64_t slot = a.slots[int64_t(l) * a.sls + t];
     const int64_t cbase = a.cache_ptrs[l];
     float sc = 1.0f;
-    if constexpr (kFp8) sc = a.scales[l];
+    if constexpr (kFmt != kFmtBf16) sc = a.scales[l];
     __builtin_amdgcn_sched_barrier(0);
     const int64_t pos = min(max(pos_in, int64_t(0)), a.max_pos - 1);
     const float* cs = a.cos_sin + pos * (2 * kP) + kPe * (j & 7);
@@ -165,75 +246,74 @@ __global__ __launch_bounds__(256, 5) void epilogue_kernel(const EpiArgs a) {
     // fence the compiler sinks the loads used only by the stores into the
     // store branch, after the reduction, adding memory round trips.
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-
-    // ---- RoPE first (its table words and partner values are dead before the
-    // normed row is built): y_i = x_i cos - x_{i+32} sin, y_{i+32} = x_{i+32} cos + x_i sin
-    const float xp[kPe] = {bf16_lo(pe.x), bf16_hi(pe.x), bf16_lo(pe.y), bf16_hi(pe.y)};
-    const float cc[kPe] = {__uint_as_float(cv.x), __uint_as_float(cv.y), __uint_as_float(cv.z),
-                           __uint_as_float(cv.w)};
-    const float sn[kPe] = {__uint_as_float(sv.x), __uint_as_float(sv.y), __uint_as_float(sv.z),
-                           __uint_as_float(sv.w)};
-    float xq[kPe];
-#pragma unroll
-    for (int e = 0; e < kPe; ++e) xq[e] = dpp_f<kDppRor8>(xp[e]);
-    const uint2 ype = rope4v(xp, xq, cc, sn, first_half, clv, slv);
-
-    // ---- RMSNorm: fp32 sum of squares over the row's 16 lanes.  The fp32
-    // values are taken from the bf16 words twice (a shift or a mask each)
-    // instead of being kept: 32 fewer live registers, so more wavefronts fit.
-    float ss = 0.0f;
-#pragma unroll
-    for (int q = 0; q < kChunks; ++q) {
-      const uint32_t w[4] = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ss = __builtin_fmaf(bf16_lo(w[i]), bf16_lo(w[i]), ss);
-        ss = __builtin_fmaf(bf16_hi(w[i]), bf16_hi(w[i]), ss);
-      }
-    }
-    ss = row_sum(ss);
-    const float rinv = 1.0f / __builtin_sqrtf(ss * (1.0f / kR) + a.eps);
-    uint4 y[kChunks];
-#pragma unroll
-    for (int q = 0; q < kChunks; ++q) {
-      // an empty asm that "changes" the words, so the conversions above are
-      // not kept alive across the reduction for reuse here
-      uint32_t w[4] = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
-      asm volatile("" : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]));
-      const uint32_t gw[4] = {gv[q].x, gv[q].y, gv[q].z, gv[q].w};
-      uint32_t yw[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        yw[i] = cvt_bf16x2(bf16_lo(w[i]) * rinv * bf16_lo(gw[i]),
-                           bf16_hi(w[i]) * rinv * bf16_hi(gw[i]));
-      y[q] = make_uint4(yw[0], yw[1], yw[2], yw[3]);
-    }
-
-    if (!active) continue;
-    if (a.dbg) {
-      uint16_t* d = a.dbg + (int64_t(l) * a.tokens + t) * (kR + kP);
-#pragma unroll
-      for (int q = 0; q < kChunks; ++q) st16(d + 8 * (j + kRowLanes * q), y[q]);
-      st8(d + kR + kPe * j, ype);
-    }
-    // ---- insert (slot -> block, offset; a negative slot skips the row)
-    if (slot < 0) continue;
-    const int64_t entry = entry_offset(slot, a);
-    if constexpr (kFp8) {
-      const float rc = 1.0f / sc;
-      const uint32_t flip = sign_flip_of(sc);
-      uint8_t* dst = reinterpret_cast<uint8_t*>(cbase) + entry;
-#pragma unroll
-      for (int q = 0; q < kChunks; ++q)
-        st8<kEpiStream>(dst + 8 * (j + kRowLanes * q), quant8<true, false, kE5M2>(y[q], sc, rc, flip));
-      st4<kEpiStream>(dst + kR + kPe * j, quant4<true, kE5M2>(ype, sc, rc, flip));
-    } else {
-      uint16_t* dst = reinterpret_cast<uint16_t*>(cbase) + entry;
-#pragma unroll
-      for (int q = 0; q < kChunks; ++q) st16<kEpiStream>(dst + 8 * (j + kRowLanes * q), y[q]);
-      st8<kEpiStream>(dst + kR + kPe * j, ype);
-    }
+    finish_row<kFmt>(a, xv, [&](int q) { return gv[q]; }, pe, cv, sv, clv, slv, slot, cbase, sc,
+                     l, t, active, j);
   }
+}
+
+// Form for up to kMaxLdsLayers layers: the layers' RMSNorm weights are
+// copied into LDS once per workgroup, and each wavefront finishes one group
+// of 4 rows.  The weight loads are issued first and the row loads right
+// after them; the LDS copy and the barrier (which waits for the LDS writes
+// only) come after all of the row's loads are in flight.
+constexpr int kMaxLdsLayers = 8;
+constexpr int kGammaChunks = kR / 8;                     // 16-byte chunks per layer
+constexpr int kGammaIters = kMaxLdsLayers * kGammaChunks / 256;
+
+template <int kFmt>
+__global__ __launch_bounds__(256) void epilogue_lds_kernel(const EpiArgs a) {
+  __shared__ uint4 glds[kMaxLdsLayers * kGammaChunks];
+  const int lane = threadIdx.x & 63;
+  const int j = lane & (kRowLanes - 1);
+  const int grp = lane / kRowLanes;
+  const uint32_t wave = threadIdx.x >> 6;
+  const uint32_t r = (blockIdx.x * kWavesPerBlock + wave) * kRowsPerWave + grp;
+
+  const uint32_t gchunks = a.layers * kGammaChunks;
+  uint4 gt[kGammaIters];
+#pragma unroll
+  for (int i = 0; i < kGammaIters; ++i) {
+    const uint32_t c = threadIdx.x + 256u * i;
+    gt[i] = ld16(a.gamma + 8 * (c < gchunks ? c : 0u));
+  }
+  const bool active = r < a.rows;
+  const uint32_t rr = active ? r : a.rows - 1;  // idle lanes still load in bounds
+  const uint32_t t = fdiv(rr, a.nlayers);
+  const uint32_t l = rr - t * a.layers;
+  // the position first, so that the table read waits only for it
+  const int64_t pos_in = a.positions[t];
+  __builtin_amdgcn_sched_barrier(0);
+  const uint16_t* row = a.all_kv + int64_t(t) * a.kts + int64_t(l) * a.kls;
+  uint4 xv[kChunks];
+#pragma unroll
+  for (int q = 0; q < kChunks; ++q) xv[q] = ld16(row + 8 * (j + kRowLanes * q));
+  const uint2 pe = *reinterpret_cast<const uint2*>(row + kR + kPe * j);
+  const int64_t slot = a.slots[int64_t(l) * a.sls + t];
+  const int64_t cbase = a.cache_ptrs[l];
+  const float sc = kFmt != kFmtBf16 ? a.scales[l] : 1.0f;
+  __builtin_amdgcn_sched_barrier(0);
+  // positions outside [0, max_pos) break the precondition; clamp so the
+  // table read stays inside the table
+  const int64_t pos = min(max(pos_in, int64_t(0)), a.max_pos - 1);
+  const float* cs = a.cos_sin + pos * (2 * kP) + kPe * (j & 7);
+  const uint4 cv = ld16(cs);
+  const uint4 sv = ld16(cs + kP / 2);
+  const uint4 clv = ld16(cs + kP);
+  const uint4 slv = ld16(cs + kP + kP / 2);
+  // no load may sink below this point (into the store branches)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+  for (int i = 0; i < kGammaIters; ++i) {
+    const uint32_t c = threadIdx.x + 256u * i;
+    if (c < gchunks) glds[c] = gt[i];
+  }
+  // a barrier that waits for the LDS writes only, not for the row loads
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  const uint4* g = glds + l * kGammaChunks + j;
+  finish_row<kFmt>(a, xv, [&](int q) { return g[kRowLanes * q]; }, pe, cv, sv, clv, slv, slot,
+                   cbase, sc, l, t, active, j);
 }
 
 }  // namespace
@@ -307,9 +387,19 @@ extern "C" int32_t mla_ctx_kv_epilogue(
   a.layers = static_cast<uint32_t>(num_layers);
   a.tokens = static_cast<uint32_t>(num_tokens);
   a.rows = static_cast<uint32_t>(rows);
-  const int64_t blocks = std::min<int64_t>(ceil_div(rows, kRowsPerBlock), default_grid_cap());
   auto s = static_cast<hipStream_t>(stream);
   const int fmt = cache_fmt(kv_cache_dtype);
+  if (num_layers <= kMaxLdsLayers) {
+    const int64_t blocks = ceil_div(rows, kRowsPerBlock);  // one group of 4 rows per wavefront
+    if (fmt == kFmtE5M2)
+      launch(epilogue_lds_kernel<kFmtE5M2>, dim3(blocks), dim3(256), 0, s, a);
+    else if (fmt == kFmtE4M3)
+      launch(epilogue_lds_kernel<kFmtE4M3>, dim3(blocks), dim3(256), 0, s, a);
+    else
+      launch(epilogue_lds_kernel<kFmtBf16>, dim3(blocks), dim3(256), 0, s, a);
+    return launch_status(fn);
+  }
+  const int64_t blocks = std::min<int64_t>(ceil_div(rows, kRowsPerBlock), default_grid_cap());
   if (fmt == kFmtE5M2)
     launch(epilogue_kernel<kFmtE5M2>, dim3(blocks), dim3(256), 0, s, a);
   else if (fmt == kFmtE4M3)

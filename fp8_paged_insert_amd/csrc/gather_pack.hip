@@ -260,23 +260,27 @@ __global__ __launch_bounds__(256) void pack_kernel(const PackArgs a) {
 }
 
 // -------------------------------------------------- pack c + gather c + 1 --
-// The first gather_blocks workgroups gather, the rest pack; the two sets of
-// chunks are independent (the gather writes a workspace the pack does not
-// touch), so the gather's short, latency-bound reads run under the pack's
-// stream instead of in a launch of their own.
+// Workgroups [gather_first, gather_first + gather_blocks) gather, the rest
+// pack; the two sets of chunks are independent (the gather writes a
+// workspace the pack does not touch), so the gather's short, latency-bound
+// reads run under the pack's stream instead of in a launch of their own.
+// gather_first is 0 (the gather's workgroups start first) or the number of
+// pack workgroups (they start last).
 template <class Op, int kKind>
 __global__ __launch_bounds__(256) void pack_gather_kernel(const PackArgs a, const GatherArgs g,
+                                                          uint32_t gather_first,
                                                           uint32_t gather_blocks) {
-  if (blockIdx.x < gather_blocks) {
+  const uint32_t gb = blockIdx.x - gather_first;  // wraps above gather_blocks when below
+  if (gb < gather_blocks) {
     const float sc = gather_scale<kKind>(g);
-    for (uint32_t item = blockIdx.x * blockDim.x + threadIdx.x; item < g.total;
+    for (uint32_t item = gb * blockDim.x + threadIdx.x; item < g.total;
          item += gather_blocks * blockDim.x)
       gather_item<kKind>(g, item, sc);
     return;
   }
   const Op op(a);
-  pack_loop(a, op, (blockIdx.x - gather_blocks) * blockDim.x + threadIdx.x,
-            (gridDim.x - gather_blocks) * blockDim.x);
+  const uint32_t pb = blockIdx.x < gather_first ? blockIdx.x : blockIdx.x - gather_blocks;
+  pack_loop(a, op, pb * blockDim.x + threadIdx.x, (gridDim.x - gather_blocks) * blockDim.x);
 }
 
 // ------------------------------------------------------- host validation --
@@ -456,18 +460,24 @@ void launch_pack_gather(const PackPlan& p, const GatherPlan& q, int64_t pack_blo
                         hipStream_t s) {
   const dim3 g(static_cast<uint32_t>(pack_blocks + q.blocks)), b(256);
   const uint32_t gb = static_cast<uint32_t>(q.blocks);
+  // Where the gather's workgroups go (measured on MI355X, 8192-token chunks
+  // of 64 heads): first on the full pack grid (one chunk per thread), where
+  // their latency-bound reads then overlap the whole pack; last on a capped
+  // grid, whose workgroups loop over several chunks and would otherwise
+  // start behind them.
+  const uint32_t first = pack_blocks < p.full_blocks ? static_cast<uint32_t>(pack_blocks) : 0u;
   switch (q.kind) {
     case kGatherCopy16:
-      launch(pack_gather_kernel<Op, kGatherCopy16>, g, b, 0, s, p.a, q.a, gb);
+      launch(pack_gather_kernel<Op, kGatherCopy16>, g, b, 0, s, p.a, q.a, first, gb);
       break;
     case kGatherDequant:
-      launch(pack_gather_kernel<Op, kGatherDequant>, g, b, 0, s, p.a, q.a, gb);
+      launch(pack_gather_kernel<Op, kGatherDequant>, g, b, 0, s, p.a, q.a, first, gb);
       break;
     case kGatherRaw8:
-      launch(pack_gather_kernel<Op, kGatherRaw8>, g, b, 0, s, p.a, q.a, gb);
+      launch(pack_gather_kernel<Op, kGatherRaw8>, g, b, 0, s, p.a, q.a, first, gb);
       break;
     default:
-      launch(pack_gather_kernel<Op, kGatherDequantE5M2>, g, b, 0, s, p.a, q.a, gb);
+      launch(pack_gather_kernel<Op, kGatherDequantE5M2>, g, b, 0, s, p.a, q.a, first, gb);
       break;
   }
 }

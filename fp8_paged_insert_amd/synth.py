@@ -144,9 +144,9 @@ def grouped_test_shape(device="cpu", seed=42, shared=False, fp8=True):
 
 
 def context_epilogue(device="cpu", seed=3, num_tokens=4096, hidden=7168,
-                     num_blocks=512, with_gemm=True, fp8=True):
+                     num_blocks=512, with_gemm=True, fp8=True, num_layers=NUM_LAYERS):
     g = gen(seed, device)
-    L, T = NUM_LAYERS, num_tokens
+    L, T = num_layers, num_tokens
     N = L * KV_WIDTH
     d = {}
     if with_gemm:

@@ -141,6 +141,19 @@ def test_epilogue_context_shape(mk, dtype):
     check(d, caches, rows, dtype)
 
 
+@pytest.mark.parametrize("L,T", [(1, 37), (8, 300), (9, 200), (5, 1000), (3, 4100),
+                                 (7, 2341), (6, 4000)])
+def test_epilogue_layer_counts_and_row_counts(mk, L, T):
+    """Layer counts 1 to 8 (the kernel that keeps the layers' weights in
+    LDS) and 9 (the kernel that reads them from global memory), with row
+    counts that leave ragged last workgroups."""
+    announce("epilogue layers/rows", L, T)
+    d = synth.context_epilogue(num_tokens=T, num_blocks=max(8, (T + 63) // 64), with_gemm=False,
+                               seed=100 + L, num_layers=L)
+    caches, rows = run_epilogue(mk, d, "fp8")
+    check(d, caches, rows, "fp8")
+
+
 def test_epilogue_shared_slots_negative_and_random_positions(mk):
     announce("epilogue shared/-1/positions")
     d = synth.context_epilogue(num_tokens=300, num_blocks=8, with_gemm=False, seed=31)
