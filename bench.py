@@ -405,7 +405,8 @@ def copy_ceiling(torch, mk, dev, flush):
     compared with: the runtime's copy (torch copy_, 1 GiB) and the library's
     streaming copy (the launch shape of its streaming kernels) at 1 GiB and
     at the total size of the context epilogue (36.6 MB moved) and of one
-    gather (14.2 MB moved); each timed by its own launch events after a
+    gather (14.2 MB moved), and a streaming kernel with the fp8 pack's
+    read:write mix (2:1) at the pack's size (437 MB moved); each timed by its own launch events after a
     cache flush (the runtime's copy with stream events), median of 20."""
     out = {}
     n = 1 << 30
@@ -433,6 +434,12 @@ def copy_ceiling(torch, mk, dev, flush):
         us, p90 = kernel_us(torch, mk, lambda: mk.mla_stream_copy(dst[:half], src[:half]), flush,
                             reps=20, warm=3)
         out[name] = rate(us, p90, 2 * half)
+    # the fp8 pack's read:write mix (two bytes read per byte written) at the
+    # pack's size: the ceiling for the pack and the joint launch
+    third = (pack_fp8_bytes(8192, 64) // 3) // 16 * 16
+    us, p90 = kernel_us(torch, mk, lambda: mk.mla_stream_mix(dst[:third], src[:2 * third], 2),
+                        flush, reps=20, warm=3)
+    out["stream_mix_2to1_pack_size"] = rate(us, p90, 3 * third)
     del src, dst
     return out
 
@@ -699,7 +706,31 @@ def projection_component(torch, mk, dev, flush):
             if i >= 3:
                 acc.append(e0.elapsed_time(e1) * 1e3)
     flops = 2 * 4096 * 7168 * L * W
+    # the matrix cores' own ceiling on this machine: the issue interval of
+    # v_mfma_f32_32x32x16_bf16 and the clock held under full MFMA load, read
+    # by the library's rate probe (one workgroup of 4 wavefronts per CU)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    clocks = torch.zeros(16 * cus, dtype=torch.int64, device=dev)
+    iters = 4096
+    mk.mla_mfma_rate(clocks, iters)  # warm-up
+    mk.mla_mfma_rate(clocks, iters)
+    torch.cuda.synchronize()
+    c = clocks.view(-1, 4).cpu()
+    cyc = (c[:, 1] - c[:, 0]).double()
+    per_mfma = float(cyc.mean()) / (iters * 12)
+    ghz = float(cyc.sum() / (c[:, 3] - c[:, 2]).double().sum()) * 0.1
+    mfma_flops = 2 * 32 * 32 * 16
+    # per wavefront of the projection: 4 x 3 tiles of 32 x 32, K / 16 steps
+    proj_mfmas = 12 * 7168 // 16
+    ceiling = {"cycles_per_mfma_32x32x16_bf16": round(per_mfma, 2),
+               "sustained_clock_ghz": round(ghz, 3),
+               "tflops_at_sustained_clock": round(4 * cus * mfma_flops / per_mfma * ghz / 1e3, 1),
+               "tflops_at_2_4_ghz": round(4 * cus * mfma_flops / per_mfma * 2.4 / 1e3, 1),
+               "projection_mfma_bound_us": round(proj_mfmas * per_mfma / ghz / 1e3, 2),
+               "note": "the projection's MFMAs alone at this issue interval and clock "
+                       "(240 tiles, one per CU, 4 wavefronts each)"}
     return {"workload": "context_kv_proj 4096x7168 . 7168x2880 (bf16 MFMA, fp32 acc)",
+            "mfma_ceiling": ceiling,
             "us": round(us, 2), "p90_us": round(p90, 2), "TFLOPs": round(flops / us / 1e6, 1),
             "frac_of_peak": round(flops / us / 1e6 / 2500.0, 4),
             "torch_matmul_us_stream_events": round(statistics.median(ref), 2),

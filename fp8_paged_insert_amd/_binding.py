@@ -43,7 +43,7 @@ EXPORTS = (
     "mla_kv_insert_grouped", "mla_rope_cos_sin_cache", "mla_ctx_kv_epilogue",
     "mla_ctx_kv_proj", "mla_ctx_latent_gather", "mla_ctx_kv_pack", "mla_ctx_kv_pack_gather",
     "mla_ctx_merge_chunk", "mla_ctx_neutralize_partials", "mla_new_token_epilogue",
-    "mla_stream_copy", "mla_transpose_bf16",
+    "mla_stream_copy", "mla_stream_mix", "mla_transpose_bf16", "mla_mfma_rate",
 )
 
 
@@ -77,6 +77,8 @@ _SIGS = {
                                       _vp, _i32, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i32,
                                       _vp, _i64, _vp]),
     "mla_stream_copy": (_i32, [_vp, _vp, _i64, _vp]),
+    "mla_mfma_rate": (_i32, [_i64, _vp, _i64, _vp]),
+    "mla_stream_mix": (_i32, [_vp, _vp, _i64, _i32, _vp]),
     "mla_transpose_bf16": (_i32, [_vp, _i64, _i64, _i64, _vp, _i64, _vp]),
     "mla_ctx_merge_chunk": (_i32, [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp,
                                    _i64, _i64, _i64, _i64, _i64, _i32, _vp]),
@@ -710,3 +712,29 @@ def mla_stream_copy(dst, src):
         raise RuntimeError("dst and src must have the same size in bytes")
     _same_device(dst, src, "dst", "src")
     _check(lib().mla_stream_copy(_ptr(dst), _ptr(src), nbytes, _stream(src)), "mla_stream_copy")
+
+
+def mla_stream_mix(dst, src, reads_per_write):
+    """dst chunk i <- XOR of src chunks r i .. r i + r - 1 (16-byte chunks,
+    r = reads_per_write; src holds r times dst's bytes), with the library's
+    streaming launch shape: a measurement aid."""
+    if not (dst.is_contiguous() and src.is_contiguous()):
+        raise RuntimeError("dst and src must be contiguous")
+    nbytes = dst.numel() * dst.element_size()
+    if src.numel() * src.element_size() != nbytes * reads_per_write:
+        raise RuntimeError("src must hold reads_per_write times the bytes of dst")
+    _same_device(dst, src, "dst", "src")
+    _check(lib().mla_stream_mix(_ptr(dst), _ptr(src), nbytes, int(reads_per_write),
+                                _stream(src)), "mla_stream_mix")
+
+
+def mla_mfma_rate(clocks, iters):
+    """Runs the library's MFMA issue-rate kernel (one workgroup of 4
+    wavefronts per CU, iters x 12 v_mfma_f32_32x32x16_bf16 per wavefront)
+    and leaves in clocks (int64 device tensor, 16 words per CU) each
+    wavefront's shader-clock and 100 MHz real-time readings at start and end:
+    a measurement aid."""
+    if clocks.dtype != torch.int64 or not clocks.is_contiguous() or not clocks.is_cuda:
+        raise RuntimeError("clocks must be a contiguous int64 device tensor")
+    _check(lib().mla_mfma_rate(int(iters), _ptr(clocks), clocks.numel(), _stream(clocks)),
+           "mla_mfma_rate")

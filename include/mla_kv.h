@@ -461,6 +461,34 @@ int32_t mla_new_token_epilogue(
  * ------------------------------------------------------------------------ */
 int32_t mla_stream_copy(void* dst, const void* src, int64_t bytes, mla_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * mla_stream_mix -- measurement aid, not a step of the path: the launch
+ * shape of mla_stream_copy with reads_per_write (1 to 4) 16-byte loads per
+ * 16-byte store: output chunk i is the XOR of input chunks
+ * reads_per_write * i ... reads_per_write * i + reads_per_write - 1.  dst
+ * holds dst_bytes, src reads_per_write * dst_bytes (device, 16-byte aligned,
+ * sizes multiples of 16, no overlap).  With reads_per_write = 2 it has the
+ * fp8 pack's read:write mix, and its rate at the pack's size is the ceiling
+ * the pack is compared with.  reads_per_write = 1 is mla_stream_copy.
+ * ------------------------------------------------------------------------ */
+int32_t mla_stream_mix(void* dst, const void* src, int64_t dst_bytes, int32_t reads_per_write,
+                       mla_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * mla_mfma_rate -- measurement aid, not a step of the path: one workgroup of
+ * 4 wavefronts on every compute unit, each wavefront issuing iters x 12
+ * independent v_mfma_f32_32x32x16_bf16 (16384 multiply-adds each) between
+ * two reads of the shader clock and of the 100 MHz real-time counter.
+ * Wavefront w of workgroup g writes clocks[(4 g + w) * 4 + 0..3] = shader
+ * clock at start, at end, real-time counter at start, at end (device memory,
+ * at least 16 words per compute unit: clock_words >= 16 x CU count).  From
+ * them: cycles per MFMA issue per SIMD and the clock held under full MFMA
+ * load, hence the bf16 matrix peak the projection is compared with
+ * (MLA_ERR_INVALID_ARGUMENT for iters outside [1, 2^20], a NULL or short
+ * clocks array).
+ * ------------------------------------------------------------------------ */
+int32_t mla_mfma_rate(int64_t iters, uint64_t* clocks, int64_t clock_words, mla_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

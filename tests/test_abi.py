@@ -229,6 +229,28 @@ def test_stream_copy_rejects(mk):
     assert "overlap" in mk.last_error()
 
 
+def test_stream_mix_rejects(mk):
+    lib = mk.lib()
+    far = P16 + (1 << 32)
+    assert lib.mla_stream_mix(P16, far, 64, 0, None) == mk.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_stream_mix(P16, far, 64, 5, None) == mk.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_stream_mix(P16, far, 0, 2, None) == mk.MLA_OK
+    assert lib.mla_stream_mix(P_ODD, far, 64, 2, None) == mk.MLA_ERR_MISALIGNED
+    assert lib.mla_stream_mix(P16, far, 40, 2, None) == mk.MLA_ERR_MISALIGNED
+    # src spans 2 x 64 bytes from P16 - 96: it reaches into dst
+    assert lib.mla_stream_mix(P16, P16 - 96, 64, 2, None) == mk.MLA_ERR_INVALID_ARGUMENT
+    assert "overlap" in mk.last_error()
+
+
+def test_mfma_rate_rejects(mk):
+    lib = mk.lib()
+    assert lib.mla_mfma_rate(0, P16, 1 << 20, None) == mk.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_mfma_rate((1 << 20) + 1, P16, 1 << 20, None) == mk.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_mfma_rate(16, None, 1 << 20, None) == mk.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_mfma_rate(16, P16, 15, None) == mk.MLA_ERR_INVALID_ARGUMENT
+    assert "needed" in mk.last_error()
+
+
 def test_transpose_rejects(mk):
     lib = mk.lib()
     far = P16 + (1 << 32)

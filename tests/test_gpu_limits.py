@@ -117,3 +117,43 @@ def test_stream_copy_is_a_byte_copy(mk):
         torch.cuda.synchronize()
         assert torch.equal(dst, src), n
     mk.mla_stream_copy(src[:0], dst[:0])
+
+
+def test_stream_mix_is_a_chunk_xor(mk):
+    """The mixed read:write measurement kernel: output chunk i is the XOR of
+    input chunks r i .. r i + r - 1, for r = 1 to 4, with a partial last
+    workgroup."""
+    announce("stream mix")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(78)
+    n = 4096 + 48
+    for r in (1, 2, 3, 4):
+        src = torch.randint(-2**31, 2**31 - 1, (n * r // 4,), generator=g, device=DEV,
+                            dtype=torch.int64).to(torch.int32)
+        dst = torch.zeros(n // 4, dtype=torch.int32, device=DEV)
+        mk.mla_stream_mix(dst, src, r)
+        torch.cuda.synchronize()
+        chunks = src.view(-1, r, 4).cpu()
+        ref = chunks[:, 0].clone()
+        for k in range(1, r):
+            ref ^= chunks[:, k]
+        assert torch.equal(dst.view(-1, 4).cpu(), ref), r
+
+
+def test_mfma_rate_clock_readings(mk):
+    """The matrix-core rate probe: every wavefront of every workgroup writes
+    increasing shader-clock and real-time readings, and the issue interval
+    and clock derived from them are in a physical range."""
+    announce("mfma rate probe")
+    cus = torch.cuda.get_device_properties(DEV).multi_processor_count
+    clocks = torch.zeros(16 * cus, dtype=torch.int64, device=DEV)
+    iters = 256
+    mk.mla_mfma_rate(clocks, iters)
+    torch.cuda.synchronize()
+    c = clocks.view(-1, 4).cpu().numpy()
+    assert (c[:, 1] > c[:, 0]).all() and (c[:, 3] > c[:, 2]).all()
+    cycles = (c[:, 1] - c[:, 0]).astype(float)
+    per_mfma = cycles.mean() / (iters * 12)
+    ghz = cycles.sum() / (c[:, 3] - c[:, 2]).astype(float).sum() * 0.1
+    announce(f"{per_mfma:.1f} cycles per MFMA at {ghz:.2f} GHz")
+    assert 8 <= per_mfma <= 256 and 0.3 <= ghz <= 3.5
