@@ -404,8 +404,8 @@ def copy_ceiling(torch, mk, dev, flush):
     """Device-to-device copies as the ceiling the HBM-bound kernels are
     compared with: the runtime's copy (torch copy_, 1 GiB) and the library's
     streaming copy (the launch shape of its streaming kernels) at 1 GiB and
-    at the total size of the context epilogue (36.6 MB moved) and of one
-    gather (14.2 MB moved), and a streaming kernel with the fp8 pack's
+    at the total size of the long-context insert (142.2 MB moved), of the
+    context epilogue (36.6 MB moved) and of one gather (14.2 MB moved), and a streaming kernel with the fp8 pack's
     read:write mix (2:1) at the pack's size (437 MB moved); each timed by its own launch events after a
     cache flush (the runtime's copy with stream events), median of 20."""
     out = {}
@@ -428,6 +428,7 @@ def copy_ceiling(torch, mk, dev, flush):
                                 "GBps": round(2 * n / us / 1e3, 1),
                                 "frac_of_peak": round(2 * n / us / 1e3 / HBM_PEAK_GBS, 4)}
     for name, moved in (("stream_copy_1GiB", 2 * n),
+                        ("stream_copy_insert_size", insert_bytes(L, 16384)),
                         ("stream_copy_epilogue_size", epilogue_bytes(L, 4096)),
                         ("stream_copy_gather_size", gather_bytes(8192))):
         half = (moved // 2) // 16 * 16
