@@ -10,11 +10,12 @@
 //    for a kernel with that read:write mix (the fp8 pack reads twice the
 //    bytes it writes).
 //  * mla_mfma_rate: one workgroup of 4 wavefronts per compute unit, each
-//    wavefront issuing a long run of independent v_mfma_f32_32x32x16_bf16
-//    (12 accumulators, as in the projection) between two reads of the
-//    shader clock and of the 100 MHz real-time counter: the matrix cores'
-//    issue rate in cycles and the clock they hold under full MFMA load, the
-//    ceiling the projection is compared with.
+//    wavefront issuing a long run of v_mfma_f32_32x32x16_bf16 on a 4 x 3
+//    tile of accumulators (the projection's) with operands that change every
+//    step, between two reads of the shader clock and of the 100 MHz
+//    real-time counter: the matrix cores' issue rate in cycles and the clock
+//    they hold under full MFMA load, the ceiling the projection is compared
+//    with.
 #include "mla_common.hpp"
 
 namespace mla {
@@ -37,37 +38,61 @@ __global__ __launch_bounds__(256) void stream_copy_kernel(uint4* dst, const uint
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-constexpr int kRateAcc = 12;
+
+// Operands like the projection's: a wavefront's 4 x 3 tile of accumulators,
+// each step multiplying 4 A fragments by 3 B fragments, with two fragment
+// sets used on alternate steps; values in +-[1, 2) with pseudo-random
+// significands, so the matrix cores switch like they do on real data (the
+// clock they hold under load depends on it).
+__device__ __forceinline__ bf16x8_t rate_operand(uint32_t seed) {
+  bf16x8_t v;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    seed = seed * 1664525u + 1013904223u;
+    const uint32_t bits = 0x3F80u | ((seed >> 9) & 0x7Fu) | ((seed >> 16) & 0x8000u);
+    v[i] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(bits));
+  }
+  return v;
+}
 
 __global__ __launch_bounds__(256) void mfma_rate_kernel(uint64_t* clocks, int32_t iters) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  // operands: 0 / 1 patterns that differ by lane
-  const uint32_t bits = 0x9E3779B9u * static_cast<uint32_t>(lane + 1);
-  bf16x8_t a, b;
+  const uint32_t seed = 0x9E3779B9u * static_cast<uint32_t>(threadIdx.x + 1) + blockIdx.x;
+  bf16x8_t fa[2][4], fb[2][3];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    a[i] = static_cast<__bf16>(static_cast<float>((bits >> i) & 1u));
-    b[i] = static_cast<__bf16>(static_cast<float>((bits >> (i + 8)) & 1u));
+  for (int s = 0; s < 2; ++s) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[s][i] = rate_operand(seed + 101u * (s * 7 + i));
+#pragma unroll
+    for (int j = 0; j < 3; ++j) fb[s][j] = rate_operand(seed + 101u * (s * 7 + 4 + j));
   }
-  f32x16_t acc[kRateAcc];
+  f32x16_t acc[4][3];
 #pragma unroll
-  for (int j = 0; j < kRateAcc; ++j)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   __syncthreads();
   const uint64_t c0 = __builtin_amdgcn_s_memtime();
   const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
-  for (int32_t it = 0; it < iters; ++it) {
+  for (int32_t it = 0; it < iters; it += 2) {
 #pragma unroll
-    for (int j = 0; j < kRateAcc; ++j)
-      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][i], fb[s][j], acc[i][j], 0, 0, 0);
   }
   float sum = 0.0f;
 #pragma unroll
-  for (int j = 0; j < kRateAcc; ++j)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sum += acc[j][r];
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sum += acc[i][j][r];
   const uint64_t c1 = __builtin_amdgcn_s_memtime();
   const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
   if (lane == 0) {
@@ -130,8 +155,8 @@ extern "C" int32_t mla_mfma_rate(int64_t iters, uint64_t* clocks, int64_t clock_
                                  mla_stream_t stream) {
   static const char* fn = "mla_mfma_rate";
   clear_error();
-  if (iters <= 0 || iters > (int64_t(1) << 20))
-    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: iters must be in [1, 2^20]", fn);
+  if (iters <= 0 || iters > (int64_t(1) << 20) || (iters & 1))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: iters must be even, in [2, 2^20]", fn);
   if (!clocks) return fail(MLA_ERR_INVALID_ARGUMENT, "%s: clocks is NULL", fn);
   const int64_t cus = cu_count();
   if (clock_words < 16 * cus)

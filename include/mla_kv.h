@@ -477,15 +477,17 @@ int32_t mla_stream_mix(void* dst, const void* src, int64_t dst_bytes, int32_t re
 /* ------------------------------------------------------------------------
  * mla_mfma_rate -- measurement aid, not a step of the path: one workgroup of
  * 4 wavefronts on every compute unit, each wavefront issuing iters x 12
- * independent v_mfma_f32_32x32x16_bf16 (16384 multiply-adds each) between
- * two reads of the shader clock and of the 100 MHz real-time counter.
+ * v_mfma_f32_32x32x16_bf16 (16384 multiply-adds each) on a 4 x 3 tile of
+ * accumulators, with pseudo-random operands in +-[1, 2) that alternate
+ * between two sets every step, between two reads of the shader clock and of
+ * the 100 MHz real-time counter.
  * Wavefront w of workgroup g writes clocks[(4 g + w) * 4 + 0..3] = shader
  * clock at start, at end, real-time counter at start, at end (device memory,
  * at least 16 words per compute unit: clock_words >= 16 x CU count).  From
  * them: cycles per MFMA issue per SIMD and the clock held under full MFMA
  * load, hence the bf16 matrix peak the projection is compared with
- * (MLA_ERR_INVALID_ARGUMENT for iters outside [1, 2^20], a NULL or short
- * clocks array).
+ * (MLA_ERR_INVALID_ARGUMENT for an odd iters or one outside [2, 2^20], a
+ * NULL or short clocks array).
  * ------------------------------------------------------------------------ */
 int32_t mla_mfma_rate(int64_t iters, uint64_t* clocks, int64_t clock_words, mla_stream_t stream);
 

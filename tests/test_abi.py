@@ -246,6 +246,7 @@ def test_mfma_rate_rejects(mk):
     lib = mk.lib()
     assert lib.mla_mfma_rate(0, P16, 1 << 20, None) == mk.MLA_ERR_INVALID_ARGUMENT
     assert lib.mla_mfma_rate((1 << 20) + 1, P16, 1 << 20, None) == mk.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_mfma_rate(15, P16, 1 << 20, None) == mk.MLA_ERR_INVALID_ARGUMENT
     assert lib.mla_mfma_rate(16, None, 1 << 20, None) == mk.MLA_ERR_INVALID_ARGUMENT
     assert lib.mla_mfma_rate(16, P16, 15, None) == mk.MLA_ERR_INVALID_ARGUMENT
     assert "needed" in mk.last_error()
