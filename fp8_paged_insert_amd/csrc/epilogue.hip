@@ -23,9 +23,10 @@
 // round trip), RoPE's (i, i + 32) pairs sit in lanes j and j ^ 8 and swap
 // with one DPP row rotation, and the token's position indexes the cos/sin
 // table directly instead of a repeated-positions buffer.  The rotation is
-// rounded correctly to bf16 even where its two products nearly cancel
-// (rope4: an fp32 fast path with an exact float64 fallback).  For up to 8
-// layers the layers' RMSNorm weights are read into LDS once per workgroup
+// rounded once to bf16 even where its two products nearly cancel (rope4v:
+// an fp32 fast path kept only where it is provably the correct rounding,
+// else float64 from the table's hi + lo values).  For up to 8 layers the
+// layers' RMSNorm weights are read into LDS once per workgroup
 // (epilogue_lds_kernel); otherwise each row group reads its layer's weights
 // from global memory (epilogue_kernel).
 #include "mla_common.hpp"

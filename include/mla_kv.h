@@ -175,8 +175,11 @@ int32_t mla_kv_insert_grouped(
  * rotate with the hi values in fp32 and, where that result could round to
  * a different bf16 value than the exact rotation (the two products nearly
  * cancelling, or the fp32 value next to a rounding boundary), recompute it
- * in float64 from hi + lo; every rotated value is thus the correctly
- * rounded bf16 of the rotation.
+ * in float64 from hi + lo and rounds once; every rotated value is thus the
+ * correctly rounded bf16 of a rotation accurate to about 2^-47 relative to
+ * the magnitudes of the pair (at most one ulp from the exact rotation's
+ * correct rounding, and equal to it unless that lies within 2^-47 of a
+ * rounding boundary).
  * ([P2] 关键源码片段: RoPE of k_pe at each context position, the positions
  * being the same for every layer; the formula itself is not printed, the
  * non-interleaved form with the given base is the reading taken.)
@@ -201,7 +204,7 @@ int32_t mla_rope_cos_sin_cache(float* out, int64_t max_pos, int64_t rope_dim,
  * For each (l, t):
  *   row[0:R]   = bf16(x_i * (mean(x^2) + eps)^(-1/2) * gamma[l, i])  (fp32 math)
  *   row[R:R+P] = bf16(rotation of k_pe by theta(positions[t]))   (pairs (i, i+P/2);
- *                correctly rounded, see mla_rope_cos_sin_cache)
+ *                rounded once, see mla_rope_cos_sin_cache)
  *   then row is inserted exactly as mla_kv_insert_grouped inserts [kv_c | k_pe].
  * dbg_rows  optional device bf16 [L, T, R+P] contiguous: receives every row
  *   (also those whose slot is negative); NULL to skip.
@@ -411,7 +414,7 @@ int32_t mla_ctx_neutralize_partials(void* out, int64_t out_tok_stride, int64_t o
  * elsewhere in this library:
  *   pe_q = RoPE(q_pe[t, h, :], pos[t]),  pe_k = RoPE(k_pe[t, :], pos[t])
  *            (half-split rotation, angles from cos_sin as in
- *            mla_ctx_kv_epilogue; each result correctly rounded to bf16)
+ *            mla_ctx_kv_epilogue; each result rounded once to bf16)
  *   q_out[t, h, :]   = [q_nope[t, h, :] | pe_q]
  *   key_out[t, h, :] = [k_nope[t, h, :] | pe_k]     (same pe_k for every head)
  *   v_out[t, h, :]   = v[t, h, :]                    (KEY_V_FP8 only)
