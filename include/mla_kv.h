@@ -175,11 +175,11 @@ int32_t mla_kv_insert_grouped(
  * rotate with the hi values in fp32 and, where that result could round to
  * a different bf16 value than the exact rotation (the two products nearly
  * cancelling, or the fp32 value next to a rounding boundary), recompute it
- * in float64 from hi + lo and rounds once; every rotated value is thus the
- * correctly rounded bf16 of a rotation accurate to about 2^-47 relative to
- * the magnitudes of the pair (at most one ulp from the exact rotation's
- * correct rounding, and equal to it unless that lies within 2^-47 of a
- * rounding boundary).
+ * in float64 from hi + lo and rounds once.  Every rotated value is thus one
+ * rounding of the rotation by the table's values, carried out with an error
+ * of about 2^-52 relative to the magnitudes of the pair: the correctly
+ * rounded bf16 of that rotation unless it lies that close to a rounding
+ * boundary (then at most one ulp away).
  * ([P2] 关键源码片段: RoPE of k_pe at each context position, the positions
  * being the same for every layer; the formula itself is not printed, the
  * non-interleaved form with the given base is the reading taken.)
