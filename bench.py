@@ -990,6 +990,13 @@ def main():
     if not args.no_components:
         flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         result["copy_ceiling"] = copy_ceiling(torch, mk, dev, flush)
+        # the dominant kernel against the measured ceiling for its traffic: a
+        # streaming kernel with the pack's read:write mix at the pack's size,
+        # timed the same way (events recorded by the launch, after a flush)
+        mix = result["copy_ceiling"]["stream_mix_2to1_pack_size"]
+        result["roofline"]["measured_ceiling"] = {
+            "GBps": mix["GBps"], "what": "copy_ceiling.stream_mix_2to1_pack_size",
+            "frac": round(roofline["achieved"] / mix["GBps"], 4)}
         comps = {"small_batch_insert": small_batch(torch, mk, dev),
                  "single_layer_insert": single_layer_component(torch, mk, dev),
                  "context_pack": context_pack_component(torch, mk, dev, flush),
