@@ -242,11 +242,14 @@ def test_long_context_pack_16_chunks_full(mk):
 
 @pytest.mark.parametrize("kind", ["fp8", "fp8_e5m2", "bfloat16", "raw"])
 @pytest.mark.parametrize("mode", ["bf16", "fp8", "fp8_scaled"])
-def test_pack_gather_joint_launch(mk, kind, mode):
+@pytest.mark.parametrize("max_blocks", [0, 2])
+def test_pack_gather_joint_launch(mk, kind, mode, max_blocks):
     """The joint launch against the oracle's pack of one chunk and gather of
     the next, for every gather kind and both 16-bit-source pack modes, on a
-    ragged shape (300 tokens x 3 heads packed, 437 tokens gathered)."""
-    announce("pack + gather joint launch", kind, mode)
+    ragged shape (300 tokens x 3 heads packed, 437 tokens gathered), with the
+    full pack grid (the gather's workgroups first) and with the pack part
+    capped at 2 workgroups (grid-stride; the gather's workgroups last)."""
+    announce("pack + gather joint launch", kind, mode, max_blocks)
     g = torch.Generator().manual_seed(300 + len(kind) + len(mode))
     T, H, Tg = 300, 3, 437
     kvb = synth.bf16_normal((T, H, 256), g, std=40.0 if mode == "fp8_scaled" else 1.0)
@@ -272,7 +275,7 @@ def test_pack_gather_joint_launch(mk, kind, mode):
     kw = dict(v=dkvb[..., 128:], v_out=vo, mode=mk.MLA_PACK_KEY_V_FP8, k_scale=ks,
               v_scale=vs) if fp8 else {}
     mk.mla_ctx_kv_pack_gather(dkvb[..., :128], dws[:, 512:], key, cache.to(DEV), sl.to(DEV), out,
-                              cache_scale=cs, kv_cache_dtype=dt, **kw)
+                              cache_scale=cs, kv_cache_dtype=dt, max_blocks=max_blocks, **kw)
     torch.cuda.synchronize()
     fmt = "e5m2" if kind == "fp8_e5m2" else "e4m3"
     ref_g = oracle.gather(cache_np, sl.numpy(), 0.8125 if cs is not None else 1.0,
