@@ -135,11 +135,21 @@ class LongContext:
         self.v8 = torch.empty(chunk, heads, 128, dtype=torch.uint8, device=dev)
         self.pack_events = []
 
+    # One timed step in this many records the events of one joint launch:
+    # each pair of launch events costs the step about 6 us on MI355X (the
+    # step without them measured 1.238-1.247 ms, with them on every step
+    # 1.244-1.247 ms, on one box), so they are taken on every other timed
+    # step, the timed chunk advancing by 4 (of 15) each time so that the
+    # samples spread over the chunk loop.
+    EVENT_EVERY = 2
+    CHUNK_STRIDE = 4
+
     def arm_timing(self, steps):
         """Create the HIP events the timed packs will record into."""
         torch = self.torch
-        n = steps
-        self.timed_chunk = -1
+        n = (steps + self.EVENT_EVERY - 1) // self.EVENT_EVERY
+        self.timed_chunk = -self.CHUNK_STRIDE
+        self.timed_steps = 0
         self.event_pool = []
         for _ in range(n):
             e0 = torch.cuda.Event(enable_timing=True)
@@ -159,15 +169,18 @@ class LongContext:
         grouped insert, then the chunk loop with the joint launch -- gather of
         chunk 0, then for every chunk c the pack of c together with the gather
         of c + 1 into the other workspace (the last chunk packs alone).  With
-        time_pack, one joint launch per step (the chunk index rotating)
-        records its own start and end events.  max_blocks > 0 caps the
-        pack's grid (grid-stride loop)."""
+        time_pack, one joint launch in every EVENT_EVERY-th step (the chunk
+        index advancing by CHUNK_STRIDE) records its own start and end events.  max_blocks > 0
+        caps the pack's grid (grid-stride loop)."""
         mk = self.mk
         mk.mla_kv_insert_grouped(self.kv_c, self.k_pe, self.ptrs, self.slots, 64, 64 * W, W,
                                  self.scales, "fp8")
         n = len(self.kvb)
         if time_pack:
-            self.timed_chunk = (self.timed_chunk + 1) % (n - 1)
+            time_pack = self.timed_steps % self.EVENT_EVERY == 0
+            self.timed_steps += 1
+        if time_pack:
+            self.timed_chunk = (self.timed_chunk + self.CHUNK_STRIDE) % (n - 1)
         mk.mla_ctx_latent_gather(self.ctx_cache, self.src_slots[:self.chunk], self.ws2[0],
                                  self.ctx_scale, "fp8")
         for c, kvb in enumerate(self.kvb):
@@ -944,7 +957,9 @@ def main():
                           "dequantising gather of the next chunk's 8192 latent rows",
                 "achieved": round(achieved, 1),
                 "timing": "HIP events recorded by the kernel launch itself (start/stop of its "
-                          "execution) on one joint launch per timed step, chunk index rotating",
+                          f"execution) on one joint launch in every {LongContext.EVENT_EVERY}nd "
+                          "timed step, the chunk index advancing by "
+                          f"{LongContext.CHUNK_STRIDE} of 15 each time",
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(), "bytes_per_launch": joint_b,
                 "avg_launch_us": round(joint_us, 2), "launches": len(wl.pack_events)}
