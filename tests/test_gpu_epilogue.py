@@ -154,6 +154,17 @@ def test_epilogue_layer_counts_and_row_counts(mk, L, T):
     check(d, caches, rows, "fp8")
 
 
+@pytest.mark.parametrize("L,T", [(8, 77), (9, 77)])
+def test_epilogue_bf16_caches_both_kernels(mk, L, T):
+    """bf16 caches through the LDS-weight kernel (8 layers) and the other one
+    (9 layers)."""
+    announce("epilogue bf16 caches", L, T)
+    d = synth.context_epilogue(num_tokens=T, num_blocks=8, with_gemm=False, seed=200 + L,
+                               num_layers=L, fp8=False)
+    caches, rows = run_epilogue(mk, d, "auto")
+    check(d, caches, rows, "auto")
+
+
 def test_epilogue_shared_slots_negative_and_random_positions(mk):
     announce("epilogue shared/-1/positions")
     d = synth.context_epilogue(num_tokens=300, num_blocks=8, with_gemm=False, seed=31)
