@@ -142,21 +142,25 @@ def set_launch_events(start=None, stop=None):
 
 
 _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_get_device = getattr(torch._C, "_cuda_getDevice", None)
 
 
 def _stream(t: torch.Tensor):
     """torch's current HIP stream on the tensor's device (a hipStream_t).  The
     library launches on the calling thread's current device, so the tensors
-    must live there (select it with torch.cuda.device / set_device)."""
-    if t.device.type != "cuda":
+    must live there (select it with torch.cuda.device / set_device).  Device
+    indices are compared as integers: t.device builds a Python object on
+    every access, which a small-batch call would pay several times."""
+    idx = t.get_device()
+    if idx < 0 or not t.is_cuda:
         raise RuntimeError(f"tensor on {t.device}, expected a GPU tensor")
-    cur = torch.cuda.current_device()
-    if t.device.index is not None and t.device.index != cur:
+    cur = _get_device() if _get_device is not None else torch.cuda.current_device()
+    if idx != cur:
         raise RuntimeError(f"tensors on {t.device} but the current device is cuda:{cur}; "
-                           f"call under torch.cuda.device({t.device.index})")
+                           f"call under torch.cuda.device({idx})")
     if _raw_stream is not None:
         return _raw_stream(cur)
-    return torch.cuda.current_stream(t.device).cuda_stream
+    return torch.cuda.current_stream(cur).cuda_stream
 
 
 def _ptr(t):
@@ -171,7 +175,7 @@ def _need(t, dtypes, name):
 
 
 def _same_device(t, ref, name, ref_name):
-    if t.device != ref.device:
+    if t.get_device() != ref.get_device() or t.is_cuda != ref.is_cuda:
         raise RuntimeError(f"{name} is not on the same CUDA device as {ref_name} "
                            f"({t.device} vs {ref.device})")
 
@@ -271,10 +275,11 @@ def _insert_args(kv_c, k_pe, kv_cache_ptrs, slot_mapping, block_size, block_stri
     if kv_c.dim() != 3 or k_pe.dim() != 3:
         raise RuntimeError("kv_c and k_pe must be [num_layers, num_tokens, dim] views")
     L, T, R = kv_c.shape
-    P = k_pe.shape[2]
-    if tuple(k_pe.shape[:2]) != (L, T):
+    Lp, Tp, P = k_pe.shape
+    if (Lp, Tp) != (L, T):
         raise RuntimeError("kv_c and k_pe disagree on layers/tokens")
-    if (R > 1 and kv_c.stride(2) != 1) or (P > 1 and k_pe.stride(2) != 1):
+    skv, spe = kv_c.stride(), k_pe.stride()
+    if (R > 1 and skv[2] != 1) or (P > 1 and spe[2] != 1):
         raise RuntimeError("kv_c / k_pe innermost dimension must be contiguous")
     _same_device(k_pe, kv_c, "k_pe", "kv_c")
     sm, sls = _slots_2d(slot_mapping, L, T)
@@ -288,8 +293,8 @@ def _insert_args(kv_c, k_pe, kv_cache_ptrs, slot_mapping, block_size, block_stri
         _check_scales(kv_scales, L, kv_c)
     elif kv_scales is not None:
         raise RuntimeError("a bf16 cache takes no kv_scales")
-    args = (_ptr(kv_c), kv_c.stride(0), kv_c.stride(1), _ptr(k_pe), k_pe.stride(0),
-            k_pe.stride(1), _ptr(kv_cache_ptrs), _ptr(kv_scales), _ptr(sm), sls, L, T, R, P,
+    args = (_ptr(kv_c), skv[0], skv[1], _ptr(k_pe), spe[0],
+            spe[1], _ptr(kv_cache_ptrs), _ptr(kv_scales), _ptr(sm), sls, L, T, R, P,
             int(block_size), int(block_stride), int(entry_stride), dt, _stream(kv_c))
     return args, kv_cache_ptrs
 
@@ -329,9 +334,10 @@ class PreparedInsert:
         self._fn = lib().mla_kv_insert_grouped
 
     def __call__(self):
-        if torch.cuda.current_device() != self._index:
+        cur = _get_device() if _get_device is not None else torch.cuda.current_device()
+        if cur != self._index:
             raise RuntimeError(f"prepared on cuda:{self._index} but the current device is "
-                               f"cuda:{torch.cuda.current_device()}")
+                               f"cuda:{cur}")
         self._args[-1] = (_raw_stream(self._index) if _raw_stream is not None else
                           torch.cuda.current_stream(self._index).cuda_stream)
         st = self._fn(*self._args)
