@@ -818,7 +818,7 @@ def cpu_baseline(torch):
     return out
 
 
-def oracle_components(torch):
+def oracle_components(torch, projection_rows=4096):
     """The oracle (plain serial C, one core) timed beside the components the
     step does not contain, each on a bounded sample of its workload and in the
     component's unit (inputs are generated outside the timed calls)."""
@@ -862,17 +862,19 @@ def oracle_components(torch):
     from concurrent.futures import ThreadPoolExecutor
 
     nt = max(1, min(16, os.cpu_count() or 1))
-    xa = u16(synth.bf16_normal((4096, 7168), g))
+    rows = projection_rows
+    xa = u16(synth.bf16_normal((rows, 7168), g))
     with ThreadPoolExecutor(max_workers=nt) as ex:
         t0 = time.perf_counter()
-        list(ex.map(lambda i: oracle.gemm_rows(xa, w, np.arange(4096 * i // nt,
-                                                                 4096 * (i + 1) // nt,
+        list(ex.map(lambda i: oracle.gemm_rows(xa, w, np.arange(rows * i // nt,
+                                                                 rows * (i + 1) // nt,
                                                                  dtype=np.int64)),
                     range(nt)))
         secs = time.perf_counter() - t0
+    what = "the whole 4096-row product" if rows == 4096 else f"{rows} of the 4096 rows"
     out["context_kv_proj"]["all_cores"] = {
-        "value": round(2 * 4096 * 7168 * L * W / secs / 1e9, 3), "unit": "GFLOP/s", "cores": nt,
-        "sample": f"the whole 4096-row product in {secs:.2f}s (wall) over {nt} threads"}
+        "value": round(2 * rows * 7168 * L * W / secs / 1e9, 3), "unit": "GFLOP/s", "cores": nt,
+        "sample": f"{what} in {secs:.2f}s (wall) over {nt} threads"}
     # context epilogue: 5 layers x 1024 tokens
     e = synth.context_epilogue("cpu", num_tokens=1024, num_blocks=16, with_gemm=False)
     caches = [c.numpy().copy() for c in e["caches"]]

@@ -61,8 +61,12 @@ def test_oracle_timed_beside_each_component():
 
     import bench
 
-    r = bench.oracle_components(torch)
+    # the multi-threaded whole projection on a few rows here (the bench runs
+    # all 4096)
+    r = bench.oracle_components(torch, projection_rows=64)
     assert set(r) == {"small_batch_insert", "context_kv_proj", "context_epilogue", "chunk_merge",
                       "new_token_epilogue"}
     for name, o in r.items():
         assert o["value"] > 0 and o["cores"] == 1 and o["unit"] and o["sample"], name
+    mt = r["context_kv_proj"]["all_cores"]
+    assert mt["value"] > 0 and mt["cores"] >= 1 and "64 of the 4096 rows" in mt["sample"]
