@@ -418,7 +418,8 @@ def copy_ceiling(torch, mk, dev, flush):
     compared with: the runtime's copy (torch copy_, 1 GiB) and the library's
     streaming copy (the launch shape of its streaming kernels) at 1 GiB and
     at the total size of the long-context insert (142.2 MB moved), of the
-    context epilogue (36.6 MB moved) and of one gather (14.2 MB moved), and a streaming kernel with the fp8 pack's
+    context epilogue (36.6 MB moved), of one gather (14.2 MB moved) and of the
+    weight transpose (82.6 MB moved), and a streaming kernel with the fp8 pack's
     read:write mix (2:1) at the pack's size (437 MB moved); each timed by its own launch events after a
     cache flush (the runtime's copy with stream events), median of 20."""
     out = {}
@@ -443,7 +444,8 @@ def copy_ceiling(torch, mk, dev, flush):
     for name, moved in (("stream_copy_1GiB", 2 * n),
                         ("stream_copy_insert_size", insert_bytes(L, 16384)),
                         ("stream_copy_epilogue_size", epilogue_bytes(L, 4096)),
-                        ("stream_copy_gather_size", gather_bytes(8192))):
+                        ("stream_copy_gather_size", gather_bytes(8192)),
+                        ("stream_copy_weight_transpose_size", 2 * 7168 * L * W * 2)):
         half = (moved // 2) // 16 * 16
         us, p90 = kernel_us(torch, mk, lambda: mk.mla_stream_copy(dst[:half], src[:half]), flush,
                             reps=20, warm=3)
@@ -751,6 +753,7 @@ def projection_component(torch, mk, dev, flush):
             "with_epilogue_us_stream_events": round(statistics.median(e2e), 2),
             "weight_transpose": {"us": round(tr_us, 2), "p90_us": round(tr_p90, 2),
                                  "bytes": 2 * 7168 * L * W * 2,
+                                 "GBps": round(2 * 7168 * L * W * 2 / tr_us / 1e3, 1),
                                  "note": "[7168, 2880] -> [2880, 7168], once per weight"},
             "with_weight_transpose_and_epilogue_us_stream_events": round(statistics.median(e2e_tr),
                                                                          2)}

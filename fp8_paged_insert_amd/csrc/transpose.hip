@@ -25,15 +25,19 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* src
                                                              int32_t rows, int32_t cols) {
   __shared__ __align__(16) uint16_t tile[kTile * kPadRow];
   const int r0 = blockIdx.y * kTile, c0 = blockIdx.x * kTile;
-  // load: 64 rows x 8 chunks of 8 values
+  // load: 64 rows x 8 chunks of 8 values, both of a thread's loads issued
+  // before either LDS write
+  const int lrow = threadIdx.x >> 3, lch = threadIdx.x & 7;
+  const bool cin = c0 + lch * 8 < cols;
+  uint4 lv[2];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int c = threadIdx.x + 256 * k;
-    const int row = c >> 3, ch = c & 7;
-    if (r0 + row < rows && c0 + ch * 8 < cols)
-      *reinterpret_cast<uint4*>(&tile[row * kPadRow + ch * 8]) =
-          ld16(src + int64_t(r0 + row) * lds_ + c0 + ch * 8);
-  }
+  for (int k = 0; k < 2; ++k)
+    if (cin && r0 + lrow + 32 * k < rows)
+      lv[k] = ld16(src + int64_t(r0 + lrow + 32 * k) * lds_ + c0 + lch * 8);
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    if (cin && r0 + lrow + 32 * k < rows)
+      *reinterpret_cast<uint4*>(&tile[(lrow + 32 * k) * kPadRow + lch * 8]) = lv[k];
   __syncthreads();
   // store: destination row = source column, 8 chunks of 8 source rows each
 #pragma unroll
