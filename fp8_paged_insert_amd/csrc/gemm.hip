@@ -37,6 +37,11 @@
 //    of the tile workgroups: with operands that start in HBM (a cache
 //    flushed by other work) the launch takes ~145 instead of ~165 us, with
 //    operands already cached the time is unchanged;
+//  * the finished tile is rounded to bf16 into LDS (over the stage buffers)
+//    and written out in 16-byte chunks along its rows: 24 store
+//    instructions per lane that cover whole 128-byte lines of Y, instead of
+//    192 two-byte stores straight from the accumulator layout (which took
+//    about 10 us of the launch);
 //  * rows beyond T and columns beyond N are clamped on load and masked on
 //    store, so any T >= 1 and any N that is a multiple of 16 work.
 #include <type_traits>
@@ -57,6 +62,9 @@ constexpr int kStageBytes = (kBM + kBN) * kRowBytes;    // X tile then W tile
 constexpr size_t kLdsBytes = size_t(2) * kStageBytes;   // two stages: 114688 bytes
 constexpr int kWaveM = 128, kWaveN = 96;                // per-wavefront tile
 constexpr int kSubM = kWaveM / 32, kSubN = kWaveN / 32;
+constexpr int kOutRow = kBN * 2 + 16;  // bytes per output-tile row in LDS (padded)
+static_assert(size_t(kBM) * kOutRow <= kLdsBytes, "the output tile fits over the stages");
+constexpr int kDppSwapPairs = 0xB1;     // DPP quad_perm [1, 0, 3, 2]: lanes 2c <-> 2c + 1
 constexpr int kXBlocks = kBM / 8 / 4;  // 1 KiB (8-row) LDS blocks of X each wavefront fills
 constexpr int kWBlocks = kBN / 8 / 4;  // and of W
 
@@ -330,21 +338,43 @@ __global__ __launch_bounds__(kThreads, 1) void kv_proj_kernel(const GemmArgs a) 
     if (kb + 2 < stages) do_stage(R2{}, kb + 2);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // the repeated copies have landed
+  __syncthreads();                      // and no wavefront reads a stage any more
 
-  // accumulator layout: value r of lane l is C[8 (r / 4) + 4 (l / 32) + (r % 4)][l % 32]
+  // Output: the workgroup's bf16 tile is assembled in LDS (kBM rows of
+  // kOutRow bytes, over the stage buffers), then written out in 16-byte
+  // chunks, consecutive lanes along a row, so every store instruction covers
+  // whole 128-byte lines of Y.  Accumulator value r of lane l is
+  // C[8 (r / 4) + 4 (l / 32) + (r % 4)][l % 32] of its 32 x 32 tile: values r
+  // and r + 1 (r even) are rows R and R + 1 of one column.  Lanes 2c and
+  // 2c + 1 swap their rounded pairs, so the even lane holds row R and the odd
+  // lane row R + 1 of columns 2c and 2c + 1: one 4-byte LDS write each.
+  const int odd = lane & 1;
 #pragma unroll
   for (int i = 0; i < kSubM; ++i) {
 #pragma unroll
     for (int j = 0; j < kSubN; ++j) {
-      const int n = n0 + wn * kWaveN + j * 32 + (lane & 31);
-      if (n >= a.N) continue;
+      const int col = wn * kWaveN + j * 32 + (lane & 31) - odd;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * kWaveM + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-        if (m < a.T)
-          a.y[int64_t(m) * a.ldy + n] = static_cast<uint16_t>(cvt_bf16x2(acc[i][j][r], 0.0f));
+      for (int r = 0; r < 16; r += 2) {
+        const uint32_t own = cvt_bf16x2(acc[i][j][r], acc[i][j][r + 1]);
+        const uint32_t other = static_cast<uint32_t>(
+            __builtin_amdgcn_update_dpp(0, static_cast<int>(own), kDppSwapPairs, 0xF, 0xF, false));
+        const uint32_t word = odd ? __builtin_amdgcn_perm(own, other, 0x07060302u)
+                                  : __builtin_amdgcn_perm(other, own, 0x05040100u);
+        const int row = wm * kWaveM + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4) + odd;
+        *reinterpret_cast<uint32_t*>(lds + row * kOutRow + col * 2) = word;
       }
     }
+  }
+  __syncthreads();
+  constexpr int kRowChunks = kBN * 2 / 16;
+#pragma unroll 4
+  for (int c = tid; c < kBM * kRowChunks; c += kThreads) {
+    const int row = c / kRowChunks, ch = c - row * kRowChunks;
+    const int m = m0 + row, n = n0 + ch * 8;
+    // N is a multiple of 16: a chunk of 8 columns is wholly inside or outside
+    if (m < a.T && n < a.N)
+      st16(a.y + int64_t(m) * a.ldy + n, *reinterpret_cast<const uint4*>(lds + row * kOutRow + ch * 16));
   }
 }
 
