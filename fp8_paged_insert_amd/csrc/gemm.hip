@@ -20,23 +20,26 @@
 //    (global_load_lds_dwordx4, 1 KiB per wavefront instruction), no
 //    register staging; LDS rows are 128 bytes with an XOR swizzle of the
 //    16-byte chunks, so the fragment reads are bank-conflict free;
-//  * two LDS stages and one barrier per stage, placed after the second of
-//    the four K steps: the fragments of steps 2 and 3 are read before it
-//    (three fragment register slots, rotating by one per stage), so the
-//    copy of the stage after next can start right after it and is spread
-//    over the MFMAs of steps 2 and 3, seven 1 KiB copies under each; step
-//    3 also hides the next stage's first fragment reads, and every step's
-//    MFMAs hide the next step's fragment reads (the issue order is pinned
-//    with sched_group_barrier).  Copies issued in one burst under the last
-//    step alone measured 10% slower with cold operands;
+//  * the X tile in a ring of three LDS buffers, the W tile in two (144 KiB),
+//    and one barrier per stage, placed after the second of the four K
+//    steps: the fragments of steps 2 and 3 are read before it (three
+//    fragment register slots, rotating by one per stage), so stage kb's W
+//    buffer is free right after it.  The copies of stage kb + 2 are spread
+//    over the whole of stage kb: its 8 X copies per wavefront under steps
+//    0 and 1 (into the X buffer stage kb - 1 left), its 6 W copies under
+//    steps 2 and 3; the barrier waits only for stage kb + 1.  Step 3 also
+//    hides the next stage's first fragment reads, and every step's MFMAs
+//    hide the next step's fragment reads (the issue order is pinned with
+//    sched_group_barrier).  All 14 copies under steps 2 and 3 (two
+//    buffers each) measured 2% slower, under step 3 alone 10% slower;
 //  * tiles are grouped per XCD so the workgroups sharing an L2 share their
 //    X and W blocks;
 //  * up to 16 extra workgroups, on compute units the tiles leave idle (16
 //    of 256 for the default problem), read one dword of every upcoming
 //    K stage's row segments so X and W arrive in the last-level cache ahead
 //    of the tile workgroups: with operands that start in HBM (a cache
-//    flushed by other work) the launch takes ~145 instead of ~165 us, with
-//    operands already cached the time is unchanged;
+//    flushed by other work) this saved about 20 us of the launch (165 ->
+//    145 us when it was added), with operands already cached nothing;
 //  * the finished tile is rounded to bf16 into LDS (over the stage buffers)
 //    and written out in 16-byte chunks along its rows: 24 store
 //    instructions per lane that cover whole 128-byte lines of Y, instead of
@@ -58,8 +61,11 @@ typedef __attribute__((address_space(1))) void global_void_t;
 constexpr int kBM = 256, kBN = 192, kBK = 64;
 constexpr int kThreads = 256;
 constexpr int kRowBytes = kBK * 2;                      // one tile row of K values in LDS
-constexpr int kStageBytes = (kBM + kBN) * kRowBytes;    // X tile then W tile
-constexpr size_t kLdsBytes = size_t(2) * kStageBytes;   // two stages: 114688 bytes
+constexpr int kXStageBytes = kBM * kRowBytes;          // one stage of the X tile
+constexpr int kWStageBytes = kBN * kRowBytes;          // one stage of the W tile
+constexpr int kXBufs = 3, kWBufs = 2;
+constexpr int kWBase = kXBufs * kXStageBytes;
+constexpr size_t kLdsBytes = size_t(kXBufs) * kXStageBytes + size_t(kWBufs) * kWStageBytes;
 constexpr int kWaveM = 128, kWaveN = 96;                // per-wavefront tile
 constexpr int kSubM = kWaveM / 32, kSubN = kWaveN / 32;
 constexpr int kOutRow = kBN * 2 + 16;  // bytes per output-tile row in LDS (padded)
@@ -147,7 +153,7 @@ __device__ __forceinline__ void prefetch_operands(const GemmArgs& a, int p) {
 }
 
 __global__ __launch_bounds__(kThreads, 1) void kv_proj_kernel(const GemmArgs a) {
-  extern __shared__ __align__(16) uint8_t lds[];   // [2 stages][kBM + kBN rows][128 B]
+  extern __shared__ __align__(16) uint8_t lds[];   // [3][kBM rows], then [2][kBN rows], of 128 B
   if (static_cast<int>(blockIdx.x) >= a.compute_blocks) {
     prefetch_operands(a, blockIdx.x - a.compute_blocks);
     return;
@@ -189,21 +195,21 @@ __global__ __launch_bounds__(kThreads, 1) void kv_proj_kernel(const GemmArgs a) 
     const int n = min(n0 + r, a.N - 1);
     wsrc[i] = a.w + int64_t(n) * a.K + ((lane & 7) ^ swz(r)) * 8;
   }
-  // half h of a stage's copies: h = 0 the first 7 blocks (X blocks 0..6),
-  // h = 1 the rest (X block 7 and the 6 W blocks)
-  auto issue_half = [&](int kb, int buf, int h) {
-    uint8_t* base = lds + buf * kStageBytes;
+  // copies of stage kb: X blocks [c0, c1) into X buffer xb, W blocks
+  // [c0, c1) into W buffer wb
+  auto issue_x = [&](int kb, int xb, int c0, int c1) {
+    uint8_t* base = lds + xb * kXStageBytes;
 #pragma unroll
-    for (int c = 0; c < 7; ++c) {
-      const int i = h * 7 + c;
-      if (i < kXBlocks)
-        copy_to_lds(xsrc[i] + kb * kBK, base + (wave * kXBlocks + i) * 1024);
-      else
-        copy_to_lds(wsrc[i - kXBlocks] + kb * kBK,
-                    base + kBM * kRowBytes + (wave * kWBlocks + i - kXBlocks) * 1024);
-    }
+    for (int i = c0; i < c1; ++i)
+      copy_to_lds(xsrc[i] + kb * kBK, base + (wave * kXBlocks + i) * 1024);
   };
-  static_assert(kXBlocks + kWBlocks == 14, "copies are issued as two halves of 7");
+  auto issue_w = [&](int kb, int wb, int c0, int c1) {
+    uint8_t* base = lds + kWBase + wb * kWStageBytes;
+#pragma unroll
+    for (int i = c0; i < c1; ++i)
+      copy_to_lds(wsrc[i] + kb * kBK, base + (wave * kWBlocks + i) * 1024);
+  };
+  static_assert(kXBlocks == 8 && kWBlocks == 6, "copies are issued 4 + 4 + 3 + 3 per stage");
 
   f32x16_t acc[kSubM][kSubN];
 #pragma unroll
@@ -226,26 +232,40 @@ __global__ __launch_bounds__(kThreads, 1) void kv_proj_kernel(const GemmArgs a) 
     for (int i = 0; i < kSubM; ++i) xoff[i][kk] = frag_off(wm * kWaveM + i * 32 + (lane & 31), kk);
 #pragma unroll
     for (int j = 0; j < kSubN; ++j)
-      woff[j][kk] = kBM * kRowBytes + frag_off(wn * kWaveN + j * 32 + (lane & 31), kk);
+      woff[j][kk] = frag_off(wn * kWaveN + j * 32 + (lane & 31), kk);
   }
 
-  // Pipeline, per stage kb computed from buffer b = kb & 1, with three
-  // fragment register slots rotating by one per stage:
-  //   step 0: MFMAs, step 1's fragments read under them;
-  //   step 1: MFMAs, steps 2 and 3's fragments read under them;
-  //   barrier: stage kb + 1 (buffer b ^ 1) has landed everywhere and no
-  //            wavefront reads buffer b any more;
-  //   steps 2, 3: MFMAs with half of stage kb + 2's copies (into b) under
-  //            each, and stage kb + 1's step-0 fragments read under step 3.
+  // Pipeline, per stage kb computed from X buffer kb % 3 and W buffer
+  // kb % 2, with three fragment register slots rotating by one per stage:
+  //   step 0: MFMAs, step 1's fragments and 4 of stage kb + 2's X copies
+  //           (into X buffer (kb + 2) % 3) under them;
+  //   step 1: MFMAs, steps 2 and 3's fragments and the other 4 X copies
+  //           under them;
+  //   barrier: stage kb + 1 has landed everywhere (only the 8 X copies
+  //           just issued may be in flight) and no wavefront reads stage
+  //           kb any more;
+  //   steps 2, 3: MFMAs with 3 of stage kb + 2's W copies (into W buffer
+  //           kb % 2) under each, and stage kb + 1's step-0 fragments read
+  //           under step 3.
+  // X buffer (kb + 2) % 3 held stage kb - 1, whose last reads returned
+  // before the previous barrier, so the X copies may start before this
+  // stage's barrier.
   const int stages = a.K / kBK;
   bf16x8_t fa[3][kSubM], fb[3][kSubN];
-  auto read_frags = [&](int slot, const uint8_t* base, int kk) {
+  auto read_frags = [&](int slot, const uint8_t* xbase, const uint8_t* wbase, int kk) {
 #pragma unroll
     for (int i = 0; i < kSubM; ++i)
-      fa[slot][i] = *reinterpret_cast<const bf16x8_t*>(base + xoff[i][kk]);
+      fa[slot][i] = *reinterpret_cast<const bf16x8_t*>(xbase + xoff[i][kk]);
 #pragma unroll
     for (int j = 0; j < kSubN; ++j)
-      fb[slot][j] = *reinterpret_cast<const bf16x8_t*>(base + woff[j][kk]);
+      fb[slot][j] = *reinterpret_cast<const bf16x8_t*>(wbase + woff[j][kk]);
+  };
+  // fragment q of a step: X fragments 0..3, then W fragments 4..6
+  auto read_one = [&](int slot, int q, const uint8_t* xbase, const uint8_t* wbase, int kk) {
+    if (q < kSubM)
+      fa[slot][q] = *reinterpret_cast<const bf16x8_t*>(xbase + xoff[q][kk]);
+    else
+      fb[slot][q - kSubM] = *reinterpret_cast<const bf16x8_t*>(wbase + woff[q - kSubM][kk]);
   };
   auto mfma_step = [&](int slot) {
 #pragma unroll
@@ -259,74 +279,102 @@ __global__ __launch_bounds__(kThreads, 1) void kv_proj_kernel(const GemmArgs a) 
   constexpr int kMfma = kSubM * kSubN;           // MFMAs per step
   static_assert(kFrags == 7 && kMfma == 12, "schedule below is for 7 reads / 12 MFMAs");
 
-  issue_half(0, 0, 0);
-  issue_half(0, 0, 1);
-  issue_half(min(1, stages - 1), 1, 0);
-  issue_half(min(1, stages - 1), 1, 1);
+  issue_x(0, 0, 0, kXBlocks);
+  issue_w(0, 0, 0, kWBlocks);
+  issue_x(min(1, stages - 1), 1, 0, kXBlocks);
+  issue_w(min(1, stages - 1), 1, 0, kWBlocks);
   __builtin_amdgcn_s_waitcnt(0x0F7E);  // vmcnt(14): stage 0 has landed
   __syncthreads();
-  read_frags(0, lds, 0);
+  read_frags(0, lds, lds + kWBase, 0);
   auto do_stage = [&](auto R, int kb) {
     constexpr int r = decltype(R)::value;
     constexpr int sa = r % 3, sb = (r + 1) % 3, sc = (r + 2) % 3;
-    const int buf = kb & 1;
-    const uint8_t* base = lds + buf * kStageBytes;
+    const int wbuf = kb & 1;
+    const uint8_t* xbase = lds + r * kXStageBytes;
+    const uint8_t* wbase = lds + kWBase + wbuf * kWStageBytes;
+    const int ahead = min(kb + 2, stages - 1);
+    constexpr int xnext = (r + 2) % 3;
     // step 0
-    read_frags(sb, base, 1);
+    read_frags(sb, xbase, wbase, 1);
+    issue_x(ahead, xnext, 0, 4);
     mfma_step(sa);
 #pragma unroll
     for (int q = 0; q < kFrags; ++q) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedLdsRead, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, kMfma - kFrags, 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
     __builtin_amdgcn_sched_barrier(0);
     // step 1
-    read_frags(sc, base, 2);
-    read_frags(sa, base, 3);
+    // program order = issue order: the copies write LDS, so the compiler
+    // keeps them in place relative to the fragment reads
+#pragma unroll
+    for (int q = 0; q < 4; ++q) read_one(sc, q, xbase, wbase, 2);
+#pragma unroll
+    for (int q = 4; q < 7; ++q) {
+      read_one(sc, q, xbase, wbase, 2);
+      issue_x(ahead, xnext, q, q + 1);
+    }
+    read_one(sa, 0, xbase, wbase, 3);
+    issue_x(ahead, xnext, 7, 8);
+#pragma unroll
+    for (int q = 1; q < 7; ++q) read_one(sa, q, xbase, wbase, 3);
     mfma_step(sb);
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
     __builtin_amdgcn_sched_group_barrier(kSchedLdsRead, 2, 0);
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
     __builtin_amdgcn_sched_group_barrier(kSchedLdsRead, 2, 0);
 #pragma unroll
-    for (int q = 0; q < 10; ++q) {
+    for (int q = 0; q < 4; ++q) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedLdsRead, 1, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): stage kb + 1 has landed
-    __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
-    // step 2
-    issue_half(min(kb + 2, stages - 1), buf, 0);
-    mfma_step(sc);
-#pragma unroll
-    for (int q = 0; q < 7; ++q) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, kMfma - 7, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    // step 3
-    read_frags(sb, lds + (buf ^ 1) * kStageBytes, 0);
-    issue_half(min(kb + 2, stages - 1), buf, 1);
-    mfma_step(sa);
-    // the copies write LDS, so they stay behind the fragment reads
 #pragma unroll
-    for (int q = 0; q < 7; ++q) {
+    for (int q = 0; q < 6; ++q) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedLdsRead, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // stage kb + 1 has landed: only stage kb + 2's X copies (the last 8
+    // issued) may still be in flight
+    // and the fragment reads of stage kb have returned; a bare barrier, since
+    // __syncthreads() would also wait for those X copies
+    __builtin_amdgcn_s_waitcnt(0x0078);  // vmcnt(8) lgkmcnt(0)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_sched_barrier(0);
+    // step 2
+    issue_w(ahead, wbuf, 0, 3);
+    mfma_step(sc);
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, kMfma - 3, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // step 3
+    read_frags(sb, lds + ((r + 1) % 3) * kXStageBytes, lds + kWBase + (wbuf ^ 1) * kWStageBytes, 0);
+    issue_w(ahead, wbuf, 3, 6);
+    mfma_step(sa);
+#pragma unroll
+    for (int q = 0; q < 7; ++q) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedLdsRead, 1, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
   using R0 = std::integral_constant<int, 0>;
