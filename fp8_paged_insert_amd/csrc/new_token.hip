@@ -71,6 +71,12 @@ struct NewTokenArgs {
   uint32_t nope, vdim, kv_lora_rank;  // elements; multiples of 16
   uint32_t rows;                      // (token, head) tasks; the cache tasks follow
   uint32_t tasks;
+  uint32_t tokens;
+  // Grouped form (the MLA shape with heads a multiple of 16): wavefront
+  // tasks of 16 heads of one token (row_waves of them), then cache tasks of
+  // 4 tokens (one per 16-lane row), wave_tasks in all.
+  uint32_t grouped, row_waves, wave_tasks;
+  FastDiv hgroups;  // heads / 16
 };
 
 __device__ __forceinline__ float scale_or_one(const float* p) { return p ? p[0] : 1.0f; }
@@ -156,6 +162,90 @@ __global__ __launch_bounds__(256) void new_token_kernel(const NewTokenArgs a) {
   const uint32_t qf = sign_flip_of(qs), kf = sign_flip_of(ks), vf = sign_flip_of(vs),
                  cf = sign_flip_of(cs);
   const uint32_t width = a.nope + kRope;
+  // ---- one token's cache entry [kv_c | rotated k_pe] (one 16-lane row; a
+  // padded token, slot -1, skips the whole row)
+  auto cache_row = [&](uint32_t t) {
+    const int64_t slot = a.slots[t];
+    if (slot < 0) return;
+    const int64_t pos = min(max(a.positions[t], int64_t(0)), a.max_pos - 1);
+    const float* tab = a.cos_sin + pos * (2 * kRope) + 4 * (j & 7);
+    const uint4 cv = ld16(tab), sv = ld16(tab + kRope / 2);
+    const uint2 kpe = ld8(a.k_pe + int64_t(t) * a.kpe_ts + 4 * j);
+    const uint16_t* kc = a.kv_c + int64_t(t) * a.kvc_ts;
+    uint8_t* dst = static_cast<uint8_t*>(a.cache) + entry_offset(slot, a) * cb;
+    for (uint32_t c = j; c < a.kv_lora_rank / 8; c += kLanes)
+      put8<kCacheFmt, kNtStream>(dst + 8 * c * cb, ld16(kc + 8 * c), cs, cr, cf);
+    put4<kCacheFmt, kNtStream>(dst + (a.kv_lora_rank + 4 * j) * cb, rope4w(kpe, cv, sv, first, tab),
+                               cs, cr, cf);
+  };
+  if (kFp8 && a.grouped) {
+    // fp8 outputs, the MLA shape (nope = V width = 128), heads in groups of 16:
+    // wavefront task w < row_waves covers heads [16 q, 16 q + 16) of token
+    // w / G, q = w mod G (G = heads / 16); its 16-lane row r takes heads
+    // 16 q + r + 4 g for g = 0..3, so each step g of the wavefront covers 4
+    // consecutive heads.  The key's rope part is the token's rotated k_pe
+    // for every head: each row rotates and converts it once and stores the
+    // result for its 4 heads (per head, that rotation and conversion were
+    // about a sixth of the fp8 forms' ALU work: 142.8 -> 127.8 us scaled,
+    // 133.9 -> 126.6 us plain at 8192 x 64).  Wavefront tasks past
+    // row_waves are cache entries, one token per row.  The bf16 form is
+    // bound by HBM, not the ALU: grouped it was 2% slower, so it keeps one
+    // task per row (and is compiled without this path, which would raise
+    // its register count from 79 to 111).
+    const uint32_t r = (threadIdx.x / kLanes) & 3;
+    const uint32_t nw = (gridDim.x * blockDim.x) / 64;
+    for (uint32_t w = (blockIdx.x * blockDim.x + threadIdx.x) / 64; w < a.wave_tasks; w += nw) {
+      if (w >= a.row_waves) {
+        const uint32_t t = (w - a.row_waves) * 4 + r;
+        if (t < a.tokens) cache_row(t);
+        continue;
+      }
+      const uint32_t t = fdiv(w, a.hgroups);
+      const uint32_t h0 = (w - t * a.hgroups.d) * 16 + r;
+      const int64_t pos = min(max(a.positions[t], int64_t(0)), a.max_pos - 1);
+      const float* tab = a.cos_sin + pos * (2 * kRope) + 4 * (j & 7);
+      const uint4 cv = ld16(tab), sv = ld16(tab + kRope / 2);
+      const uint2 kpe = ld8(a.k_pe + int64_t(t) * a.kpe_ts + 4 * j);
+      uint2 krot = make_uint2(0, 0);
+      uint32_t kcode = 0;
+      // two batches of 2 heads: a batch's loads are issued before its first
+      // conversion (4 heads at once would need more than 128 VGPRs)
+#pragma unroll
+      for (int b = 0; b < 4; b += 2) {
+        uint4 xq[2], xk[2], xv[2];
+        uint2 qpe[2];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const int64_t h = h0 + 4 * (b + g);
+          xq[g] = ld16_once(a.q_nope + int64_t(t) * a.qn_ts + h * a.qn_hs + 8 * j);
+          xk[g] = ld16_once(a.k_nope + int64_t(t) * a.kn_ts + h * a.kn_hs + 8 * j);
+          if constexpr (kFp8) xv[g] = ld16_once(a.v + int64_t(t) * a.v_ts + h * a.v_hs + 8 * j);
+          qpe[g] = ld8(a.q_pe + int64_t(t) * a.qp_ts + h * a.qp_hs + 4 * j);
+        }
+        if (b == 0) {
+          krot = rope4w(kpe, cv, sv, first, tab);
+          if constexpr (kFp8) kcode = quant4<kScaled, false>(krot, ks, kr, kf);
+        }
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const int64_t task = int64_t(t) * a.heads.d + h0 + 4 * (b + g);
+          uint8_t* qo = static_cast<uint8_t*>(a.q_out) + task * width * ob;
+          uint8_t* ko = static_cast<uint8_t*>(a.key_out) + task * width * ob;
+          put8<kOut, kNtStream, kScaled>(qo + 8 * j * ob, xq[g], qs, qr, qf);
+          put8<kOut, kNtStream, kScaled>(ko + 8 * j * ob, xk[g], ks, kr, kf);
+          put4<kOut, kNtStream, kScaled>(qo + (128 + 4 * j) * ob,
+                                           rope4w(qpe[g], cv, sv, first, tab), qs, qr, qf);
+          if constexpr (kFp8) {
+            st4<kNtStream>(ko + 128 + 4 * j, kcode);
+            put8<kFmtE4M3, kNtStream, kScaled>(a.v_out + task * 128 + 8 * j, xv[g], vs, vr, vf);
+          } else {
+            st8<kNtStream>(ko + (128 + 4 * j) * 2, krot);
+          }
+        }
+      }
+    }
+    return;
+  }
   const uint32_t step = (gridDim.x * blockDim.x) / kLanes;
   for (uint32_t task = (blockIdx.x * blockDim.x + threadIdx.x) / kLanes; task < a.tasks;
        task += step) {
@@ -209,20 +299,7 @@ __global__ __launch_bounds__(256) void new_token_kernel(const NewTokenArgs a) {
           put8<kFmtE4M3, kNtStream, kScaled>(vo + 8 * c, ld16_once(vi + 8 * c), vs, vr, vf);
       }
     } else {
-      // ---- one token's cache entry [kv_c | rotated k_pe]
-      const uint32_t t = task - a.rows;
-      const int64_t slot = a.slots[t];
-      if (slot < 0) continue;  // padded token: the whole row skips
-      const int64_t pos = min(max(a.positions[t], int64_t(0)), a.max_pos - 1);
-      const float* tab = a.cos_sin + pos * (2 * kRope) + 4 * (j & 7);
-      const uint4 cv = ld16(tab), sv = ld16(tab + kRope / 2);
-      const uint2 kpe = ld8(a.k_pe + int64_t(t) * a.kpe_ts + 4 * j);
-      const uint16_t* kc = a.kv_c + int64_t(t) * a.kvc_ts;
-      uint8_t* dst = static_cast<uint8_t*>(a.cache) + entry_offset(slot, a) * cb;
-      for (uint32_t c = j; c < a.kv_lora_rank / 8; c += kLanes)
-        put8<kCacheFmt, kNtStream>(dst + 8 * c * cb, ld16(kc + 8 * c), cs, cr, cf);
-      put4<kCacheFmt, kNtStream>(dst + (a.kv_lora_rank + 4 * j) * cb, rope4w(kpe, cv, sv, first, tab),
-                                 cs, cr, cf);
+      cache_row(task - a.rows);
     }
   }
 }
@@ -344,6 +421,12 @@ extern "C" int32_t mla_new_token_epilogue(
   a.kv_lora_rank = static_cast<uint32_t>(kv_lora_rank);
   a.rows = static_cast<uint32_t>(rows);
   a.tasks = static_cast<uint32_t>(tasks);
+  a.tokens = static_cast<uint32_t>(num_tokens);
+  const bool grouped = fp8 && nope == 128 && vdim == 128 && num_heads > 0 && num_heads % 16 == 0;
+  a.grouped = grouped;
+  a.hgroups = make_fastdiv(static_cast<uint32_t>(grouped ? num_heads / 16 : 1));
+  a.row_waves = static_cast<uint32_t>(grouped ? rows / 16 : 0);
+  a.wave_tasks = static_cast<uint32_t>(grouped ? rows / 16 + (cache ? ceil_div(num_tokens, 4) : 0) : 0);
   // Default grid: one 16-lane row per task for bf16 outputs; for fp8 outputs
   // 4 workgroups per CU looping over the tasks, so each wavefront's per-launch
   // set-up (the scales' reciprocals by IEEE division, when scaled) is paid once
@@ -351,7 +434,7 @@ extern "C" int32_t mla_new_token_epilogue(
   // path: scaled 141.8 us on the full grid against 132.2 us, plain 131.3
   // against 128.6 us.
   const bool scaled = fp8 && (q_scale || k_scale || v_scale);
-  const int64_t full = ceil_div(tasks * kLanes, 256);
+  const int64_t full = grouped ? ceil_div(int64_t(a.wave_tasks) * 64, 256) : ceil_div(tasks * kLanes, 256);
   const int64_t dflt = fp8 ? std::min(full, int64_t(4) * cu_count()) : full;
   const dim3 g(max_blocks > 0 ? std::min(full, max_blocks) : dflt), b(256);
   const int fmt = cache ? cache_fmt(cache_dtype) : kFmtBf16;

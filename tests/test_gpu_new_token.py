@@ -13,9 +13,10 @@ differ in their last bits and that moves a rounding);
 their fp8 codes are identical wherever the GPU's bf16 rotation equals the
 oracle's, else within one code.  Workloads: strided views of the model's tensors (query
 [T, H, 192], kv_b_proj output [T, H, 256], latent row [T, 576]), 1 to 300
-tokens and 1 to 16 heads with a padded token, both output modes and all
-three cache formats, the full 8192-token x 64-head prefill (every token), a
-capped grid, and a cache-only call.
+tokens and 1 to 32 heads with a padded token, both output modes and all
+three cache formats (fp8 outputs with heads a multiple of 16 run the grouped
+form), the full 8192-token x 64-head prefill (every token), capped grids of
+both forms, and a cache-only call.
 """
 import numpy as np
 import pytest
@@ -185,6 +186,10 @@ CASES = [  # (seed, T, H, cache format, fp8 outputs)
     (37, 130, 4, "e5m2", True),
     (38, 300, 16, "e4m3", True),
     (39, 300, 16, "bf16", False),
+    # fp8 outputs with heads a multiple of 16 take the grouped form (16 heads
+    # per wavefront); 77 tokens leave the last cache wavefront 1 row of 4
+    (42, 77, 32, "e5m2", True),
+    (43, 45, 16, "bf16", True),
 ]
 
 
@@ -210,9 +215,13 @@ def test_full_prefill(mk, fp8):
     check_case(mk, Case(8, 8192, 64, "e4m3", num_blocks=512), fp8)
 
 
-def test_capped_grid_and_cache_only(mk):
-    announce("new-token epilogue capped grid / cache only")
-    case = Case(41, 200, 8, "e4m3")
+@pytest.mark.parametrize("H", [8, 16])
+def test_capped_grid_and_cache_only(mk, H):
+    """A capped grid gives the same bytes as the default one (8 heads: one
+    task per 16-lane row; 16 heads: the grouped form), and num_heads = 0
+    runs only the cache insert."""
+    announce("new-token epilogue capped grid / cache only", H)
+    case = Case(41, 201, H, "e4m3")
     a = case.run_gpu(mk, True)
     b = case.run_gpu(mk, True, max_blocks=7)
     for x, y in zip(a, b):
