@@ -427,15 +427,17 @@ extern "C" int32_t mla_new_token_epilogue(
   a.hgroups = make_fastdiv(static_cast<uint32_t>(grouped ? num_heads / 16 : 1));
   a.row_waves = static_cast<uint32_t>(grouped ? rows / 16 : 0);
   a.wave_tasks = static_cast<uint32_t>(grouped ? rows / 16 + (cache ? ceil_div(num_tokens, 4) : 0) : 0);
-  // Default grid: one 16-lane row per task for bf16 outputs; for fp8 outputs
-  // 4 workgroups per CU looping over the tasks, so each wavefront's per-launch
-  // set-up (the scales' reciprocals by IEEE division, when scaled) is paid once
-  // per ~30 tasks.  Measured at 8192 x 64 with the straight-line MLA-shape
-  // path: scaled 141.8 us on the full grid against 132.2 us, plain 131.3
-  // against 128.6 us.
+  // Default grid: the full grid (one task per 16-lane row, or one grouped
+  // task per wavefront) except for fp8 outputs in the ungrouped form, which
+  // run 4 workgroups per CU looping over the tasks, so each wavefront's
+  // per-launch set-up (the scales' reciprocals by IEEE division, when
+  // scaled) is paid once per ~30 tasks.  Measured at 8192 x 64: ungrouped,
+  // scaled 141.8 us on the full grid against 132.2 us, plain 131.3 against
+  // 128.6 us; grouped (16 heads per task), the full grid is fastest: 120.3
+  // and 120.9 us plain and scaled against 126.6 and 127.7 us at 4 per CU.
   const bool scaled = fp8 && (q_scale || k_scale || v_scale);
   const int64_t full = grouped ? ceil_div(int64_t(a.wave_tasks) * 64, 256) : ceil_div(tasks * kLanes, 256);
-  const int64_t dflt = fp8 ? std::min(full, int64_t(4) * cu_count()) : full;
+  const int64_t dflt = fp8 && !grouped ? std::min(full, int64_t(4) * cu_count()) : full;
   const dim3 g(max_blocks > 0 ? std::min(full, max_blocks) : dflt), b(256);
   const int fmt = cache ? cache_fmt(cache_dtype) : kFmtBf16;
   auto s = static_cast<hipStream_t>(stream);
