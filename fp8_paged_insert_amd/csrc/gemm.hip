@@ -34,12 +34,10 @@
 //    buffers each) measured 2% slower, under step 3 alone 10% slower;
 //  * tiles are grouped per XCD so the workgroups sharing an L2 share their
 //    X and W blocks;
-//  * up to 16 extra workgroups, on compute units the tiles leave idle (16
-//    of 256 for the default problem), read one dword of every upcoming
-//    K stage's row segments so X and W arrive in the last-level cache ahead
-//    of the tile workgroups: with operands that start in HBM (a cache
-//    flushed by other work) this saved about 20 us of the launch (165 ->
-//    145 us when it was added), with operands already cached nothing;
+//  * no cache-warming workgroups on the CUs the tiles leave idle: with the
+//    copies spread over whole stages they made the launch 1.2 us slower
+//    (earlier, with every copy after the barrier, they saved about 20 us of
+//    a launch whose operands start in HBM);
 //  * the finished tile is rounded to bf16 into LDS (over the stage buffers)
 //    and written out in 16-byte chunks along its rows: 24 store
 //    instructions per lane that cover whole 128-byte lines of Y, instead of
@@ -81,11 +79,6 @@ constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, one L2 each
 constexpr int kMaxLdsDevices = 64;  // devices whose LDS attribute is remembered
 constexpr int kGroupRows = 4;
 
-// Workgroups that only warm the last-level cache (see prefetch_operands):
-// at most this many, and only on compute units the tiles leave idle.
-constexpr int kPrefetchWgs = 16;
-constexpr int kPrefetchFirst = 2;    // first K stage they touch
-constexpr int kPrefetchBatch = 16;   // loads in flight per lane
 
 struct GemmArgs {
   const uint16_t* x;
@@ -94,8 +87,6 @@ struct GemmArgs {
   int64_t ldx, ldy;
   int32_t T, K, N;
   int32_t tiles_n, tiles, tiles_per_xcd;
-  int32_t compute_blocks;  // tiles_per_xcd * kXcds; blocks past these prefetch
-  int32_t pf_blocks;       // number of prefetching workgroups (0 = none)
 };
 
 // The 16-byte chunk c of tile row r sits in LDS slot c ^ swz(r) of that row.
@@ -110,54 +101,8 @@ __device__ __forceinline__ void copy_to_lds(const uint16_t* src, uint8_t* dst) {
   __builtin_amdgcn_global_load_lds((global_void_t*)src, (lds_void_t*)dst, 16, 0, 0);
 }
 
-// Cache warming by the workgroups past the tiles.  With one tile per compute
-// unit a launch leaves some units idle (240 tiles for the 4096 x 2880
-// output on 256 units).  Those units walk the operands in K-stage order, from
-// stage kPrefetchFirst on, loading the first dword of every stage's 128-byte
-// segment of every X and W row, so the lines are fetched from HBM into the
-// last-level cache before the tile workgroups ask for them (a segment that
-// straddles two lines has its second line touched by the next stage's load).
-// Nothing waits on these workgroups and nothing they read is used: they only
-// decide which cache level serves the tile workgroups' copies.  Each lane
-// computes a batch of addresses, issues the batch's loads back to back and
-// folds the values into a word that is stored only under a condition the
-// host never allows (T < 0), which keeps the loads in the program.  The host
-// keeps pf_blocks * kThreads <= T + N, so one wrap per advance suffices.
-__device__ __forceinline__ void prefetch_operands(const GemmArgs& a, int p) {
-  const int64_t rows = int64_t(a.T) + a.N;  // a stage's row segments: X rows, then W rows
-  const int64_t step = int64_t(a.pf_blocks) * kThreads;
-  const int stages = a.K / kBK;
-  int64_t r = int64_t(p) * kThreads + threadIdx.x;
-  int kb = kPrefetchFirst;
-  uint32_t sink = 0;
-  while (kb < stages) {
-    const uint32_t* src[kPrefetchBatch];
-#pragma unroll
-    for (int u = 0; u < kPrefetchBatch; ++u) {
-      const int k = min(kb, stages - 1);
-      const uint16_t* row = r < a.T ? a.x + r * a.ldx : a.w + (r - a.T) * a.K;
-      src[u] = reinterpret_cast<const uint32_t*>(row + k * kBK);
-      r += step;
-      if (r >= rows) {
-        r -= rows;
-        ++kb;
-      }
-    }
-    uint32_t v[kPrefetchBatch];
-#pragma unroll
-    for (int u = 0; u < kPrefetchBatch; ++u) v[u] = *src[u];
-#pragma unroll
-    for (int u = 0; u < kPrefetchBatch; ++u) sink ^= v[u];
-  }
-  if (a.T < 0) a.y[threadIdx.x] = static_cast<uint16_t>(sink);
-}
-
 __global__ __launch_bounds__(kThreads, 1) void kv_proj_kernel(const GemmArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];   // [3][kBM rows], then [2][kBN rows], of 128 B
-  if (static_cast<int>(blockIdx.x) >= a.compute_blocks) {
-    prefetch_operands(a, blockIdx.x - a.compute_blocks);
-    return;
-  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -462,13 +407,7 @@ extern "C" int32_t mla_ctx_kv_proj(const void* X, int64_t x_row_stride, int64_t 
   const int64_t tiles = ceil_div(T, kBM) * a.tiles_n;
   a.tiles = static_cast<int32_t>(tiles);
   a.tiles_per_xcd = static_cast<int32_t>(ceil_div(tiles, kXcds));
-  a.compute_blocks = a.tiles_per_xcd * kXcds;
-  // prefetching workgroups only on compute units the tiles leave idle, and
-  // no more lanes than a stage has row segments (T + N)
-  a.pf_blocks = static_cast<int32_t>(std::max<int64_t>(
-      0, std::min<int64_t>({kPrefetchWgs, cu_count() - a.compute_blocks, (T + N) / kThreads})));
-  if (K / kBK <= kPrefetchFirst) a.pf_blocks = 0;
-  const int64_t grid = int64_t(a.compute_blocks) + a.pf_blocks;
+  const int64_t grid = int64_t(a.tiles_per_xcd) * kXcds;  // blocks past the tiles return
   // The LDS reservation is a per-device attribute of the kernel: set it once
   // on each device the projection runs on.
   static int attr_set[kMaxLdsDevices] = {0};

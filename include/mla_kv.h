@@ -235,9 +235,6 @@ int32_t mla_ctx_kv_epilogue(
  * Y device bf16 [T, N] row-major (row stride y_row_stride).
  * K must be a multiple of 64 and N a multiple of 16; pointers and row
  * strides 16-byte aligned.  T may be any value >= 0.
- * When the output tiles leave compute units idle, the launch adds up to 16
- * workgroups that only read X and W ahead of the tile workgroups (warming
- * the last-level cache); they write nothing, and nothing waits on them.
  * ------------------------------------------------------------------------ */
 int32_t mla_ctx_kv_proj(const void* X, int64_t x_row_stride, int64_t T,
                         int64_t K, const void* W, int64_t N, void* Y,

@@ -2,8 +2,8 @@
 
 A serving loop captures its per-step kernels once and replays them with new
 inputs copied into the same buffers.  The captured step here is a KV-only
-projection (300 x 512 . 512 x 576: eight K stages, so its cache-warming
-workgroups run too), a grouped fp8 insert (5 layers x 4 tokens), a new-token
+projection (300 x 512 . 512 x 576: eight K stages, so its three-buffer
+LDS ring wraps), a grouped fp8 insert (5 layers x 4 tokens), a new-token
 epilogue (4 tokens x 8 heads, fp8 outputs, fp8 cache) and a chunk merge
 (4 tokens x 8 heads x 128).  Every
 replay runs on fresh inputs written eagerly between replays, and its results

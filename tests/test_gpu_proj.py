@@ -75,8 +75,8 @@ def test_proj_one_hot_columns_exact(mk):
 
 @pytest.mark.parametrize("K", [128, 512])
 def test_proj_strided_rows(mk, K):
-    """X with a padded row stride; at K = 512 the cache-warming workgroups
-    (K stages from the third on) also read X through that stride."""
+    """X with a padded row stride (two and eight K stages: the three-buffer X
+    ring wraps at K = 512)."""
     announce("proj strided", K)
     g = torch.Generator().manual_seed(10)
     T, N = 200, 96
@@ -90,9 +90,8 @@ def test_proj_strided_rows(mk, K):
 
 def test_proj_more_tiles_than_compute_units(mk):
     """4400 x 256 . 256 x 2880: 18 x 15 = 270 tiles, more than the 256 compute
-    units, so no cache-warming workgroups run and some tiles start in a second
-    round; the last tile row is ragged (4400 = 17 * 256 + 48).  Every output
-    against the oracle."""
+    units, so some tiles start in a second round; the last tile row is ragged
+    (4400 = 17 * 256 + 48).  Every output against the oracle."""
     announce("proj 270 tiles")
     g = torch.Generator().manual_seed(12)
     T, K, N = 4400, 256, 2880
