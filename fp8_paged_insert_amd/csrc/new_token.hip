@@ -186,8 +186,8 @@ __global__ __launch_bounds__(256) void new_token_kernel(const NewTokenArgs a) {
     // consecutive heads.  The key's rope part is the token's rotated k_pe
     // for every head: each row rotates and converts it once and stores the
     // result for its 4 heads (per head, that rotation and conversion were
-    // about a sixth of the fp8 forms' ALU work: 142.8 -> 127.8 us scaled,
-    // 133.9 -> 126.6 us plain at 8192 x 64).  Wavefront tasks past
+    // about a sixth of the fp8 forms' ALU work; with the full grid, 142.8 ->
+    // 120.0 us scaled, 133.9 -> 119.6 us plain at 8192 x 64).  Wavefront tasks past
     // row_waves are cache entries, one token per row.  The bf16 form is
     // bound by HBM, not the ALU: grouped it was 2% slower, so it keeps one
     // task per row (and is compiled without this path, which would raise
@@ -206,7 +206,6 @@ __global__ __launch_bounds__(256) void new_token_kernel(const NewTokenArgs a) {
       const float* tab = a.cos_sin + pos * (2 * kRope) + 4 * (j & 7);
       const uint4 cv = ld16(tab), sv = ld16(tab + kRope / 2);
       const uint2 kpe = ld8(a.k_pe + int64_t(t) * a.kpe_ts + 4 * j);
-      uint2 krot = make_uint2(0, 0);
       uint32_t kcode = 0;
       // two batches of 2 heads: a batch's loads are issued before its first
       // conversion (4 heads at once would need more than 128 VGPRs)
@@ -219,28 +218,21 @@ __global__ __launch_bounds__(256) void new_token_kernel(const NewTokenArgs a) {
           const int64_t h = h0 + 4 * (b + g);
           xq[g] = ld16_once(a.q_nope + int64_t(t) * a.qn_ts + h * a.qn_hs + 8 * j);
           xk[g] = ld16_once(a.k_nope + int64_t(t) * a.kn_ts + h * a.kn_hs + 8 * j);
-          if constexpr (kFp8) xv[g] = ld16_once(a.v + int64_t(t) * a.v_ts + h * a.v_hs + 8 * j);
+          xv[g] = ld16_once(a.v + int64_t(t) * a.v_ts + h * a.v_hs + 8 * j);
           qpe[g] = ld8(a.q_pe + int64_t(t) * a.qp_ts + h * a.qp_hs + 4 * j);
         }
-        if (b == 0) {
-          krot = rope4w(kpe, cv, sv, first, tab);
-          if constexpr (kFp8) kcode = quant4<kScaled, false>(krot, ks, kr, kf);
-        }
+        if (b == 0) kcode = quant4<kScaled, false>(rope4w(kpe, cv, sv, first, tab), ks, kr, kf);
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
           const int64_t task = int64_t(t) * a.heads.d + h0 + 4 * (b + g);
-          uint8_t* qo = static_cast<uint8_t*>(a.q_out) + task * width * ob;
-          uint8_t* ko = static_cast<uint8_t*>(a.key_out) + task * width * ob;
-          put8<kOut, kNtStream, kScaled>(qo + 8 * j * ob, xq[g], qs, qr, qf);
-          put8<kOut, kNtStream, kScaled>(ko + 8 * j * ob, xk[g], ks, kr, kf);
-          put4<kOut, kNtStream, kScaled>(qo + (128 + 4 * j) * ob,
-                                           rope4w(qpe[g], cv, sv, first, tab), qs, qr, qf);
-          if constexpr (kFp8) {
-            st4<kNtStream>(ko + 128 + 4 * j, kcode);
-            put8<kFmtE4M3, kNtStream, kScaled>(a.v_out + task * 128 + 8 * j, xv[g], vs, vr, vf);
-          } else {
-            st8<kNtStream>(ko + (128 + 4 * j) * 2, krot);
-          }
+          uint8_t* qo = static_cast<uint8_t*>(a.q_out) + task * width;
+          uint8_t* ko = static_cast<uint8_t*>(a.key_out) + task * width;
+          put8<kFmtE4M3, kNtStream, kScaled>(qo + 8 * j, xq[g], qs, qr, qf);
+          put8<kFmtE4M3, kNtStream, kScaled>(ko + 8 * j, xk[g], ks, kr, kf);
+          put4<kFmtE4M3, kNtStream, kScaled>(qo + 128 + 4 * j, rope4w(qpe[g], cv, sv, first, tab),
+                                             qs, qr, qf);
+          st4<kNtStream>(ko + 128 + 4 * j, kcode);
+          put8<kFmtE4M3, kNtStream, kScaled>(a.v_out + task * 128 + 8 * j, xv[g], vs, vr, vf);
         }
       }
     }
