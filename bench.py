@@ -133,22 +133,20 @@ class LongContext:
         self.ws2 = [torch.empty(chunk, W, dtype=torch.bfloat16, device=dev) for _ in range(2)]
         self.key = torch.empty(chunk, heads, 192, dtype=torch.uint8, device=dev)
         self.v8 = torch.empty(chunk, heads, 128, dtype=torch.uint8, device=dev)
-        self.pack_events = []
+        self.pack_windows = []
 
-    # One timed step in this many records the events of one joint launch:
-    # each pair of launch events costs the step about 6 us on MI355X (the
-    # step without them measured 1.238-1.247 ms, with them on every step
-    # 1.244-1.247 ms, on one box), so they are taken on every other timed
-    # step, the timed chunk advancing by 4 (of 15) each time so that the
-    # samples spread over the chunk loop.
-    EVENT_EVERY = 2
-    CHUNK_STRIDE = 4
+    # Timed steps record a pair of HIP events on the stream around their 15
+    # back-to-back joint launches (one event before the first, one after the
+    # last), so the window's length / 15 is the joint launch's average
+    # duration, the gaps between the launches included.  Events recorded by
+    # a launch itself around one joint launch read about 2.5 us longer than
+    # the profiler's duration of that kernel.
+    EVENT_EVERY = 1
 
     def arm_timing(self, steps):
-        """Create the HIP events the timed packs will record into."""
+        """Create the HIP events the timed windows will record into."""
         torch = self.torch
         n = (steps + self.EVENT_EVERY - 1) // self.EVENT_EVERY
-        self.timed_chunk = -self.CHUNK_STRIDE
         self.timed_steps = 0
         self.event_pool = []
         for _ in range(n):
@@ -169,32 +167,33 @@ class LongContext:
         grouped insert, then the chunk loop with the joint launch -- gather of
         chunk 0, then for every chunk c the pack of c together with the gather
         of c + 1 into the other workspace (the last chunk packs alone).  With
-        time_pack, one joint launch in every EVENT_EVERY-th step (the chunk
-        index advancing by CHUNK_STRIDE) records its own start and end events.  max_blocks > 0
-        caps the pack's grid (grid-stride loop)."""
+        time_pack, every EVENT_EVERY-th step records a pair of events on the
+        stream around its joint launches.  max_blocks > 0 caps the pack's grid
+        (grid-stride loop)."""
         mk = self.mk
         mk.mla_kv_insert_grouped(self.kv_c, self.k_pe, self.ptrs, self.slots, 64, 64 * W, W,
                                  self.scales, "fp8")
         n = len(self.kvb)
+        window = None
         if time_pack:
-            time_pack = self.timed_steps % self.EVENT_EVERY == 0
+            if self.timed_steps % self.EVENT_EVERY == 0:
+                window = self.event_pool.pop()
             self.timed_steps += 1
-        if time_pack:
-            self.timed_chunk = (self.timed_chunk + self.CHUNK_STRIDE) % (n - 1)
         mk.mla_ctx_latent_gather(self.ctx_cache, self.src_slots[:self.chunk], self.ws2[0],
                                  self.ctx_scale, "fp8")
         for c, kvb in enumerate(self.kvb):
             ws = self.ws2[c % 2]
             if c + 1 < n:
-                if time_pack and c == self.timed_chunk:
-                    e0, e1 = self.event_pool.pop()
-                    mk.set_launch_events(e0, e1)
-                    self.pack_events.append((e0, e1))
+                if window is not None and c == 0:
+                    window[0].record()
                 nxt = self.src_slots[(c + 1) * self.chunk:(c + 2) * self.chunk]
                 mk.mla_ctx_kv_pack_gather(kvb[..., :128], ws[:, 512:], self.key, self.ctx_cache,
                                           nxt, self.ws2[(c + 1) % 2], v=kvb[..., 128:],
                                           v_out=self.v8, mode=mk.MLA_PACK_KEY_V_FP8,
                                           cache_scale=self.ctx_scale, max_blocks=max_blocks)
+                if window is not None and c == n - 2:
+                    window[1].record()
+                    self.pack_windows.append(window)
             else:
                 mk.mla_ctx_kv_pack(kvb[..., :128], ws[:, 512:], self.key, v=kvb[..., 128:],
                                    v_out=self.v8, mode=mk.MLA_PACK_KEY_V_FP8,
@@ -970,20 +969,21 @@ def main():
     nbytes = wl.bytes_per_step()
     value = nbytes * args.steps / secs / 1e9
 
-    joint_us = statistics.mean(e0.elapsed_time(e1) * 1e3 for e0, e1 in wl.pack_events)
+    per_window = len(wl.kvb) - 1
+    joint_us = statistics.mean(e0.elapsed_time(e1) * 1e3 / per_window for e0, e1 in wl.pack_windows)
     joint_b = pack_fp8_bytes(wl.chunk, wl.heads) + gather_bytes(wl.chunk)
     achieved = joint_b / joint_us / 1e3
     roofline = {"bound": "hbm", "kernel": "pack_gather_kernel",
                 "launch": "fp8 full-key + V pack of one 8192-token x 64-head chunk and the "
                           "dequantising gather of the next chunk's 8192 latent rows",
                 "achieved": round(achieved, 1),
-                "timing": "HIP events recorded by the kernel launch itself (start/stop of its "
-                          f"execution) on one joint launch in every {LongContext.EVENT_EVERY}nd "
-                          "timed step, the chunk index advancing by "
-                          f"{LongContext.CHUNK_STRIDE} of 15 each time",
+                "timing": "HIP events recorded on the launch stream before the first and "
+                          "after the last of the 15 back-to-back joint launches of every timed "
+                          "step; the window / 15 (the gaps between launches included)",
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(), "bytes_per_launch": joint_b,
-                "avg_launch_us": round(joint_us, 2), "launches": len(wl.pack_events)}
+                "avg_launch_us": round(joint_us, 2),
+                "launches": len(wl.pack_windows) * per_window}
 
     result = {
         "metric": "grouped MLA KV insert/pack: effective HBM GB/s (% of peak); "
