@@ -246,11 +246,22 @@ struct PackFp8 {
   }
 };
 
-// Chunks first, first + stride, ... below a.total.
+// Chunks first, first + stride, ... below a.total, software-pipelined: the
+// next chunk's loads are issued before the current chunk is converted and
+// stored (the compiler cannot move them above that store by itself, since
+// it cannot rule out aliasing), so with a capped grid a thread keeps its
+// next loads in flight while it converts.
 template <class Op>
 __device__ __forceinline__ void pack_loop(const PackArgs& a, const Op& op, uint32_t first,
                                           uint32_t stride) {
-  for (uint32_t item = first; item < a.total; item += stride) op.store(a, op.load(a, item));
+  if (first >= a.total) return;
+  auto cur = op.load(a, first);
+  for (uint32_t item = first + stride; item < a.total; item += stride) {
+    const auto nxt = op.load(a, item);
+    op.store(a, cur);
+    cur = nxt;
+  }
+  op.store(a, cur);
 }
 
 template <class Op>
