@@ -434,9 +434,12 @@ int32_t mla_ctx_neutralize_partials(void* out, int64_t out_tok_stride, int64_t o
  *             non-negative slots inside the cache, or -1 (precondition).
  * rope must be 64; nope, vdim and kv_lora_rank multiples
  * of 16; addresses and strides (in bytes) 16-byte aligned.  num_heads may be
- * 0 (cache insert only).  max_blocks caps the grid (0 = one item per thread);
- * the kernel loops grid-stride.  Host-side validation happens before any
- * launch, so a rejected call writes nothing.
+ * 0 (cache insert only).  max_blocks caps the grid (0 = the library's
+ * default: the full grid -- one (token, head) task per 16-lane row, or, for
+ * fp8 outputs with nope = vdim = 128 and heads a multiple of 16, one task of
+ * 16 heads per wavefront -- except fp8 outputs of other shapes, which run 4
+ * workgroups per CU); the kernel loops grid-stride.  Host-side validation
+ * happens before any launch, so a rejected call writes nothing.
  * ------------------------------------------------------------------------ */
 int32_t mla_new_token_epilogue(
     const void* q_nope, int64_t qn_tok_stride, int64_t qn_head_stride, const void* q_pe,
