@@ -234,7 +234,9 @@ int32_t mla_ctx_kv_epilogue(
  *   it once with mla_transpose_bf16 (rows K, cols N).
  * Y device bf16 [T, N] row-major (row stride y_row_stride).
  * K must be a multiple of 64 and N a multiple of 16; pointers and row
- * strides 16-byte aligned.  T may be any value >= 0.
+ * strides 16-byte aligned.  T may be any value >= 0.  The kernel addresses
+ * a 256-row tile of X by 32-bit byte offsets: 255 * x_row_stride + K must
+ * stay below 2^30 elements (else MLA_ERR_UNSUPPORTED).
  * ------------------------------------------------------------------------ */
 int32_t mla_ctx_kv_proj(const void* X, int64_t x_row_stride, int64_t T,
                         int64_t K, const void* W, int64_t N, void* Y,

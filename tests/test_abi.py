@@ -374,6 +374,17 @@ def test_sizes_beyond_one_launch_are_refused_before_launching(mk):
     assert mk.lib().mla_ctx_kv_proj(P16, 7168, big, 7168, P16, 2880, P16, 2880,
                                     None) == mk.MLA_ERR_UNSUPPORTED
     assert "beyond 2^31" in mk.last_error()
+    # the projection's tile copies use 32-bit byte offsets: a 256-row tile of X
+    # spanning 2 GiB (a row stride of about 4.2M elements, or K that large) is
+    # refused (W's 192-row tiles span less, since X's stride is at least K)
+    span = (1 << 30) // 255
+    assert mk.lib().mla_ctx_kv_proj(P16, span + 64, 4, 64, P16, 16, P16, 16,
+                                    None) == mk.MLA_ERR_UNSUPPORTED
+    assert "2 GiB" in mk.last_error()
+    big_k = (1 << 30) // 256 // 64 * 64 + 64
+    assert mk.lib().mla_ctx_kv_proj(P16, big_k, 4, big_k, P16, 16, P16, 16,
+                                    None) == mk.MLA_ERR_UNSUPPORTED
+    assert "2 GiB" in mk.last_error()
     # just inside the limits the same calls pass validation (T = 0 variants are no-ops)
     assert pack_call(mk, T=0) == mk.MLA_OK
 
