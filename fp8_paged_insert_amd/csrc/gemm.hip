@@ -188,14 +188,17 @@ __global__ __launch_bounds__(kThreads, 1) void kv_proj_kernel(const GemmArgs a) 
   auto frag_off = [&](int row, int kk) {
     return row * kRowBytes + (((2 * kk + hi) ^ swz(row)) << 4);
   };
-  int xoff[kSubM][kBK / 16], woff[kSubN][kBK / 16];
+  int xoff[kSubM][kBK / 16], xoff2[kSubM][kBK / 16], woff[kSubN][kBK / 16];
 #pragma unroll
   for (int kk = 0; kk < kBK / 16; ++kk) {
 #pragma unroll
-    for (int i = 0; i < kSubM; ++i) xoff[i][kk] = frag_off(wm * kWaveM + i * 32 + (lane & 31), kk);
+    for (int i = 0; i < kSubM; ++i) {
+      xoff[i][kk] = frag_off(wm * kWaveM + i * 32 + (lane & 31), kk);
+      xoff2[i][kk] = xoff[i][kk] + 2 * kXStageBytes;
+    }
 #pragma unroll
     for (int j = 0; j < kSubN; ++j)
-      woff[j][kk] = frag_off(wn * kWaveN + j * 32 + (lane & 31), kk);
+      woff[j][kk] = kWBase + frag_off(wn * kWaveN + j * 32 + (lane & 31), kk);
   }
 
   // Pipeline, per stage kb computed from X buffer kb % 3 and W buffer
@@ -215,20 +218,32 @@ __global__ __launch_bounds__(kThreads, 1) void kv_proj_kernel(const GemmArgs a) 
   // stage's barrier.
   const int stages = a.K / kBK;
   bf16x8_t fa[3][kSubM], fb[3][kSubN];
-  auto read_frags = [&](int slot, const uint8_t* xbase, const uint8_t* wbase, int kk) {
+  // X fragment i of X buffer xb, W fragment j of W buffer wb.  The K loop
+  // is unrolled by six stages, so both buffer indices are compile-time
+  // constants, and every read's buffer base fits the ds_read immediate
+  // (below 64 KiB): X buffers 0 and 1 directly, X buffer 2 through xoff2
+  // (its base folded in), the W buffers through woff (the W region's base
+  // folded in).  No read needs a vector add (0.6% faster than one add per
+  // read of X buffer 2 and of every W buffer).
+  auto xfrag = [&](int xb, int i, int kk) {
+    return xb == 2 ? *reinterpret_cast<const bf16x8_t*>(lds + xoff2[i][kk])
+                   : *reinterpret_cast<const bf16x8_t*>(lds + xb * kXStageBytes + xoff[i][kk]);
+  };
+  auto wfrag = [&](int wb, int j, int kk) {
+    return *reinterpret_cast<const bf16x8_t*>(lds + wb * kWStageBytes + woff[j][kk]);
+  };
+  auto read_frags = [&](int slot, int xb, int wb, int kk) {
 #pragma unroll
-    for (int i = 0; i < kSubM; ++i)
-      fa[slot][i] = *reinterpret_cast<const bf16x8_t*>(xbase + xoff[i][kk]);
+    for (int i = 0; i < kSubM; ++i) fa[slot][i] = xfrag(xb, i, kk);
 #pragma unroll
-    for (int j = 0; j < kSubN; ++j)
-      fb[slot][j] = *reinterpret_cast<const bf16x8_t*>(wbase + woff[j][kk]);
+    for (int j = 0; j < kSubN; ++j) fb[slot][j] = wfrag(wb, j, kk);
   };
   // fragment q of a step: X fragments 0..3, then W fragments 4..6
-  auto read_one = [&](int slot, int q, const uint8_t* xbase, const uint8_t* wbase, int kk) {
+  auto read_one = [&](int slot, int q, int xb, int wb, int kk) {
     if (q < kSubM)
-      fa[slot][q] = *reinterpret_cast<const bf16x8_t*>(xbase + xoff[q][kk]);
+      fa[slot][q] = xfrag(xb, q, kk);
     else
-      fb[slot][q - kSubM] = *reinterpret_cast<const bf16x8_t*>(wbase + woff[q - kSubM][kk]);
+      fb[slot][q - kSubM] = wfrag(wb, q - kSubM, kk);
   };
   auto mfma_step = [&](int slot) {
 #pragma unroll
@@ -248,17 +263,15 @@ __global__ __launch_bounds__(kThreads, 1) void kv_proj_kernel(const GemmArgs a) 
   issue_w(min(1, stages - 1), 1, 0, kWBlocks);
   __builtin_amdgcn_s_waitcnt(0x0F7E);  // vmcnt(14): stage 0 has landed
   __syncthreads();
-  read_frags(0, lds, lds + kWBase, 0);
+  read_frags(0, 0, 0, 0);
   auto do_stage = [&](auto R, int kb) {
     constexpr int r = decltype(R)::value;
     constexpr int sa = r % 3, sb = (r + 1) % 3, sc = (r + 2) % 3;
-    const int wbuf = kb & 1;
-    const uint8_t* xbase = lds + r * kXStageBytes;
-    const uint8_t* wbase = lds + kWBase + wbuf * kWStageBytes;
+    constexpr int xbuf = r % 3, wbuf = r % 2;
     const int ahead = min(kb + 2, stages - 1);
     constexpr int xnext = (r + 2) % 3;
     // step 0
-    read_frags(sb, xbase, wbase, 1);
+    read_frags(sb, xbuf, wbuf, 1);
     issue_x(ahead, xnext, 0, 4);
     mfma_step(sa);
 #pragma unroll
@@ -277,16 +290,16 @@ __global__ __launch_bounds__(kThreads, 1) void kv_proj_kernel(const GemmArgs a) 
     // program order = issue order: the copies write LDS, so the compiler
     // keeps them in place relative to the fragment reads
 #pragma unroll
-    for (int q = 0; q < 4; ++q) read_one(sc, q, xbase, wbase, 2);
+    for (int q = 0; q < 4; ++q) read_one(sc, q, xbuf, wbuf, 2);
 #pragma unroll
     for (int q = 4; q < 7; ++q) {
-      read_one(sc, q, xbase, wbase, 2);
+      read_one(sc, q, xbuf, wbuf, 2);
       issue_x(ahead, xnext, q, q + 1);
     }
-    read_one(sa, 0, xbase, wbase, 3);
+    read_one(sa, 0, xbuf, wbuf, 3);
     issue_x(ahead, xnext, 7, 8);
 #pragma unroll
-    for (int q = 1; q < 7; ++q) read_one(sa, q, xbase, wbase, 3);
+    for (int q = 1; q < 7; ++q) read_one(sa, q, xbuf, wbuf, 3);
     mfma_step(sb);
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
     __builtin_amdgcn_sched_group_barrier(kSchedLdsRead, 2, 0);
@@ -324,7 +337,7 @@ __global__ __launch_bounds__(kThreads, 1) void kv_proj_kernel(const GemmArgs a) 
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, kMfma - 3, 0);
     __builtin_amdgcn_sched_barrier(0);
     // step 3
-    read_frags(sb, lds + ((r + 1) % 3) * kXStageBytes, lds + kWBase + (wbuf ^ 1) * kWStageBytes, 0);
+    read_frags(sb, (r + 1) % 3, (r + 1) % 2, 0);
     issue_w(ahead, wbuf, 3, 6);
     mfma_step(sa);
 #pragma unroll
@@ -343,10 +356,16 @@ __global__ __launch_bounds__(kThreads, 1) void kv_proj_kernel(const GemmArgs a) 
   using R0 = std::integral_constant<int, 0>;
   using R1 = std::integral_constant<int, 1>;
   using R2 = std::integral_constant<int, 2>;
-  for (int kb = 0; kb < stages; kb += 3) {
+  using R3 = std::integral_constant<int, 3>;
+  using R4 = std::integral_constant<int, 4>;
+  using R5 = std::integral_constant<int, 5>;
+  for (int kb = 0; kb < stages; kb += 6) {
     do_stage(R0{}, kb);
     if (kb + 1 < stages) do_stage(R1{}, kb + 1);
     if (kb + 2 < stages) do_stage(R2{}, kb + 2);
+    if (kb + 3 < stages) do_stage(R3{}, kb + 3);
+    if (kb + 4 < stages) do_stage(R4{}, kb + 4);
+    if (kb + 5 < stages) do_stage(R5{}, kb + 5);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // the repeated copies have landed
   __syncthreads();                      // and no wavefront reads a stage any more
