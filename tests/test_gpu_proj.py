@@ -50,8 +50,12 @@ def check_close(got_bits, ref_bits, what):
 
 
 @pytest.mark.parametrize("T,K,N", [(1, 64, 16), (300, 128, 208), (256, 192, 192),
-                                   (513, 640, 400), (37, 64, 2880)])
+                                   (513, 640, 400), (37, 64, 2880),
+                                   (200, 320, 192), (129, 384, 96), (64, 448, 2880)])
 def test_proj_ragged_shapes(mk, T, K, N):
+    """Ragged row and column tiles; K from 1 to 10 stages of 64 (the K loop
+    is unrolled by six stages over a three-buffer X ring and a two-buffer W
+    ring, so 5, 6 and 7 stages end the loop at each buffer phase)."""
     announce("proj", T, K, N)
     g = torch.Generator().manual_seed(T + K + N)
     x = synth.bf16_normal((T, K), g)
