@@ -241,3 +241,77 @@ def test_epilogue_one_hot_rows(mk):
             assert r[l, t, (13 * t + 97 * l) % 512] == bf(math.sqrt(512.0))
             assert r[l, t, 512] == bf(math.cos(11 * t)) or bf16_ulps(r[l, t, 512], bf(math.cos(11 * t))) <= 1
             assert bf16_ulps(r[l, t, 544], bf(math.sin(11 * t))) <= 1
+
+
+@pytest.mark.parametrize("L", [5, 9])
+def test_epilogue_special_rows(mk, L):
+    """Rows outside the ordinary range, through both kernels (weights in LDS
+    for 5 layers, from global memory for 9): an all-zero kv_c with signed
+    zeros (the norm scales by 1/sqrt(eps)), a NaN in kv_c (every normed value
+    NaN), +-Inf in kv_c (the sum of squares is infinite, so the finite values
+    normalise to signed zeros and the infinite one to NaN), values near 1e15
+    (their squares stay inside fp32), values near 1e-30 (their squares
+    underflow; eps dominates on both sides), bf16 subnormals, and NaN / Inf
+    in k_pe at position 0 (where sin = 0) and elsewhere.  Normed and rotated
+    values: NaN exactly where the oracle has NaN, every other value within 1
+    bf16 ulp; fp8 codes: a NaN code where the row is NaN, elsewhere within one
+    code and identical where the rows agree; the oracle's insert of the GPU's
+    own rows gives the GPU's caches bit for bit (NaN signs included)."""
+    announce("epilogue special rows", L)
+    T = 64
+    d = synth.context_epilogue(num_tokens=T, num_blocks=4, with_gemm=False, seed=300 + L,
+                               num_layers=L)
+    akv = d["all_kv"].clone().float()
+    akv[0, 0, :512] = 0.0
+    akv[0, 0, 1:512:3] = -0.0
+    akv[1, 1 % L, 77] = float("nan")
+    akv[2, 2 % L, 5] = float("inf")
+    akv[3, 3 % L, 500] = float("-inf")
+    akv[4, 4 % L, :512] *= 3e13
+    akv[5, 0, :512] *= 2e-32
+    akv[7, 1, 512 + 3] = float("nan")
+    akv[8, 2, 512 + 40] = float("inf")
+    akv[9, 3, 512 + 10] = float("-inf")
+    akv[10, 4 % L, 512 + 33] = float("inf")
+    akv = akv.to(torch.bfloat16)
+    # bf16 subnormals (exponent field 0) for row (6, 0)
+    g = torch.Generator().manual_seed(301)
+    mant = torch.randint(1, 128, (512,), generator=g, dtype=torch.int32)
+    sign = torch.randint(0, 2, (512,), generator=g, dtype=torch.int32) << 15
+    akv.view(torch.int16)[6, 0, :512] = (mant | sign).to(torch.int16)
+    d["all_kv"] = akv
+    pos = d["positions"].clone()
+    pos[7] = 0
+    pos[8] = 0
+    pos[9] = 123
+    pos[10] = 4000
+    d["positions"] = pos
+    caches, rows = run_epilogue(mk, d, "fp8")
+
+    ref_caches = [u8(c).copy() for c in d["caches"]]
+    ref_rows = oracle.ctx_kv_epilogue(u16(d["all_kv"]), u16(d["gamma"]), d["eps"],
+                                      d["positions"].numpy(), d["slot_mapping"].numpy(),
+                                      ref_caches, d["scales"].numpy())
+    got_rows = u16(rows)
+    is_nan = lambda b: ((b & 0x7F80) == 0x7F80) & ((b & 0x7F) != 0)
+    rn, gn = is_nan(ref_rows), is_nan(got_rows)
+    assert np.array_equal(rn, gn), f"NaN positions differ: {np.argwhere(rn != gn)[:4]}"
+    # rows are [layer, token, 576]
+    assert rn[1 % L, 1, :512].all() and rn[2 % L, 2, 5] and not rn[2 % L, 2, 6]
+    assert got_rows[0, 0, 1] == 0x8000 and got_rows[0, 0, 0] == 0x0000
+    ul = bf16_ulps(np.where(rn, 0, got_rows), np.where(rn, 0, ref_rows))
+    assert ul.max() <= 1, f"rows differ by up to {ul.max()} bf16 ulp at {np.argwhere(ul > 1)[:4]}"
+    sm = d["slot_mapping"].numpy()
+    for l in range(L):
+        got = u8(caches[l]).reshape(-1, 576)[sm[l]]
+        ref = ref_caches[l].reshape(-1, 576)[sm[l]]
+        nan_row = rn[l]
+        assert np.all((got[nan_row] & 0x7F) == 0x7F), f"layer {l}: NaN codes"
+        assert np.all((ref[nan_row] & 0x7F) == 0x7F), f"layer {l}: oracle NaN codes"
+        apart = fp8_codes_apart(np.where(nan_row, 0, got), np.where(nan_row, 0, ref))
+        assert apart.max() <= 1, f"layer {l}: codes up to {apart.max()} apart"
+        agree = (got_rows[l] == ref_rows[l]) & ~nan_row
+        assert np.array_equal(got[agree], ref[agree]), f"layer {l}"
+    announce(f"special rows: {int(rn.sum())} NaN values, {int((ul == 0).sum())}/{ul.size} "
+             "identical")
+    check_rows_insert(d, caches, rows, "fp8")
