@@ -16,7 +16,9 @@ oracle's, else within one code.  Workloads: strided views of the model's tensors
 tokens and 1 to 32 heads with a padded token, both output modes and all
 three cache formats (fp8 outputs with heads a multiple of 16 run the grouped
 form), the full 8192-token x 64-head prefill (every token), capped grids of
-both forms, and a cache-only call.
+both forms, a cache-only call, and special values (NaN, +-Inf, -0,
+subnormals, values beyond the fp8 range; rotations that produce NaN are
+compared as NaN, since the sign of a NaN made by arithmetic is not fixed).
 """
 import numpy as np
 import pytest
@@ -291,3 +293,80 @@ def test_other_head_widths(mk, nope, vdim, fp8):
                  "query rope codes")
     assert_codes(u8(kg)[..., nope:], k8[..., nope:], u16(kb)[..., nope:], kref[..., nope:],
                  "key rope codes")
+
+
+def is_bf16_nan(b):
+    return ((b & 0x7F80) == 0x7F80) & ((b & 0x7F) != 0)
+
+
+def check_rope_special(got, ref, what):
+    """Rotations with special inputs: NaN exactly where the oracle's is NaN
+    (the sign of a NaN made by arithmetic is not fixed), every other value
+    within 1 bf16 ulp."""
+    rn = is_bf16_nan(ref)
+    assert np.array_equal(rn, is_bf16_nan(got)), f"{what}: NaN positions differ"
+    ul = bf16_ulps(np.where(rn, 0, got), np.where(rn, 0, ref))
+    assert ul.max() <= 1, f"{what}: up to {ul.max()} ulp"
+    return rn
+
+
+def check_codes_special(got, ref, gpu_bf16, ref_bf16, rn, what):
+    assert np.all((got[rn] & 0x7F) == 0x7F) and np.all((ref[rn] & 0x7F) == 0x7F), what
+    agree = (gpu_bf16 == ref_bf16) & ~rn
+    assert np.array_equal(got[agree], ref[agree]), what
+    assert fp8_codes_apart(np.where(rn, 0, got), np.where(rn, 0, ref)).max() <= 1, what
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_special_values(mk, fp8):
+    """NaN (both signs), +-Inf, -0, a bf16 subnormal and +-1.7e38 planted in
+    q_nope, k_nope, V and kv_c (casts and copies: bit-exact, saturating at
+    the fp8 bound), and NaN / +-Inf in q_pe and k_pe, at position 0 (sin = 0,
+    so the partner of an infinite value becomes NaN) and elsewhere; 16 heads,
+    so the fp8 outputs take the grouped form."""
+    announce("new-token epilogue special values", fp8)
+    case = Case(70, 40, 16, "e4m3")
+    d = case.d
+    pats = torch.tensor([0x7FC0, 0xFFC0, 0x7F80, 0xFF80, 0x8000, 0x0005, 0x7F00, 0xFF00],
+                        dtype=torch.int32).to(torch.int16)
+    q, kvb, kv = (d[k].view(torch.int16) for k in ("q", "kvb", "kv"))
+    q[0, 0, 0:8] = pats
+    q[3, 15, 120:128] = pats
+    kvb[1, 1, 0:8] = pats              # k_nope
+    kvb[2, 7, 128:136] = pats          # V
+    kv[2, 0:8] = pats                  # kv_c
+    nan, inf, ninf = 0x7FC0, 0x7F80, 0xFF80 - 0x10000  # bit patterns as int16 values
+    q[0, 2, NOPE + 3] = nan
+    q[0, 2, NOPE + 40] = inf
+    q[6, 3, NOPE + 10] = ninf
+    kv[0, R + 40] = inf                 # position 0: its partner k_pe[8] -> NaN
+    kv[7, R + 2] = nan
+    kv[9, R + 50] = ninf
+    d["positions"][0] = 0
+    case.g = {k: v.to(DEV) for k, v in d.items() if isinstance(v, torch.Tensor)}
+
+    qg, kg, vg, cg = case.run_gpu(mk, fp8)
+    qb, kb, _, _ = case.run_gpu(mk, False, cache=False)
+    q_o, key_o, v_o, cache_o, h, slots = case.run_oracle(fp8)
+    qref, kref, _ = case.run_oracle(False)[:3]
+    conv = u8 if fp8 else u16
+    assert np.array_equal(conv(qg)[..., :NOPE], q_o[..., :NOPE]), "query nope part"
+    assert np.array_equal(conv(kg)[..., :NOPE], key_o[..., :NOPE]), "key nope part"
+    if fp8:
+        assert np.array_equal(u8(vg), v_o), "V"
+    qrn = check_rope_special(u16(qb)[..., NOPE:], qref[..., NOPE:], "query rope")
+    krn = check_rope_special(u16(kb)[..., NOPE:], kref[..., NOPE:], "key rope")
+    assert qrn[0, 2].sum() >= 2 and krn[0, :, 8].all() and krn[7].any()
+    if fp8:
+        check_codes_special(u8(qg)[..., NOPE:], q_o[..., NOPE:], u16(qb)[..., NOPE:],
+                            qref[..., NOPE:], qrn, "query rope codes")
+        check_codes_special(u8(kg)[..., NOPE:], key_o[..., NOPE:], u16(kb)[..., NOPE:],
+                            kref[..., NOPE:], krn, "key rope codes")
+    got = u8(cg).reshape(-1, R + P)
+    ref = cache_o.reshape(-1, R + P)
+    ok = slots >= 0
+    gs, rs = got[slots[ok]], ref[slots[ok]]
+    assert np.array_equal(gs[:, :R], rs[:, :R]), "cache kv_c part"
+    check_codes_special(gs[:, R:], rs[:, R:], u16(kb)[ok][:, 0, NOPE:], kref[ok][:, 0, NOPE:],
+                        krn[ok][:, 0], "cache rope codes")
+    announce(f"special values: {int(qrn.sum())} query and {int(krn.sum())} key NaN rotations")
