@@ -100,6 +100,43 @@ def test_gather_partial_width_and_zero_tokens(mk):
     assert empty.shape == (0, 576)
 
 
+
+@pytest.mark.parametrize("kind", ["fp8", "raw", "bfloat16"])
+@pytest.mark.parametrize("layout", ["padded_entries", "padded_blocks", "block_size_one"])
+def test_gather_padded_layouts(mk, kind, layout):
+    """Cache views whose entries or blocks are padded (entry stride 640 with
+    the row at byte offset 32 of the entry; 16 of 17 entries used per block)
+    and a block size of 1, read through the view's strides: every row equals
+    the oracle's gather of the same logical [num_blocks, block_size, 576]
+    cache (raw: the codes themselves)."""
+    announce("gather layout", kind, layout)
+    g = torch.Generator().manual_seed(400 + len(kind) * 7 + len(layout))
+    bf16 = kind == "bfloat16"
+    shape = {"padded_entries": (24, 32, 640), "padded_blocks": (40, 17, 576),
+             "block_size_one": (700, 1, 576 + 64)}[layout]
+    buf = synth.random_bf16_bits(shape, g) if bf16 else synth.random_bytes(shape, g)
+    view = {"padded_entries": lambda b: b[:, :, 16 if bf16 else 32:][:, :, :576],
+            "padded_blocks": lambda b: b[:, :16, :],
+            "block_size_one": lambda b: b[:, :, :576]}[layout]
+    host = view(buf)
+    nb, bs = host.shape[0], host.shape[1]
+    slots = torch.randperm(nb * bs, generator=g)[:min(600, nb * bs)].to(torch.int64)
+    dev = view(buf.to(DEV))
+    assert dev.stride() == host.stride()
+    logical = (u16(host) if bf16 else u8(host)).copy()
+    if kind == "raw":
+        out = torch.empty(slots.numel(), 576, dtype=torch.uint8, device=DEV)
+        mk.mla_ctx_latent_gather(dev, slots.to(DEV), out, None, "fp8")
+        ref = logical.reshape(-1, 576)[slots.numpy()]
+        assert np.array_equal(u8(out), ref)
+        return
+    scale = None if bf16 else 0.7312
+    out = gpu_gather(mk, dev, slots.to(DEV), scale, dtype="bfloat16" if bf16 else "fp8")
+    ref = oracle.gather(logical, slots.numpy(), scale) if scale else oracle.gather(logical,
+                                                                                slots.numpy())
+    assert np.array_equal(u16(out), ref)
+
+
 # -------------------------------------------------------------------- pack --
 @pytest.mark.parametrize("H", [3, 4])
 @pytest.mark.parametrize("T", [0, 1, 37, 300])
