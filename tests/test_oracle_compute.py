@@ -95,6 +95,36 @@ def test_rmsnorm_matches_f64_formula(orc):
         assert bf16_ulp_dist(ours, orc.f64_to_bf16(ref.numpy())).max() == 0
 
 
+
+def test_rmsnorm_special_values(orc):
+    """IEEE consequences of the definition x * (mean x^2 + eps)^-1/2 * gamma:
+    an all-zero row gives zeros carrying the signs of x * gamma; a NaN makes
+    every output NaN; an infinite element makes the scale 0, so it becomes
+    NaN (Inf * 0) and every finite element a signed zero."""
+    n = 512
+    gamma = np.full(n, bf(1.0), np.uint16)
+    gamma[3] = bf(-2.0)
+    nan_bits = lambda y: ((y & 0x7F80) == 0x7F80) & ((y & 0x7F) != 0)
+    x = np.zeros(n, np.uint16)
+    x[1::2] = 0x8000                                  # -0
+    y = orc.rmsnorm_row(x, gamma, 1e-6)
+    sign = (x >> 15) ^ (gamma >> 15)
+    assert np.array_equal(y, (sign << 15).astype(np.uint16))
+    g = torch.Generator().manual_seed(6)
+    base = u16(torch.randn(n, generator=g).to(torch.bfloat16))
+    xn = base.copy()
+    xn[200] = 0x7FC0
+    assert nan_bits(orc.rmsnorm_row(xn, gamma, 1e-6)).all()
+    for inf in (0x7F80, 0xFF80):
+        xi = base.copy()
+        xi[10] = inf
+        y = orc.rmsnorm_row(xi, gamma, 1e-6)
+        assert nan_bits(y[10])
+        rest = np.delete(np.arange(n), 10)
+        assert not (y[rest] & 0x7FFF).any()
+        assert np.array_equal(y[rest] >> 15, (xi[rest] >> 15) ^ (gamma[rest] >> 15))
+
+
 # --------------------------------------------------------------------- RoPE --
 def test_rope_position_zero_is_identity(orc):
     g = torch.Generator().manual_seed(5)
