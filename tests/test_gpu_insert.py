@@ -159,6 +159,46 @@ def test_exhaustive_bf16_patterns_through_fp8_converter(mk):
                                  f"gpu 0x{got[tuple(i)]:02x}, oracle 0x{ref[tuple(i)]:02x}")
 
 
+
+@pytest.mark.parametrize("dtype", ["fp8", "fp8_e5m2"])
+def test_extreme_scales_through_fp8_converter(mk, dtype):
+    """All 65536 bf16 patterns quantised with scales at and inside the edges
+    of the range where the quotient is exact (2^-85 <= |s| < 2^126, the
+    stated precondition): the smallest, the largest fp32 below 2^126, odd
+    significands and a negative scale; e4m3fn and e5m2 codes equal the
+    oracle's (one IEEE fp32 division, then the format's rounding) bit for
+    bit, so the device's reciprocal-and-FMA quotient, its subnormal results
+    and the saturation behave as on the host across the whole range."""
+    announce("extreme scales", dtype)
+    f = np.float32
+    scales = torch.tensor([f(2.0 ** -85), f(1.5 * 2.0 ** -85), f(1e-20), f(3e-9),
+                           f(1.2345678 * 2.0 ** 40), f(1e30),
+                           np.nextafter(f(2.0 ** 126), f(0)), f(-1.7 * 2.0 ** -85)],
+                          dtype=torch.float32)
+    assert float(scales.abs().min()) >= 2.0 ** -85 and float(scales.abs().max()) < 2.0 ** 126
+    L = scales.numel()
+    rows = 65536 // 512 + 1
+    bits = np.arange(rows * 576, dtype=np.int64) % 65536
+    x = torch.from_numpy(bits.astype(np.int32)).to(torch.int16).view(torch.bfloat16).reshape(rows, 576)
+    d = dict(kv_c=x[:, :512].unsqueeze(0).expand(L, rows, 512),
+             k_pe=x[:, 512:].unsqueeze(0).expand(L, rows, 64),
+             caches=[torch.zeros(rows, 1, 576, dtype=torch.uint8) for _ in range(L)],
+             scales=scales, slot_mapping=torch.arange(rows, dtype=torch.int64).reshape(1, rows)
+             .expand(L, rows), num_layers=L, num_tokens=rows, block_size=1)
+    gpu = run_gpu(mk, d, dtype)
+    quant = oracle.quantize if dtype == "fp8" else oracle.quantize_e5m2
+    for l in range(L):
+        ref = quant(u16(x), float(scales[l])).reshape(rows, 1, 576)
+        got = np_cache(gpu[l])
+        if not np.array_equal(got, ref):
+            i = np.argwhere(got != ref)[0]
+            b = int(u16(x)[i[0], i[2]])
+            raise AssertionError(f"scale {float(scales[l])!r}: bf16 0x{b:04x} -> "
+                                 f"gpu 0x{got[tuple(i)]:02x}, oracle 0x{ref[tuple(i)]:02x}")
+        announce(f"scale {float(scales[l]):.4g}: {int((ref & 0x7F).astype(bool).sum())} "
+                 "nonzero codes, all equal")
+
+
 def test_padded_layout_and_block_size_one(mk):
     announce("padded_layout")
     g = torch.Generator().manual_seed(77)
