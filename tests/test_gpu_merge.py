@@ -87,6 +87,28 @@ def test_single_merge_random(mk, T, H, D):
     announce(f"outputs identical: {np.mean(ulps == 0):.5f}")
 
 
+
+@pytest.mark.parametrize("stretch,offset", [(40.0, 0.0), (1.0, 1.0e5), (0.01, -3.0e4)])
+def test_merge_wide_lse_range(mk, stretch, offset):
+    """lse values far outside the workload's N(8, 3^2): spread 40x (most
+    pairs differ by hundreds, so one weight underflows to 0 and the other
+    partial passes through), shifted to 1e5 (exp(lse) itself overflows fp32;
+    only differences may be exponentiated), and squeezed to 1/100 of the
+    spread around -3e4 (weights nearly equal); 10% of the entries -inf.
+    Outputs and lse against the oracle as in the other merge tests."""
+    announce("merge wide lse", stretch, offset)
+    d = synth.attention_partials(seed=77, num_tokens=300, heads=8, head_dim=128, chunks=2,
+                                 empty_frac=0.1)
+    (oa, ob), (la, lb) = d["outs"], d["lses"]
+    la = la * stretch + offset
+    lb = lb * stretch + offset
+    go, gl = gpu_merge(mk, oa, la, ob, lb, mk.MLA_MERGE_ACCUMULATE)
+    ro, rl = oracle_merge(oa, la, ob, lb, oracle.MERGE_ACCUMULATE)
+    ulps = merge_close(u16(go), ro, oa, ob, f32np(la), f32np(lb))
+    lse_close(f32np(gl), rl)
+    announce(f"outputs identical: {np.mean(ulps == 0):.5f}")
+
+
 def test_identities_and_edge_cases(mk):
     announce("merge identities")
     T, H, D = 16, 4, 128
