@@ -31,6 +31,31 @@ def test_version(mk):
     assert "gfx950" in mk.version()
 
 
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """Without the built HIP library every call raises: there is no CPU or
+    fallback path behind the binding."""
+    import fp8_paged_insert_amd._binding as B
+    monkeypatch.setattr(B, "LIB_PATH", os.path.join(ROOT, "_no_such_dir", "libmla_kv.so"))
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(RuntimeError, match="no fallback"):
+        B.version()
+    with pytest.raises(RuntimeError, match="not built"):
+        B.lib()
+
+
+def test_product_package_does_not_use_the_oracle():
+    """The package (binding, build script, input generators) never imports
+    or loads anything under oracle/."""
+    pkg = os.path.join(ROOT, "fp8_paged_insert_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
+                assert "mla_oracle" not in text and "liborc" not in text, f
+
+
 @pytest.mark.parametrize("s,code", [("auto", 0), ("bfloat16", 1), ("fp8", 2), ("fp8_e4m3", 2),
                                     ("fp8_e5m2", 3)])
 def test_parse_dtype_accepts_whitelist(mk, s, code):
